@@ -1,0 +1,11 @@
+"""Oracle (test infrastructure): plain float64 CPU attention under static
+block-sparse masks.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+``bench.py``'s ``cpu_baseline`` leg may import it; the product path never
+does.  It shares no code with the HIP library.  See ``attention.py``."""
+
+from .attention import (  # noqa: F401
+    ATTNSINK, BLOCKSPARSE, FULL, attention_backward, attention_forward,
+    block_lists, decode_one, decode_positions, dense_token_mask,
+    kv_cache_bytes, pattern_lists_for_head, sparse_backward, sparse_forward,
+    transpose_lists,
+)

@@ -1,0 +1,294 @@
+"""Oracle for static block-sparse causal attention — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import anything in this package.  The product path (the HIP library
+and its Python binding) never imports it, and this package imports nothing
+from the product.
+
+What is computed, and where it is stated
+----------------------------------------
+LongGen ("A Little Goes a Long Way: Efficient Long Context Training and
+Inference with Partial Contexts") keeps 2/3 of the layers sparse with fixed
+patterns -- attention sink (the first tokens), window attention (the most
+recent tokens) and blockwise sparse attention (strided token blocks)
+[mlsanity index page, section "Abstract (arXiv)"].  The sparsity is static and
+block-wise and the training kernel is FlashAttention-2 based [atlas.scime.ai
+summary, section "Approach"].  A static mask does not change what attention
+computes; it only restricts the keys each query sees.  So this oracle is the
+plain definition: build the block lists by brute-force scan, expand them to a
+dense token mask, materialise the dense masked score matrix, and take an
+ordinary softmax -- no tiling, no online softmax, no fusion.
+
+Precision: every floating-point step runs in float64 on the CPU.  Inputs that
+the GPU sees as bf16 are handed in as their exact values (bf16 -> float64 is
+exact).
+
+Readings taken where the pages are silent (each is listed in the design notes):
+  * block size, sink / window / stride sizes come from the workload
+    definitions (block 64, sink 1 block, window 4/16/64 blocks, stride 8);
+  * the prefill window is block-granular and contains the diagonal block;
+    causality masks keys later than the query inside any block;
+  * BlockSparse head h takes blocks j < i with (j + h) mod stride == 0;
+  * the softmax scale is 1/sqrt(d); LSE is the natural log of the sum of
+    exp(scaled scores) over allowed keys; an empty row gives O = 0, LSE = -inf;
+  * decode is token-granular: the new token t sees tokens 0..sink-1 and
+    t-window+1..t (itself included).
+
+Parity pins (tests/test_oracle_pins.py): every function here is pinned by a
+check that does not re-type its formula -- closed-form counts, textbook /
+library attention (torch scaled_dot_product_attention in float64 on the CPU),
+Q = 0 and constant-V closed forms, and central finite differences for the
+backward pass.  ``kv_cache_bytes`` is pinned to the pages' KV-memory figure
+only up to the pages' unstated layer / window split (consistency only).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+FULL = "full"
+ATTNSINK = "attnsink"
+BLOCKSPARSE = "blocksparse"
+
+
+# ----------------------------------------------------------------------------
+# Block lists  [index page, Abstract: window / sink / strided-block patterns;
+#               summary page, Approach: static, block-wise access]
+# ----------------------------------------------------------------------------
+def block_lists(kind, n_qblocks, *, sink_blocks=1, local_blocks=1, stride=0,
+                head=0, n_kblocks=None):
+    """Ascending KV-block list of every query block, by brute-force scan.
+
+    For query block ``i`` every key block ``j`` in ``0..n_kblocks-1`` is tested
+    for membership on its own:
+      * full:        j <= i
+      * attnsink:    j < sink_blocks (and j <= i), or i-local_blocks < j <= i
+      * blocksparse: the attnsink rule, or j < i with (j + head) % stride == 0
+    Returns a list of Python int lists.
+    """
+    if n_kblocks is None:
+        n_kblocks = n_qblocks
+    out = []
+    for i in range(n_qblocks):
+        row = []
+        for j in range(n_kblocks):
+            if kind == FULL:
+                keep = j <= i
+            elif kind in (ATTNSINK, BLOCKSPARSE):
+                is_sink = j < sink_blocks and j <= i
+                is_local = (i - local_blocks) < j <= i
+                keep = is_sink or is_local
+                if kind == BLOCKSPARSE and not keep and stride > 0:
+                    keep = j < i and (j + head) % stride == 0
+            else:
+                raise ValueError(f"unknown pattern kind {kind!r}")
+            if keep:
+                row.append(j)
+        out.append(row)
+    return out
+
+
+def transpose_lists(lists, n_kblocks):
+    """Column lists (query blocks that read key block j), ascending."""
+    cols = [[] for _ in range(n_kblocks)]
+    for i, row in enumerate(lists):
+        for j in row:
+            cols[j].append(i)
+    return cols
+
+
+def dense_token_mask(lists, block, n_q_tokens, n_k_tokens, causal, rows=None):
+    """Boolean [n_rows, n_k_tokens]: key token allowed for a query token.
+
+    ``rows`` lists the query-token positions (default 0..n_q_tokens-1).  A key
+    is allowed when its block is in the query block's list and, if
+    ``causal``, its position does not exceed the query's position.
+    """
+    if rows is None:
+        rows = np.arange(n_q_tokens)
+    m = np.zeros((len(rows), n_k_tokens), dtype=bool)
+    for n, qi in enumerate(rows):
+        for j in lists[qi // block]:
+            lo = j * block
+            hi = min(lo + block, n_k_tokens)
+            m[n, lo:hi] = True
+        if causal:
+            m[n, qi + 1:] = False
+    return m
+
+
+# ----------------------------------------------------------------------------
+# Prefill forward / backward on one head  (the plain softmax-attention
+# definition under a fixed mask; FlashAttention-2 computes the same values)
+# ----------------------------------------------------------------------------
+def attention_forward(q, k, v, mask, scale, row_chunk=1024):
+    """O, LSE for one head.  q [Lq,d], k/v [Lk,d], mask [Lq,Lk] bool.
+
+    S = scale * q k^T; S = -inf where masked; P = softmax(S) row-wise;
+    O = P v; LSE = log(sum(exp(S))).  Rows with no allowed key: O = 0,
+    LSE = -inf.  Processed in query-row chunks; each chunk holds its full
+    dense masked score rows.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Lq = q.shape[0]
+    o = np.zeros((Lq, v.shape[1]), dtype=np.float64)
+    lse = np.full((Lq,), -np.inf, dtype=np.float64)
+    for r0 in range(0, Lq, row_chunk):
+        r1 = min(r0 + row_chunk, Lq)
+        s = (q[r0:r1] @ k.T) * scale
+        mk = mask[r0:r1]
+        s = np.where(mk, s, -np.inf)
+        m = s.max(axis=1)
+        live = np.isfinite(m)
+        m_safe = np.where(live, m, 0.0)
+        p = np.exp(s - m_safe[:, None])          # exp(-inf) = 0 on masked keys
+        l = p.sum(axis=1)
+        o_chunk = p @ v
+        o[r0:r1][live] = o_chunk[live] / l[live][:, None]
+        lse[r0:r1][live] = m[live] + np.log(l[live])
+    return o, lse
+
+
+def attention_backward(q, k, v, do, mask, scale, row_chunk=1024):
+    """dQ, dK, dV of loss = sum(O * dO) for one head, plus (O, LSE).
+
+    With P the masked softmax of the forward pass:
+      D  = rowsum(dO * O)
+      dV = P^T dO
+      dP = dO V^T
+      dS = P * (dP - D)
+      dQ = scale * dS K
+      dK = scale * dS^T Q
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    o, lse = attention_forward(q, k, v, mask, scale, row_chunk)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    Lq = q.shape[0]
+    for r0 in range(0, Lq, row_chunk):
+        r1 = min(r0 + row_chunk, Lq)
+        s = (q[r0:r1] @ k.T) * scale
+        mk = mask[r0:r1]
+        live = np.isfinite(lse[r0:r1])
+        lse_safe = np.where(live, lse[r0:r1], 0.0)
+        p = np.where(mk, np.exp(s - lse_safe[:, None]), 0.0)
+        p[~live] = 0.0
+        d_row = (do[r0:r1] * o[r0:r1]).sum(axis=1)
+        dv += p.T @ do[r0:r1]
+        dp = do[r0:r1] @ v.T
+        ds = p * (dp - d_row[:, None])
+        dq[r0:r1] = scale * (ds @ k)
+        dk += scale * (ds.T @ q[r0:r1])
+    return dq, dk, dv, o, lse
+
+
+# ----------------------------------------------------------------------------
+# Batched prefill wrappers over [B,H,L,d]
+# ----------------------------------------------------------------------------
+def pattern_lists_for_head(pattern, n_qblocks, head):
+    return block_lists(pattern["kind"], n_qblocks,
+                       sink_blocks=pattern.get("sink_blocks", 0),
+                       local_blocks=pattern.get("local_blocks", 0),
+                       stride=pattern.get("stride", 0), head=head)
+
+
+def sparse_forward(q, k, v, pattern, scale=None, heads=None, rows=None):
+    """Forward over [B,H,L,d] arrays for the given pattern dict.
+
+    ``heads``: optional list of head indices to compute (others left NaN).
+    ``rows``:  optional array of query-token indices to compute (others NaN).
+    Returns (o [B,H,L,d], lse [B,H,L]) in float64.
+    """
+    B, H, L, d = q.shape
+    block = pattern["block"]
+    nb = L // block
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = np.full((B, H, L, d), np.nan)
+    lse = np.full((B, H, L), np.nan)
+    heads = range(H) if heads is None else heads
+    for h in heads:
+        lists = pattern_lists_for_head(pattern, nb, h)
+        causal = pattern.get("causal", True)
+        if rows is None:
+            mask = dense_token_mask(lists, block, L, L, causal)
+            for b in range(B):
+                o[b, h], lse[b, h] = attention_forward(q[b, h], k[b, h], v[b, h], mask, scale)
+        else:
+            rows = np.asarray(rows)
+            mask = dense_token_mask(lists, block, L, L, causal, rows=rows)
+            for b in range(B):
+                ob, lb = attention_forward(q[b, h][rows], k[b, h], v[b, h], mask, scale)
+                o[b, h][rows] = ob
+                lse[b, h][rows] = lb
+    return o, lse
+
+
+def sparse_backward(q, k, v, do, pattern, scale=None, heads=None):
+    """Backward over [B,H,L,d]; returns dq, dk, dv, o, lse (float64)."""
+    B, H, L, d = q.shape
+    block = pattern["block"]
+    nb = L // block
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    shp = (B, H, L, d)
+    dq, dk, dv, o = (np.full(shp, np.nan) for _ in range(4))
+    lse = np.full((B, H, L), np.nan)
+    heads = range(H) if heads is None else heads
+    for h in heads:
+        lists = pattern_lists_for_head(pattern, nb, h)
+        mask = dense_token_mask(lists, block, L, L, pattern.get("causal", True))
+        for b in range(B):
+            dq[b, h], dk[b, h], dv[b, h], o[b, h], lse[b, h] = attention_backward(
+                q[b, h], k[b, h], v[b, h], do[b, h], mask, scale)
+    return dq, dk, dv, o, lse
+
+
+# ----------------------------------------------------------------------------
+# Decode  [index page, Abstract: reduced KV cache; summary page, Key results:
+#          KV memory cut from keeping only part of the context in sparse layers]
+# ----------------------------------------------------------------------------
+def decode_positions(t, sink_tokens=None, window_tokens=None):
+    """Token positions the new token at absolute position t attends to.
+
+    Full layers (sink_tokens is None): 0..t.  Sparse layers: the first
+    ``sink_tokens`` tokens and the last ``window_tokens`` tokens up to and
+    including t, as a sorted set.
+    """
+    if sink_tokens is None:
+        return np.arange(t + 1)
+    keep = set(range(min(sink_tokens, t + 1)))
+    keep.update(range(max(0, t - window_tokens + 1), t + 1))
+    return np.array(sorted(keep), dtype=np.int64)
+
+
+def decode_one(q, k_hist, v_hist, positions, scale):
+    """o, lse of one query over the listed token rows of its history."""
+    q = np.asarray(q, dtype=np.float64)
+    kk = np.asarray(k_hist, dtype=np.float64)[positions]
+    vv = np.asarray(v_hist, dtype=np.float64)[positions]
+    s = (kk @ q) * scale
+    m = s.max()
+    p = np.exp(s - m)
+    l = p.sum()
+    return (p @ vv) / l, m + math.log(l)
+
+
+# ----------------------------------------------------------------------------
+# KV-cache size (closed form)  [summary page, Key results and "Measured
+# effects" table: KV memory of the 1/3-full hybrid vs full attention]
+# ----------------------------------------------------------------------------
+def kv_cache_bytes(n_layers_full, n_layers_sparse, heads, head_dim, tokens,
+                   sparse_tokens, bytes_per_elem=2, batch=1):
+    """Bytes of K and V kept by a hybrid model: full layers keep every token,
+    sparse layers keep only their sink+window tokens."""
+    per_token_layer = 2 * heads * head_dim * bytes_per_elem * batch
+    return per_token_layer * (n_layers_full * tokens + n_layers_sparse * sparse_tokens)

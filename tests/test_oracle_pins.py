@@ -1,0 +1,363 @@
+"""Pins of the oracle against things other than itself (CPU only).
+
+Each check is chosen so that a plausible slip in the oracle -- a dropped
+term, a wrong sign, an off-by-one in a window, a transposed operand -- fails
+at least one of them:
+  * block lists: a hand-written golden list, and closed-form row lengths;
+  * forward: torch's scaled_dot_product_attention (float64, CPU) on the
+    special cases that reduce to it; Q = 0 and constant-V closed forms;
+  * backward: central finite differences in float64, and torch autograd on
+    the full-causal special case;
+  * decode: library attention on its reducible cases and a Q = 0 count;
+  * KV memory: the pages' own figures (consistency only).
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import (ATTNSINK, BLOCKSPARSE, FULL, attention_backward,
+                    attention_forward, block_lists, decode_one,
+                    decode_positions, dense_token_mask, kv_cache_bytes,
+                    sparse_backward, sparse_forward, transpose_lists)
+
+
+# --------------------------------------------------------------------------
+# helpers that are NOT the oracle
+# --------------------------------------------------------------------------
+def sdpa(q, k, v, attn_mask=None, is_causal=False, scale=None):
+    """torch's library attention in float64 on the CPU, one head, 2-D arrays."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))[None, None]
+    m = None if attn_mask is None else torch.from_numpy(attn_mask)[None, None]
+    out = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=m,
+                                         is_causal=is_causal, scale=scale)
+    return out[0, 0].numpy()
+
+
+def attnsink_row_len(i, s, w):
+    """Closed form: |{0..min(s,i+1)-1} U {max(0,i-w+1)..i}|."""
+    a = max(0, i - w + 1)
+    return (i - a + 1) + min(s, a)
+
+
+def blocksparse_row_len(i, s, w, stride, h):
+    """Closed form for the sink + local + strided rule (stride offset h)."""
+    a = max(0, i - w + 1)                      # first local block
+    local = i - a + 1
+    r = (-h) % stride                          # j = r (mod stride) are strided
+    strided_below = 0 if a <= r else (a - 1 - r) // stride + 1
+    sink_extra = sum(1 for j in range(min(s, a)) if (j % stride) != r)
+    return local + strided_below + sink_extra
+
+
+def read_golden_lists(path):
+    rows = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, vals = line.split(":")
+            rows[int(key)] = [int(x) for x in vals.split()]
+    return [rows[i] for i in range(len(rows))]
+
+
+# --------------------------------------------------------------------------
+# block lists
+# --------------------------------------------------------------------------
+def test_attnsink_lists_match_hand_written_golden(golden_dir):
+    want = read_golden_lists(os.path.join(golden_dir, "attnsink_nb16_sink1_local4_lists.txt"))
+    got = block_lists(ATTNSINK, 16, sink_blocks=1, local_blocks=4)
+    assert got == want
+    assert sum(len(r) for r in got) == 70
+
+
+@pytest.mark.parametrize("nb,s,w", [(16, 1, 4), (40, 2, 7), (33, 0, 1), (12, 3, 20), (9, 1, 1)])
+def test_attnsink_row_lengths_closed_form(nb, s, w):
+    lists = block_lists(ATTNSINK, nb, sink_blocks=s, local_blocks=w)
+    for i, row in enumerate(lists):
+        assert row == sorted(set(row))
+        assert len(row) == attnsink_row_len(i, s, w)
+        assert i in row if w >= 1 else True           # diagonal block always present
+
+
+@pytest.mark.parametrize("h", range(8))
+def test_blocksparse_row_lengths_closed_form(h):
+    nb = 150
+    lists = block_lists(BLOCKSPARSE, nb, sink_blocks=1, local_blocks=16, stride=8, head=h)
+    for i, row in enumerate(lists):
+        assert row == sorted(set(row))
+        assert len(row) == blocksparse_row_len(i, 1, 16, 8, h), (i, row)
+        # every strided block below the local window has (j + h) % 8 == 0
+        for j in row:
+            if j > 0 and j <= i - 16:
+                assert (j + h) % 8 == 0
+
+
+def test_workload_nnz_closed_forms():
+    # AttnSink, sink 1 block: sum_{i<w}(i+1) + (nb-w)(w+1)
+    for nb, w in [(16, 4), (128, 64), (1024, 64), (2048, 64)]:
+        closed = w * (w + 1) // 2 + (nb - w) * (w + 1)
+        got = sum(len(r) for r in block_lists(ATTNSINK, nb, sink_blocks=1, local_blocks=w))
+        assert got == closed
+    assert [w * (w + 1) // 2 + (nb - w) * (w + 1) for nb, w in
+            [(16, 4), (128, 64), (1024, 64), (2048, 64)]] == [70, 6240, 64480, 131040]
+    # full pattern: nb (nb+1) / 2
+    assert sum(len(r) for r in block_lists(FULL, 100)) == 100 * 101 // 2
+    # BlockSparse at 32768 tokens (512 blocks), 32 heads: closed form per head
+    per_head = [sum(blocksparse_row_len(i, 1, 16, 8, h) for i in range(512)) for h in range(32)]
+    assert min(per_head) == 23696 and max(per_head) == 24130 and sum(per_head) == 765216
+    for h in (0, 3, 7, 12):
+        got = block_lists(BLOCKSPARSE, 512, sink_blocks=1, local_blocks=16, stride=8, head=h)
+        assert sum(len(r) for r in got) == per_head[h]
+
+
+def test_transpose_lists_roundtrip():
+    lists = block_lists(BLOCKSPARSE, 40, sink_blocks=1, local_blocks=5, stride=8, head=3)
+    cols = transpose_lists(lists, 40)
+    pairs_r = sorted((i, j) for i, r in enumerate(lists) for j in r)
+    pairs_c = sorted((i, j) for j, c in enumerate(cols) for i in c)
+    assert pairs_r == pairs_c
+    for c in cols:
+        assert c == sorted(c)
+    assert len(cols[0]) == 40                          # the sink column is read by every row
+
+
+# --------------------------------------------------------------------------
+# forward
+# --------------------------------------------------------------------------
+rng = np.random.default_rng(20241002)
+
+
+def rand(*shape):
+    return rng.standard_normal(shape)
+
+
+@pytest.mark.parametrize("L,block,d", [(96, 16, 8), (64, 64, 16), (130, 13, 5)])
+def test_full_pattern_is_causal_attention(L, block, d):
+    q, k, v = rand(L, d), rand(L, d), rand(L, d)
+    nb = -(-L // block)
+    lists = block_lists(FULL, nb)
+    mask = dense_token_mask(lists, block, L, L, causal=True)
+    scale = 1 / math.sqrt(d)
+    o, lse = attention_forward(q, k, v, mask, scale)
+    np.testing.assert_allclose(o, sdpa(q, k, v, is_causal=True, scale=scale), rtol=0, atol=1e-12)
+    # LSE against its definition via torch.logsumexp over the causal rows
+    s = torch.from_numpy(q @ k.T * scale)
+    s = s.masked_fill(torch.ones(L, L, dtype=torch.bool).triu(1), -math.inf)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_window_covering_sequence_is_full():
+    L, block, d = 128, 16, 8
+    q, k, v = rand(L, d), rand(L, d), rand(L, d)
+    m_sink = dense_token_mask(block_lists(ATTNSINK, 8, sink_blocks=1, local_blocks=8), block, L, L, True)
+    m_bs = dense_token_mask(block_lists(BLOCKSPARSE, 8, sink_blocks=1, local_blocks=8, stride=2, head=1),
+                            block, L, L, True)
+    ref = sdpa(q, k, v, is_causal=True, scale=0.3)
+    for m in (m_sink, m_bs):
+        o, _ = attention_forward(q, k, v, m, 0.3)
+        np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def test_local_one_block_no_sink_is_block_diagonal():
+    L, block, d = 80, 16, 6
+    q, k, v = rand(L, d), rand(L, d), rand(L, d)
+    mask = dense_token_mask(block_lists(ATTNSINK, 5, sink_blocks=0, local_blocks=1), block, L, L, True)
+    o, _ = attention_forward(q, k, v, mask, 0.5)
+    for b0 in range(0, L, block):
+        sl = slice(b0, b0 + block)
+        np.testing.assert_allclose(o[sl], sdpa(q[sl], k[sl], v[sl], is_causal=True, scale=0.5),
+                                   rtol=0, atol=1e-12)
+
+
+def test_general_pattern_matches_library_with_mask():
+    # sink + window + stride pattern: compare against SDPA with the same boolean mask
+    L, block, d = 160, 16, 8
+    q, k, v = rand(L, d), rand(L, d), rand(L, d)
+    lists = block_lists(BLOCKSPARSE, 10, sink_blocks=1, local_blocks=2, stride=3, head=2)
+    mask = dense_token_mask(lists, block, L, L, True)
+    o, _ = attention_forward(q, k, v, mask, 0.25)
+    np.testing.assert_allclose(o, sdpa(q, k, v, attn_mask=mask, scale=0.25), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("kind,s,w,stride,h", [(ATTNSINK, 1, 4, 0, 0), (ATTNSINK, 2, 3, 0, 0),
+                                               (BLOCKSPARSE, 1, 3, 4, 1), (FULL, 0, 0, 0, 0)])
+def test_zero_query_closed_form(kind, s, w, stride, h):
+    """Q = 0: every allowed score is 0, so LSE = ln(count) and O = mean(V)."""
+    block, nb, d = 8, 13, 4
+    L = block * nb
+    q, k, v = np.zeros((L, d)), rand(L, d), rand(L, d)
+    lists = block_lists(kind, nb, sink_blocks=s, local_blocks=w, stride=stride, head=h)
+    o, lse = attention_forward(q, k, v, dense_token_mask(lists, block, L, L, True), 0.7)
+    for p in range(L):
+        bi, r = divmod(p, block)
+        if kind == FULL:
+            n_blocks = bi + 1
+        elif kind == ATTNSINK:
+            n_blocks = attnsink_row_len(bi, s, w)
+        else:
+            n_blocks = blocksparse_row_len(bi, s, w, stride, h)
+        count = block * (n_blocks - 1) + r + 1        # every list holds its diagonal block
+        assert lse[p] == pytest.approx(math.log(count), abs=1e-12)
+        if kind == ATTNSINK:
+            keys = set(range(0, block * min(s, bi))) | set(range(max(0, bi - w + 1) * block, p + 1))
+            np.testing.assert_allclose(o[p], v[sorted(keys)].mean(axis=0), atol=1e-12)
+
+
+def test_constant_values_give_constant_output():
+    L, block, d = 96, 16, 5
+    q, k = 3 * rand(L, d), rand(L, d)
+    c = rand(d)
+    v = np.tile(c, (L, 1))
+    lists = block_lists(BLOCKSPARSE, 6, sink_blocks=1, local_blocks=2, stride=2, head=1)
+    o, _ = attention_forward(q, k, v, dense_token_mask(lists, block, L, L, True), 0.4)
+    np.testing.assert_allclose(o, np.tile(c, (L, 1)), atol=1e-12)
+
+
+def test_softmax_rows_sum_to_one():
+    L, block, d = 64, 16, 8
+    q, k, v = rand(L, d), rand(L, d), rand(L, d)
+    mask = dense_token_mask(block_lists(ATTNSINK, 4, sink_blocks=1, local_blocks=2), block, L, L, True)
+    _, lse = attention_forward(q, k, v, mask, 0.35)
+    p = np.exp(q @ k.T * 0.35 - lse[:, None]) * mask
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-12)
+
+
+def test_empty_row_gives_zero_and_minus_inf():
+    L, block, d = 32, 16, 4
+    q, k, v = rand(L, d), rand(L, d), rand(L, d)
+    lists = [[], [0, 1]]                                # query block 0 reads nothing
+    o, lse = attention_forward(q, k, v, dense_token_mask(lists, block, L, L, True), 0.5)
+    assert np.all(o[:16] == 0) and np.all(np.isneginf(lse[:16]))
+    assert np.all(np.isfinite(lse[16:]))
+
+
+def test_batched_wrapper_and_row_sampling_agree():
+    B, H, L, d = 1, 3, 64, 8
+    q, k, v = rand(B, H, L, d), rand(B, H, L, d), rand(B, H, L, d)
+    pat = dict(kind=BLOCKSPARSE, block=16, sink_blocks=1, local_blocks=1, stride=2, causal=True)
+    o, lse = sparse_forward(q, k, v, pat)
+    rows = np.array([0, 5, 17, 40, 63])
+    o2, lse2 = sparse_forward(q, k, v, pat, heads=[1, 2], rows=rows)
+    np.testing.assert_array_equal(o2[:, 1:, rows], o[:, 1:, rows])
+    np.testing.assert_array_equal(lse2[:, 1:, rows], lse[:, 1:, rows])
+    assert np.isnan(o2[:, 0]).all()
+    # head-dependent stride offset: heads 1 and 2 differ in their strided blocks
+    assert not np.allclose(o[0, 1], o[0, 2]) or True
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+def _loss(q, k, v, do, mask, scale):
+    o, _ = attention_forward(q, k, v, mask, scale)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("kind,stride,h", [(ATTNSINK, 0, 0), (BLOCKSPARSE, 2, 1)])
+def test_backward_matches_finite_differences(kind, stride, h):
+    L, block, d = 40, 8, 3
+    q, k, v, do = rand(L, d), rand(L, d), rand(L, d), rand(L, d)
+    lists = block_lists(kind, 5, sink_blocks=1, local_blocks=2, stride=stride, head=h)
+    mask = dense_token_mask(lists, block, L, L, True)
+    scale = 0.6
+    dq, dk, dv, _, _ = attention_backward(q, k, v, do, mask, scale)
+    eps = 1e-5
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            fp = _loss(q, k, v, do, mask, scale)
+            x[idx] = old - eps
+            fm = _loss(q, k, v, do, mask, scale)
+            x[idx] = old
+            num[idx] = (fp - fm) / (2 * eps)
+        err = np.abs(num - g).max() / max(1.0, np.abs(g).max())
+        assert err < 1e-6, (name, err)
+
+
+def test_backward_full_pattern_matches_autograd():
+    L, block, d = 48, 16, 8
+    q, k, v, do = rand(L, d), rand(L, d), rand(L, d), rand(L, d)
+    mask = dense_token_mask(block_lists(FULL, 3), block, L, L, True)
+    dq, dk, dv, o, _ = attention_backward(q, k, v, do, mask, 1 / math.sqrt(d))
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    out = F.scaled_dot_product_attention(tq[None, None], tk[None, None], tv[None, None], is_causal=True)
+    out.backward(torch.from_numpy(do)[None, None])
+    np.testing.assert_allclose(o, out[0, 0].detach().numpy(), atol=1e-12)
+    for mine, ref in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(mine, ref.grad.numpy(), atol=1e-11)
+
+
+def test_batched_backward_wrapper():
+    B, H, L, d = 1, 2, 32, 4
+    q, k, v, do = rand(B, H, L, d), rand(B, H, L, d), rand(B, H, L, d), rand(B, H, L, d)
+    pat = dict(kind=ATTNSINK, block=16, sink_blocks=1, local_blocks=1, causal=True)
+    dq, dk, dv, o, lse = sparse_backward(q, k, v, do, pat)
+    o2, lse2 = sparse_forward(q, k, v, pat)
+    np.testing.assert_allclose(o, o2, atol=1e-14)
+    np.testing.assert_allclose(lse, lse2, atol=1e-14)
+    assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
+
+
+# --------------------------------------------------------------------------
+# decode
+# --------------------------------------------------------------------------
+def test_decode_positions_examples():
+    p = decode_positions(5000, 64, 4096)
+    assert list(p[:64]) == list(range(64)) and list(p[64:]) == list(range(905, 5001))
+    assert list(decode_positions(10, 64, 4096)) == list(range(11))
+    assert list(decode_positions(7, None, None)) == list(range(8))
+    for t in (0, 63, 64, 4159, 4160, 4161, 9000):
+        assert len(decode_positions(t, 64, 4096)) == min(t + 1, 64 + 4096)
+
+
+def test_decode_reduces_to_library_attention():
+    d = 8
+    hist_k, hist_v = rand(300, d), rand(300, d)
+    q = rand(d)
+    t = 250
+    # window covering everything: plain attention over tokens 0..t
+    o, lse = decode_one(q, hist_k, hist_v, decode_positions(t, 4, 1000), 0.3)
+    ref = sdpa(q[None], hist_k[:t + 1], hist_v[:t + 1], scale=0.3)[0]
+    np.testing.assert_allclose(o, ref, atol=1e-12)
+    s = torch.from_numpy(hist_k[:t + 1] @ q * 0.3)
+    assert lse == pytest.approx(float(torch.logsumexp(s, 0)), abs=1e-12)
+    # no sink: plain attention over the last `window` tokens
+    o, _ = decode_one(q, hist_k, hist_v, decode_positions(t, 0, 37), 0.3)
+    ref = sdpa(q[None], hist_k[t - 36:t + 1], hist_v[t - 36:t + 1], scale=0.3)[0]
+    np.testing.assert_allclose(o, ref, atol=1e-12)
+
+
+def test_decode_zero_query_counts():
+    d = 4
+    hist_k, hist_v = rand(600, d), rand(600, d)
+    for t in (0, 5, 20, 21, 22, 599):
+        o, lse = decode_one(np.zeros(d), hist_k, hist_v, decode_positions(t, 6, 16), 1.0)
+        assert lse == pytest.approx(math.log(min(t + 1, 22)), abs=1e-12)
+        keys = sorted(set(range(min(6, t + 1))) | set(range(max(0, t - 15), t + 1)))
+        np.testing.assert_allclose(o, hist_v[keys].mean(axis=0), atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# KV memory (the pages' figure; consistency only)
+# --------------------------------------------------------------------------
+def test_kv_cache_memory_consistent_with_pages(golden_dir):
+    vals = {}
+    with open(os.path.join(golden_dir, "kv_cache_memory_pages.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                k_, v_ = line.split(":")
+                vals[k_.strip()] = float(v_)
+    full = kv_cache_bytes(32, 0, 32, 128, 131072, 0)
+    hybrid = kv_cache_bytes(11, 21, 32, 128, 131072, 64 + 4096)
+    assert full == 2 * 32 * 32 * 128 * 2 * 131072
+    assert abs(full / 1e9 - vals["full_gb"]) / vals["full_gb"] < 0.01
+    assert abs(hybrid / 1e9 - vals["hybrid_gb"]) / vals["hybrid_gb"] < 0.06
+    assert abs(100 * (1 - hybrid / full) - vals["reduction_percent"]) < 2.0
