@@ -1,0 +1,237 @@
+/*
+ * attn_sparse.h -- C ABI of the MI355X (gfx950) static block-sparse attention
+ * library (libattn_sparse.so).
+ *
+ * The method: LongGen ("A Little Goes a Long Way: Efficient Long Context
+ * Training and Inference with Partial Contexts") keeps one third of the layers
+ * on full attention and makes the other two thirds sparse with fixed,
+ * GPU-friendly patterns: attention sink (initial tokens), window attention
+ * (recent tokens) and blockwise sparse attention (strided token blocks)
+ * [mlsanity index page, "Abstract (arXiv)"].  Sparse layers sit at the top and
+ * bottom and full layers in the middle; the sparsity is static and block-wise
+ * [atlas.scime.ai summary, "Approach"].  Sparse layers keep a reduced KV cache
+ * during decoding [same summary, "Key results"].
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are contiguous, row-major [B, H, L, d] (batch, head, token,
+ *    head dim).  LSE is float32 [B, H, L]: the natural log of the sum of
+ *    exp(scale * q.k) over the keys a query may see.
+ *  - A "block" is 64 consecutive tokens.  L must be a multiple of 64.
+ *  - Device pointers are HIP device (or managed) pointers; `stream` is a
+ *    hipStream_t passed as void* (NULL = the default stream).
+ *  - Ownership: the caller allocates and frees every buffer (tensors, index,
+ *    workspace).  The library allocates no device memory, keeps no mutable
+ *    global state, and is reentrant.
+ *  - Errors: arguments are checked synchronously.  On a negative status
+ *    nothing has been enqueued and no output has been touched.  A failed
+ *    kernel launch returns ATTN_ERR_HIP.  Faults inside kernels surface at the
+ *    caller's next synchronisation of `stream`.  No C++ exception crosses the
+ *    ABI.
+ *  - Kernels treat a malformed device index defensively: row pointers are
+ *    clamped to [0, nnz] and out-of-range block ids are skipped, so a bad
+ *    index gives wrong numbers, never an out-of-bounds access.  Use
+ *    attn_index_validate on the host copy before uploading it.
+ */
+#ifndef ATTN_SPARSE_H
+#define ATTN_SPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1, /* null pointer, bad size, L % 64 != 0, ...      */
+  ATTN_ERR_UNSUPPORTED = -2, /* valid request this build does not implement  */
+  ATTN_ERR_BAD_INDEX = -3,   /* malformed block index (host validation)      */
+  ATTN_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required   */
+  ATTN_ERR_HIP = -5          /* HIP runtime error (launch / device query)    */
+} attn_status_t;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+/* Pattern kinds.  Full: every key block up to the diagonal.  AttnSink: sink
+ * blocks plus a window of the most recent blocks.  BlockSparse: AttnSink plus
+ * strided earlier blocks whose phase depends on the head. */
+typedef enum { ATTN_FULL = 0, ATTN_ATTNSINK = 1, ATTN_BLOCKSPARSE = 2 } attn_kind_t;
+
+/* Operation ids for attn_workspace_bytes. */
+typedef enum {
+  ATTN_OP_FWD = 0,
+  ATTN_OP_BWD = 1,
+  ATTN_OP_SPARSE_DECODE = 2,
+  ATTN_OP_FULL_DECODE = 3
+} attn_op_t;
+
+/* Static pattern description (host struct, passed by pointer).
+ * Query block i (tokens 64i..64i+63) reads key block j when
+ *   j <  sink_blocks and j <= i                              (sink)
+ *   i - local_blocks < j <= i                                (window; it
+ *                                                             holds the diagonal)
+ *   kind == BLOCKSPARSE, j < i and (j + h) % stride == 0     (strided; h = head)
+ * Full ignores the other fields and reads every j <= i.  With causal != 0,
+ * keys later than the query token are masked inside any block. */
+typedef struct {
+  int32_t kind;         /* attn_kind_t                                       */
+  int32_t block;        /* tokens per block; must be 64                      */
+  int32_t sink_blocks;  /* >= 0                                              */
+  int32_t local_blocks; /* >= 1 for AttnSink / BlockSparse                   */
+  int32_t stride;       /* BlockSparse: >= 1; otherwise ignored              */
+  int32_t causal;       /* 1: mask key position > query position             */
+} attn_pattern_t;
+
+/* Block index in CSR form (and its transpose, CSC, for the backward pass).
+ * Offsets are global into col_idx / row_idx.  Head hh of the index owns
+ *   row_ptr[hh*(n_qblocks+1) .. hh*(n_qblocks+1)+n_qblocks]
+ *   col_ptr[hh*(n_kblocks+1) .. hh*(n_kblocks+1)+n_kblocks].
+ * n_heads is either 1 (one pattern broadcast to every head) or H (attention
+ * head h uses index head h).  Lists are strictly ascending.  For the kernels
+ * every pointer is a device pointer; for attn_index_validate they are host
+ * pointers. */
+typedef struct {
+  int32_t n_heads;
+  int32_t n_qblocks;
+  int32_t n_kblocks;
+  int64_t nnz;            /* total entries in col_idx (== in row_idx)       */
+  const int32_t *row_ptr; /* [n_heads*(n_qblocks+1)]                        */
+  const int32_t *col_idx; /* [nnz]                                         */
+  const int32_t *col_ptr; /* [n_heads*(n_kblocks+1)] or NULL (forward only) */
+  const int32_t *row_idx; /* [nnz] or NULL                                  */
+} attn_index_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *attn_status_str(attn_status_t status);
+
+/* ---------------------------------------------------------------------------
+ * Host helpers: pure CPU, no HIP calls, caller-owned host buffers.
+ * ------------------------------------------------------------------------- */
+
+/* Total entries of the index of `pattern` for n_heads index heads and L
+ * tokens (L % block == 0), written to *nnz_out. */
+attn_status_t attn_index_nnz(const attn_pattern_t *pattern, int32_t n_heads,
+                             int64_t L, int64_t *nnz_out);
+
+/* Builds the index of `pattern` into caller buffers sized as in attn_index_t
+ * (nnz from attn_index_nnz).  Index head hh uses stride phase hh.  col_ptr
+ * and row_idx may both be NULL (forward-only index). */
+attn_status_t attn_index_build(const attn_pattern_t *pattern, int32_t n_heads,
+                               int64_t L, int32_t *row_ptr, int32_t *col_idx,
+                               int32_t *col_ptr, int32_t *row_idx);
+
+/* Checks a HOST copy of an index: monotone pointers within [0, nnz], block
+ * ids in range and strictly ascending, and (when present) that the CSC is
+ * exactly the transpose of the CSR.  Returns ATTN_ERR_BAD_INDEX otherwise. */
+attn_status_t attn_index_validate(const attn_index_t *host_index);
+
+/* Hybrid layer map: is_full[l] = 1 for full_first <= l <= full_last, else 0
+ * (one third full layers in the middle, sparse at top and bottom:
+ * atlas.scime.ai summary, "Approach"). */
+attn_status_t attn_layer_map(int32_t n_layers, int32_t full_first,
+                             int32_t full_last, uint8_t *is_full);
+
+/* Workspace bytes needed by an operation (0 if none).  `L_or_cap` is L for
+ * prefill ops and the cache capacity (full decode) or sink+window (sparse
+ * decode) for decode ops. */
+size_t attn_workspace_bytes(int32_t op, attn_dtype_t dtype, int32_t B,
+                            int32_t H, int64_t L_or_cap, int32_t d);
+
+/* ---------------------------------------------------------------------------
+ * Device operations: validate synchronously, then enqueue on `stream`.
+ * ------------------------------------------------------------------------- */
+
+/* Prefill forward (LongGen sparse layers; full layers with a Full index).
+ * For every (b, h) and query token i: O[i] = softmax(scale * q_i K_S^T) V_S
+ * over the allowed key set S of i, LSE[i] = log sum exp(scale * q_i K_S^T).
+ *   dtype: ATTN_BF16 (q/k/v/o bf16, fp32 accumulation) or ATTN_F32 (all
+ *          fp32).  d in {64, 128}.  pattern->block == 64, L % 64 == 0.
+ *   dev_index: device CSR for L/64 query and key blocks (CSC unused).
+ *   q, k, v: [B,H,L,d] in; o: [B,H,L,d] out; lse: [B,H,L] fp32 out.
+ *   Rows with no allowed key give O = 0, LSE = -inf.  No workspace. */
+attn_status_t attn_sparse_fwd(attn_dtype_t dtype, int32_t B, int32_t H,
+                              int64_t L, int32_t d, float scale,
+                              const attn_pattern_t *pattern,
+                              const attn_index_t *dev_index, const void *q,
+                              const void *k, const void *v, void *o,
+                              float *lse, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Backward of the prefill forward, for context-extension training (the
+ * LongGen sparse layers are trained during length extension: mlsanity index
+ * page, "Abstract (arXiv)").  With P the masked softmax and loss gradients
+ * dO: D = rowsum(dO*O), dV = P^T dO, dS = P*(dO V^T - D), dQ = scale dS K,
+ * dK = scale dS^T Q.
+ *   dtype: ATTN_BF16 only; d in {64, 128}.
+ *   dev_index: CSR and CSC (col_ptr/row_idx must be set).
+ *   q, k, v, o, dout: [B,H,L,d] bf16 in; lse: [B,H,L] fp32 in (from the
+ *   forward); dq, dk, dv: [B,H,L,d] bf16 out.
+ *   workspace: attn_workspace_bytes(ATTN_OP_BWD, ...) bytes (device). */
+attn_status_t attn_sparse_bwd(attn_dtype_t dtype, int32_t B, int32_t H,
+                              int64_t L, int32_t d, float scale,
+                              const attn_pattern_t *pattern,
+                              const attn_index_t *dev_index, const void *q,
+                              const void *k, const void *v, const void *o,
+                              const float *lse, const void *dout, void *dq,
+                              void *dk, void *dv, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Decode one new token per sequence in a sparse (sink + window) layer,
+ * against its reduced ring-buffer cache.
+ *   Cache layout: k_cache, v_cache [B,H,S,d] with S = sink_tokens +
+ *   window_tokens.  Token p lives in slot p if p < sink_tokens, else in slot
+ *   sink_tokens + (p - sink_tokens) % window_tokens.
+ *   dev_pos: [B] int64 device, the absolute position t >= 0 of the new token.
+ *   The new token's k_new / v_new ([B,H,1,d]) are written to slot(t); then q
+ *   ([B,H,1,d]) attends to tokens {0..sink-1} U {t-window+1..t}.  The cache
+ *   must already hold those tokens (attn_ring_fill, or earlier decodes).
+ *   o: [B,H,1,d] out; lse: [B,H] fp32 out.  dtype: ATTN_BF16; d in {64,128}.
+ *   A negative position gives o = 0, lse = NaN and appends nothing.
+ *   workspace: attn_workspace_bytes(ATTN_OP_SPARSE_DECODE, ..., S, d). */
+attn_status_t attn_sparse_decode(attn_dtype_t dtype, int32_t B, int32_t H,
+                                 int32_t d, float scale, int32_t sink_tokens,
+                                 int32_t window_tokens, const int64_t *dev_pos,
+                                 const void *q, const void *k_new,
+                                 const void *v_new, void *k_cache,
+                                 void *v_cache, void *o, float *lse,
+                                 void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* Decode one new token per sequence in a full-attention layer.
+ *   k_cache, v_cache: [B,H,capacity,d]; token p lives in slot p.
+ *   dev_pos: [B] int64 device positions t; k_new / v_new go to slot t and q
+ *   attends to slots 0..t.  max_pos: a host-side upper bound on every t
+ *   (sizes the split-KV grid; must be < capacity).  A position outside
+ *   [0, max_pos] gives o = 0, lse = NaN and appends nothing.
+ *   dtype: ATTN_BF16; d in {64, 128}.
+ *   workspace: attn_workspace_bytes(ATTN_OP_FULL_DECODE, ..., max_pos+1, d). */
+attn_status_t attn_full_decode(attn_dtype_t dtype, int32_t B, int32_t H,
+                               int32_t d, float scale, int64_t capacity,
+                               int64_t max_pos, const int64_t *dev_pos,
+                               const void *q, const void *k_new,
+                               const void *v_new, void *k_cache, void *v_cache,
+                               void *o, float *lse, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Fills a sparse layer's ring cache from prefill K/V (the reduced cache of
+ * the LongGen sparse layers: atlas.scime.ai summary, "Key results").
+ *   k_src, v_src: [B,H,src_len,d]; sequence b holds tokens 0..len_b-1 with
+ *   len_b = dev_len[b] (int64 device, 0 <= len_b <= src_len).
+ *   Copies tokens 0..min(sink,len_b)-1 and the last `window_tokens` tokens
+ *   (never below position sink_tokens) into their slots of k_cache/v_cache
+ *   [B,H,sink+window,d] (slot rule as in attn_sparse_decode).  Slots of
+ *   tokens that do not exist are left untouched.  dtype: ATTN_BF16. */
+attn_status_t attn_ring_fill(attn_dtype_t dtype, int32_t B, int32_t H,
+                             int32_t d, int32_t sink_tokens,
+                             int32_t window_tokens, const int64_t *dev_len,
+                             const void *k_src, const void *v_src,
+                             int64_t src_len, void *k_cache, void *v_cache,
+                             void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_SPARSE_H */

@@ -1,0 +1,222 @@
+// C ABI entry points: synchronous argument checks, then dispatch to the HIP
+// launchers.  Nothing is enqueued when a check fails.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn_sparse.h"
+#include "kernels.h"
+
+namespace {
+
+using attn::IndexView;
+
+bool index_shape_ok(const attn_index_t *ix, int32_t H, int64_t L, bool need_csc) {
+  if (!ix || !ix->row_ptr || !ix->col_idx) return false;
+  if (ix->n_heads != 1 && ix->n_heads != H) return false;
+  if (ix->n_qblocks != L / attn::kBlock || ix->n_kblocks != L / attn::kBlock) return false;
+  if (ix->nnz < 0 || ix->nnz > INT32_MAX) return false;
+  if (need_csc && (!ix->col_ptr || !ix->row_idx)) return false;
+  return true;
+}
+
+IndexView view_of(const attn_index_t *ix) {
+  IndexView v;
+  v.row_ptr = ix->row_ptr;
+  v.col_idx = ix->col_idx;
+  v.col_ptr = ix->col_ptr;
+  v.row_idx = ix->row_idx;
+  v.n_heads = ix->n_heads;
+  v.n_qblocks = ix->n_qblocks;
+  v.n_kblocks = ix->n_kblocks;
+  v.nnz = (int32_t)ix->nnz;
+  return v;
+}
+
+bool prefill_dims_ok(int32_t B, int32_t H, int64_t L, int32_t d, float scale,
+                     const attn_pattern_t *p) {
+  if (B < 1 || H < 1 || L < attn::kBlock || L % attn::kBlock != 0) return false;
+  if (!p || p->block != attn::kBlock) return false;
+  if (!(scale > 0.f) || !isfinite(scale)) return false;
+  // int32 token / tile arithmetic inside the kernels
+  if ((int64_t)B * H * L > INT32_MAX) return false;
+  (void)d;
+  return true;
+}
+
+attn_status_t hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+size_t decode_ws_bytes(int32_t B, int32_t H, int64_t n_keys, int32_t d) {
+  int32_t ns = 0, len = 0;
+  attn::decode_split_plan(B, H, n_keys, &ns, &len);
+  return (size_t)B * H * ns * (d + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_workspace_bytes(int32_t op, attn_dtype_t dtype, int32_t B, int32_t H,
+                            int64_t L_or_cap, int32_t d) {
+  (void)dtype;
+  if (B < 1 || H < 1 || L_or_cap < 1 || d < 1) return 0;
+  switch (op) {
+    case ATTN_OP_FWD: return 0;
+    case ATTN_OP_BWD: return (size_t)B * H * L_or_cap * sizeof(float);
+    case ATTN_OP_SPARSE_DECODE:
+    case ATTN_OP_FULL_DECODE: return decode_ws_bytes(B, H, L_or_cap, d);
+  }
+  return 0;
+}
+
+attn_status_t attn_sparse_fwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t L, int32_t d,
+                              float scale, const attn_pattern_t *pattern,
+                              const attn_index_t *dev_index, const void *q, const void *k,
+                              const void *v, void *o, float *lse, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!prefill_dims_ok(B, H, L, d, scale, pattern)) return ATTN_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
+  if (!index_shape_ok(dev_index, H, L, false)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  attn::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.ix = view_of(dev_index);
+  a.B = B;
+  a.H = H;
+  a.L = (int32_t)L;
+  a.d = d;
+  a.scale = scale;
+  a.causal = pattern->causal ? 1 : 0;
+  hipStream_t s = (hipStream_t)stream;
+  return hip_status(dtype == ATTN_BF16 ? attn::launch_fwd_bf16(a, s) : attn::launch_fwd_f32(a, s));
+}
+
+attn_status_t attn_sparse_bwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t L, int32_t d,
+                              float scale, const attn_pattern_t *pattern,
+                              const attn_index_t *dev_index, const void *q, const void *k,
+                              const void *v, const void *o, const float *lse, const void *dout,
+                              void *dq, void *dk, void *dv, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  if (!prefill_dims_ok(B, H, L, d, scale, pattern)) return ATTN_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
+  if (!index_shape_ok(dev_index, H, L, true)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = attn_workspace_bytes(ATTN_OP_BWD, dtype, B, H, L, d);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  attn::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = (float *)workspace;
+  a.ix = view_of(dev_index);
+  a.B = B;
+  a.H = H;
+  a.L = (int32_t)L;
+  a.d = d;
+  a.scale = scale;
+  a.causal = pattern->causal ? 1 : 0;
+  return hip_status(attn::launch_bwd_bf16(a, (hipStream_t)stream));
+}
+
+static attn_status_t decode_common(attn_dtype_t dtype, int32_t B, int32_t H, int32_t d,
+                                   float scale, int64_t cap, int32_t sink, int32_t window,
+                                   int64_t max_pos, const int64_t *dev_pos, const void *q,
+                                   const void *k_new, const void *v_new, void *k_cache,
+                                   void *v_cache, void *o, float *lse, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  if (B < 1 || H < 1 || !(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (!dev_pos || !q || !k_new || !v_new || !k_cache || !v_cache || !o || !lse)
+    return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * H > INT32_MAX / 4) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const int64_t n_keys = sink >= 0 ? cap : max_pos + 1;
+  const size_t need = decode_ws_bytes(B, H, n_keys, d);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  attn::DecodeArgs a;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.o = o;
+  a.lse = lse;
+  a.pos = dev_pos;
+  a.part = (float *)workspace;
+  a.B = B;
+  a.H = H;
+  a.d = d;
+  a.cap = cap;
+  a.sink = sink;
+  a.window = window;
+  a.max_pos = max_pos;
+  attn::decode_split_plan(B, H, n_keys, &a.n_split, &a.split_len);
+  a.scale = scale;
+  return hip_status(attn::launch_decode_bf16(a, (hipStream_t)stream));
+}
+
+attn_status_t attn_sparse_decode(attn_dtype_t dtype, int32_t B, int32_t H, int32_t d, float scale,
+                                 int32_t sink_tokens, int32_t window_tokens,
+                                 const int64_t *dev_pos, const void *q, const void *k_new,
+                                 const void *v_new, void *k_cache, void *v_cache, void *o,
+                                 float *lse, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+  if (sink_tokens < 0 || window_tokens < 1) return ATTN_ERR_INVALID_ARG;
+  const int64_t cap = (int64_t)sink_tokens + window_tokens;
+  if (cap > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  return decode_common(dtype, B, H, d, scale, cap, sink_tokens, window_tokens, 0, dev_pos, q,
+                       k_new, v_new, k_cache, v_cache, o, lse, workspace, workspace_bytes,
+                       stream);
+}
+
+attn_status_t attn_full_decode(attn_dtype_t dtype, int32_t B, int32_t H, int32_t d, float scale,
+                               int64_t capacity, int64_t max_pos, const int64_t *dev_pos,
+                               const void *q, const void *k_new, const void *v_new,
+                               void *k_cache, void *v_cache, void *o, float *lse,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  if (capacity < 1 || max_pos < 0 || max_pos >= capacity) return ATTN_ERR_INVALID_ARG;
+  if (max_pos + 1 > (int64_t)INT32_MAX * 256) return ATTN_ERR_INVALID_ARG;
+  return decode_common(dtype, B, H, d, scale, capacity, -1, 0, max_pos, dev_pos, q, k_new, v_new,
+                       k_cache, v_cache, o, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_ring_fill(attn_dtype_t dtype, int32_t B, int32_t H, int32_t d,
+                             int32_t sink_tokens, int32_t window_tokens, const int64_t *dev_len,
+                             const void *k_src, const void *v_src, int64_t src_len,
+                             void *k_cache, void *v_cache, void *stream) {
+  if (B < 1 || H < 1 || sink_tokens < 0 || window_tokens < 1 || src_len < 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (!dev_len || !k_src || !v_src || !k_cache || !v_cache) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * H > 65535) return ATTN_ERR_INVALID_ARG;  // grid.y limit
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  attn::RingFillArgs a;
+  a.k_src = k_src;
+  a.v_src = v_src;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.len = dev_len;
+  a.src_len = src_len;
+  a.B = B;
+  a.H = H;
+  a.d = d;
+  a.sink = sink_tokens;
+  a.window = window_tokens;
+  return hip_status(attn::launch_ring_fill_bf16(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,176 @@
+// Host-side static block index: CSR (per query block) and CSC (per key block)
+// lists of the LongGen sparse patterns, plus the hybrid layer map.
+//
+// Patterns: attention sink (initial tokens), window attention (recent tokens)
+// and blockwise sparse attention (strided token blocks) [LongGen, mlsanity
+// index page "A Little Goes a Long Way...", "Abstract (arXiv)"]; the access
+// is static and block-wise, sparse layers at the top and bottom, full layers
+// in the middle [atlas.scime.ai summary, "Approach"].
+//
+// Each row is generated directly in ascending order as
+//   sink blocks [0, min(sink, i+1))
+//   strided blocks in [sink, a) with (j + h) % stride == 0   (BlockSparse)
+//   window blocks [max(a, sink), i]          with a = max(0, i - local + 1)
+// which is a disjoint, sorted partition of the set the header defines.
+
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "../../include/attn_sparse.h"
+
+namespace {
+
+bool pattern_ok(const attn_pattern_t *p, int64_t L) {
+  if (!p || p->block <= 0 || L <= 0 || L % p->block != 0) return false;
+  if (L / p->block > INT32_MAX - 1) return false;
+  if (p->kind == ATTN_FULL) return true;
+  if (p->kind != ATTN_ATTNSINK && p->kind != ATTN_BLOCKSPARSE) return false;
+  if (p->sink_blocks < 0 || p->local_blocks < 1) return false;
+  if (p->kind == ATTN_BLOCKSPARSE && p->stride < 1) return false;
+  return true;
+}
+
+// Appends the row of query block i for head h to `out`; returns its length.
+template <class Sink>
+int64_t emit_row(const attn_pattern_t *p, int64_t i, int32_t h, Sink &&sink) {
+  int64_t n = 0;
+  if (p->kind == ATTN_FULL) {
+    for (int64_t j = 0; j <= i; ++j) sink(j), ++n;
+    return n;
+  }
+  const int64_t s = p->sink_blocks;
+  const int64_t a = std::max<int64_t>(0, i - p->local_blocks + 1);
+  const int64_t sink_end = std::min<int64_t>(s, i + 1);
+  for (int64_t j = 0; j < sink_end; ++j) sink(j), ++n;
+  if (p->kind == ATTN_BLOCKSPARSE) {
+    const int64_t st = p->stride;
+    // first j >= s with (j + h) % st == 0
+    int64_t r = ((-(int64_t)h) % st + st) % st;
+    int64_t j0 = s <= r ? r : r + ((s - r + st - 1) / st) * st;
+    for (int64_t j = j0; j < a; j += st) sink(j), ++n;
+  }
+  for (int64_t j = std::max(a, s); j <= i; ++j) sink(j), ++n;
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_status_str(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_BAD_INDEX: return "malformed block index";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+attn_status_t attn_index_nnz(const attn_pattern_t *p, int32_t n_heads, int64_t L,
+                             int64_t *nnz_out) {
+  if (!nnz_out || n_heads < 1 || !pattern_ok(p, L)) return ATTN_ERR_INVALID_ARG;
+  const int64_t nb = L / p->block;
+  int64_t total = 0;
+  const int32_t distinct = p->kind == ATTN_BLOCKSPARSE ? n_heads : 1;
+  for (int32_t h = 0; h < distinct; ++h)
+    for (int64_t i = 0; i < nb; ++i) total += emit_row(p, i, h, [](int64_t) {});
+  if (distinct == 1) total *= n_heads;
+  if (total > INT32_MAX) return ATTN_ERR_UNSUPPORTED;  // int32 offsets
+  *nnz_out = total;
+  return ATTN_OK;
+}
+
+attn_status_t attn_index_build(const attn_pattern_t *p, int32_t n_heads, int64_t L,
+                               int32_t *row_ptr, int32_t *col_idx, int32_t *col_ptr,
+                               int32_t *row_idx) {
+  int64_t nnz = 0;
+  attn_status_t st = attn_index_nnz(p, n_heads, L, &nnz);
+  if (st != ATTN_OK) return st;
+  if (!row_ptr || !col_idx) return ATTN_ERR_INVALID_ARG;
+  if ((col_ptr == nullptr) != (row_idx == nullptr)) return ATTN_ERR_INVALID_ARG;
+  const int64_t nb = L / p->block;
+  int64_t off = 0;
+  for (int32_t h = 0; h < n_heads; ++h) {
+    const int64_t head_start = off;
+    int32_t *rp = row_ptr + (int64_t)h * (nb + 1);
+    for (int64_t i = 0; i < nb; ++i) {
+      rp[i] = (int32_t)off;
+      emit_row(p, i, h, [&](int64_t j) { col_idx[off++] = (int32_t)j; });
+    }
+    rp[nb] = (int32_t)off;
+    if (col_ptr) {
+      int32_t *cp = col_ptr + (int64_t)h * (nb + 1);
+      std::vector<int64_t> count(nb + 1, 0);
+      for (int64_t e = head_start; e < off; ++e) count[col_idx[e]]++;
+      int64_t acc = head_start;
+      for (int64_t j = 0; j < nb; ++j) {
+        cp[j] = (int32_t)acc;
+        int64_t c = count[j];
+        count[j] = acc;  // becomes the fill cursor
+        acc += c;
+      }
+      cp[nb] = (int32_t)acc;
+      for (int64_t i = 0; i < nb; ++i)  // rows visited in order -> ascending
+        for (int64_t e = rp[i]; e < rp[i + 1]; ++e) row_idx[count[col_idx[e]]++] = (int32_t)i;
+    }
+  }
+  return ATTN_OK;
+}
+
+attn_status_t attn_index_validate(const attn_index_t *ix) {
+  if (!ix || ix->n_heads < 1 || ix->n_qblocks < 1 || ix->n_kblocks < 1 || ix->nnz < 0 ||
+      ix->nnz > INT32_MAX || !ix->row_ptr || (ix->nnz > 0 && !ix->col_idx))
+    return ATTN_ERR_INVALID_ARG;
+  if ((ix->col_ptr == nullptr) != (ix->row_idx == nullptr)) return ATTN_ERR_INVALID_ARG;
+  const int64_t nq = ix->n_qblocks, nk = ix->n_kblocks, nnz = ix->nnz;
+  for (int32_t h = 0; h < ix->n_heads; ++h) {
+    const int32_t *rp = ix->row_ptr + (int64_t)h * (nq + 1);
+    for (int64_t i = 0; i < nq; ++i) {
+      if (rp[i] < 0 || rp[i + 1] < rp[i] || rp[i + 1] > nnz) return ATTN_ERR_BAD_INDEX;
+      for (int64_t e = rp[i]; e < rp[i + 1]; ++e) {
+        const int32_t j = ix->col_idx[e];
+        if (j < 0 || j >= nk) return ATTN_ERR_BAD_INDEX;
+        if (e > rp[i] && ix->col_idx[e - 1] >= j) return ATTN_ERR_BAD_INDEX;
+      }
+    }
+  }
+  if (!ix->col_ptr) return ATTN_OK;
+  // CSC must be the exact transpose of the CSR, head by head.
+  for (int32_t h = 0; h < ix->n_heads; ++h) {
+    const int32_t *rp = ix->row_ptr + (int64_t)h * (nq + 1);
+    const int32_t *cp = ix->col_ptr + (int64_t)h * (nk + 1);
+    for (int64_t j = 0; j < nk; ++j) {
+      if (cp[j] < 0 || cp[j + 1] < cp[j] || cp[j + 1] > nnz) return ATTN_ERR_BAD_INDEX;
+      for (int64_t e = cp[j]; e < cp[j + 1]; ++e) {
+        const int32_t i = ix->row_idx[e];
+        if (i < 0 || i >= nq) return ATTN_ERR_BAD_INDEX;
+        if (e > cp[j] && ix->row_idx[e - 1] >= i) return ATTN_ERR_BAD_INDEX;
+      }
+    }
+    // same number of entries per head, and every (i, j) of the CSC is in the CSR
+    if ((cp[nk] - cp[0]) != (rp[nq] - rp[0])) return ATTN_ERR_BAD_INDEX;
+    for (int64_t j = 0; j < nk; ++j)
+      for (int64_t e = cp[j]; e < cp[j + 1]; ++e) {
+        const int32_t i = ix->row_idx[e];
+        const int32_t *b = ix->col_idx + rp[i], *en = ix->col_idx + rp[i + 1];
+        if (!std::binary_search(b, en, (int32_t)j)) return ATTN_ERR_BAD_INDEX;
+      }
+  }
+  return ATTN_OK;
+}
+
+attn_status_t attn_layer_map(int32_t n_layers, int32_t full_first, int32_t full_last,
+                             uint8_t *is_full) {
+  if (n_layers < 1 || !is_full) return ATTN_ERR_INVALID_ARG;
+  for (int32_t l = 0; l < n_layers; ++l)
+    is_full[l] = (l >= full_first && l <= full_last) ? 1 : 0;
+  return ATTN_OK;
+}
+
+}  // extern "C"

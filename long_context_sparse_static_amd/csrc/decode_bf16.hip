@@ -1,0 +1,273 @@
+// Single-token decode against a KV cache, bf16 storage / fp32 arithmetic.
+//
+// LongGen's sparse layers keep only their sink and window tokens, which is
+// where its KV-memory saving and decode speedup come from (atlas.scime.ai
+// summary of "A Little Goes a Long Way...", "Key results"; mlsanity index
+// page, "Abstract (arXiv)"); its full layers keep every token.  Decode reads
+// each cached K/V row once, so it is bound by HBM bandwidth: the kernels are
+// written for wide coalesced streaming, not for the matrix cores.
+//
+//   decode_split_kernel  grid (n_split, B*H): one workgroup streams a
+//                        contiguous slot range of one (b, h) and writes a
+//                        partial (m, l, o) in base 2; the workgroup owning
+//                        the new token's slot also appends k_new / v_new
+//                        (every workgroup reads that slot from k_new / v_new,
+//                        so no ordering between them is needed).
+//   decode_combine_kernel grid (B*H): merges the partials, writes o and lse.
+//   ring_fill_kernel     copies prefill K/V into the sink + window ring.
+//
+// Ring slot of token p: p if p < sink, else sink + (p - sink) % window.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecUnroll = 8;  // keys in flight per lane group
+
+__device__ __forceinline__ int64_t ring_slot(int64_t p, int sink, int window) {
+  return p < sink ? p : sink + (p - sink) % window;
+}
+
+// Valid slot count and the new token's slot for position t; false if t is
+// outside what the layer accepts.
+__device__ __forceinline__ bool decode_geometry(const DecodeArgs &a, int64_t t, int64_t *n_valid,
+                                                int64_t *slot_new) {
+  if (a.sink >= 0) {
+    if (t < 0) return false;
+    const int64_t cap = (int64_t)a.sink + a.window;
+    *n_valid = t + 1 < cap ? t + 1 : cap;
+    *slot_new = ring_slot(t, a.sink, a.window);
+  } else {
+    if (t < 0 || t > a.max_pos || t >= a.cap) return false;
+    *n_valid = t + 1;
+    *slot_new = t;
+  }
+  return true;
+}
+
+template <int D>
+__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a) {
+  constexpr int LPK = D / 8;          // lanes per key row (16 bytes each)
+  constexpr int KPW = 64 / LPK;       // keys per wave per step
+  constexpr int NWAVE = kDecThreads / 64;
+  __shared__ float red[NWAVE][D + 2];
+
+  const int split = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.H;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane / LPK, c = lane % LPK;
+  float *part = a.part + ((size_t)bh * a.n_split + split) * (D + 2);
+
+  const int64_t t = a.pos[b];
+  int64_t n_valid = 0, slot_new = -1;
+  const bool ok = decode_geometry(a, t, &n_valid, &slot_new);
+  const int64_t s0 = (int64_t)split * a.split_len;
+  const int64_t s1 = ok ? (s0 + a.split_len < n_valid ? s0 + a.split_len : n_valid) : 0;
+
+  const size_t row0 = (size_t)bh * a.cap;
+  const bf16 *kc = (const bf16 *)a.k_cache + row0 * D;
+  const bf16 *vc = (const bf16 *)a.v_cache + row0 * D;
+  const bf16 *kn = (const bf16 *)a.k_new + (size_t)bh * D;
+  const bf16 *vn = (const bf16 *)a.v_new + (size_t)bh * D;
+
+  // Append the new token (one workgroup per (b, h) owns its slot).
+  if (ok && slot_new >= s0 && slot_new < s1 && threadIdx.x < LPK) {
+    *(u32x4 *)((bf16 *)a.k_cache + (row0 + slot_new) * D + threadIdx.x * 8) =
+        *(const u32x4 *)(kn + threadIdx.x * 8);
+    *(u32x4 *)((bf16 *)a.v_cache + (row0 + slot_new) * D + threadIdx.x * 8) =
+        *(const u32x4 *)(vn + threadIdx.x * 8);
+  }
+
+  const float cs = a.scale * kLog2e;
+  float qf[8];
+  {
+    const u32x4 qw = *(const u32x4 *)((const bf16 *)a.q + (size_t)bh * D + c * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qf[2 * i] = bf16_lo(qw[i]) * cs;
+      qf[2 * i + 1] = bf16_hi(qw[i]) * cs;
+    }
+  }
+  float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+
+  constexpr int STEP = NWAVE * KPW * kDecUnroll;
+  for (int64_t kb = s0 + (int64_t)wave * KPW * kDecUnroll; kb < s1; kb += STEP) {
+    u32x4 kw[kDecUnroll], vw[kDecUnroll];
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int64_t key = kb + u * KPW + g;
+      const int64_t safe = key < s1 ? key : s0;
+      const bf16 *kp = safe == slot_new ? kn : kc + safe * D;
+      const bf16 *vp = safe == slot_new ? vn : vc + safe * D;
+      kw[u] = __builtin_nontemporal_load((const u32x4 *)(kp + c * 8));
+      vw[u] = __builtin_nontemporal_load((const u32x4 *)(vp + c * 8));
+    }
+    float sc[kDecUnroll];
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc = __builtin_fmaf(qf[2 * i], bf16_lo(kw[u][i]), acc);
+        acc = __builtin_fmaf(qf[2 * i + 1], bf16_hi(kw[u][i]), acc);
+      }
+#pragma unroll
+      for (int off = 1; off < LPK; off <<= 1) acc += __shfl_xor(acc, off);
+      const int64_t key = kb + u * KPW + g;
+      sc[u] = key < s1 ? acc : -INFINITY;
+      mx = fmaxf(mx, sc[u]);
+    }
+    if (mx == -INFINITY) continue;
+    const float alpha = fast_exp2(m - mx);  // m = -inf -> 0
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] *= alpha;
+    m = mx;
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const float p = fast_exp2(sc[u] - m);
+      l += p;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __builtin_fmaf(p, bf16_lo(vw[u][i]), o[2 * i]);
+        o[2 * i + 1] = __builtin_fmaf(p, bf16_hi(vw[u][i]), o[2 * i + 1]);
+      }
+    }
+  }
+
+  // Merge the KPW lane groups of this wave (lanes with equal c).
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off);
+    const float l2 = __shfl_xor(l, off);
+    const float mn = fmaxf(m, m2);
+    const float a1 = mn == -INFINITY ? 0.f : fast_exp2(m - mn);
+    const float a2 = mn == -INFINITY ? 0.f : fast_exp2(m2 - mn);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = o[i] * a1 + __shfl_xor(o[i], off) * a2;
+    l = l * a1 + l2 * a2;
+    m = mn;
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[wave][c * 8 + i] = o[i];
+    if (c == 0) {
+      red[wave][D] = m;
+      red[wave][D + 1] = l;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int dd = threadIdx.x;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) mm = fmaxf(mm, red[w][D]);
+    float acc = 0.f, ll = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+      const float sc = mm == -INFINITY ? 0.f : fast_exp2(red[w][D] - mm);
+      acc += red[w][dd] * sc;
+      ll += red[w][D + 1] * sc;
+    }
+    part[dd] = acc;
+    if (dd == 0) {
+      part[D] = mm;
+      part[D + 1] = ll;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+  const int bh = blockIdx.x, b = bh / a.H;
+  const int dd = threadIdx.x;
+  const float *part = a.part + (size_t)bh * a.n_split * (D + 2);
+  int64_t n_valid = 0, slot_new = 0;
+  const bool ok = decode_geometry(a, a.pos[b], &n_valid, &slot_new);
+  const int used = ok ? (int)((n_valid + a.split_len - 1) / a.split_len) : 0;
+  float mm = -INFINITY;
+  for (int s = 0; s < used; ++s) mm = fmaxf(mm, part[(size_t)s * (D + 2) + D]);
+  float acc = 0.f, ll = 0.f;
+  for (int s = 0; s < used; ++s) {
+    const float *ps = part + (size_t)s * (D + 2);
+    const float sc = mm == -INFINITY ? 0.f : fast_exp2(ps[D] - mm);
+    acc += ps[dd] * sc;
+    ll += ps[D + 1] * sc;
+  }
+  const float out = ll > 0.f ? acc / ll : 0.f;
+  ((bf16 *)a.o)[(size_t)bh * D + dd] = (bf16)out;
+  if (dd == 0) a.lse[bh] = !ok ? NAN : (ll > 0.f ? (mm + fast_log2(ll)) * kLn2 : -INFINITY);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void ring_fill_kernel(RingFillArgs a) {
+  constexpr int CPR = D / 8;
+  const int bh = blockIdx.y, b = bh / a.H;
+  const int64_t ring = (int64_t)a.sink + a.window;
+  const int64_t ci = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (ci >= ring * CPR) return;
+  const int64_t r = ci / CPR;
+  const int c = (int)(ci % CPR);
+  int64_t n = a.len[b];
+  if (n < 0) return;
+  if (n > a.src_len) n = a.src_len;
+  int64_t p;
+  if (r < a.sink) {
+    p = r;
+  } else {
+    const int64_t first = n - a.window > a.sink ? n - a.window : (int64_t)a.sink;
+    p = first + (r - a.sink);
+  }
+  if (p >= n) return;
+  const int64_t slot = ring_slot(p, a.sink, a.window);
+  const size_t src = ((size_t)bh * a.src_len + p) * D + c * 8;
+  const size_t dst = ((size_t)bh * ring + slot) * D + c * 8;
+  *(u32x4 *)((bf16 *)a.k_cache + dst) = *(const u32x4 *)((const bf16 *)a.k_src + src);
+  *(u32x4 *)((bf16 *)a.v_cache + dst) = *(const u32x4 *)((const bf16 *)a.v_src + src);
+}
+
+}  // namespace
+
+void decode_split_plan(int32_t B, int32_t H, int64_t n_keys, int32_t *n_split, int32_t *split_len) {
+  // Aim for >= 8 workgroups per CU across 256 CUs, but keep each split at
+  // >= 512 keys so a workgroup streams >= 256 KB (d = 128).
+  const int64_t bh = (int64_t)B * H;
+  int64_t want = (2048 + bh - 1) / bh;
+  int64_t len = (n_keys + want - 1) / want;
+  if (len < 512) len = 512;
+  len = (len + 255) / 256 * 256;
+  int64_t ns = (n_keys + len - 1) / len;
+  if (ns < 1) ns = 1;
+  *n_split = (int32_t)ns;
+  *split_len = (int32_t)len;
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {
+  dim3 grid(a.n_split, a.B * a.H);
+  if (a.d == 128) {
+    hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(kDecThreads), 0, s, a);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(a.B * a.H), dim3(128), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(kDecThreads), 0, s, a);
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(a.B * a.H), dim3(64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_fill_bf16(const RingFillArgs &a, hipStream_t s) {
+  const int64_t ring = (int64_t)a.sink + a.window;
+  const int64_t chunks = ring * (a.d / 8);
+  dim3 grid((unsigned)((chunks + 255) / 256), a.B * a.H);
+  if (a.d == 128)
+    hipLaunchKernelGGL(ring_fill_kernel<128>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(ring_fill_kernel<64>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace attn

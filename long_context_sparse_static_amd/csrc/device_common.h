@@ -1,0 +1,61 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, the bf16
+// MFMA wrapper, wave reductions and the XCD-aware workgroup remap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16) on the CDNA4 matrix cores.
+// Lane l holds A row (l % 32), k = 8*(l/32) .. +7; B column (l % 32) with the
+// same k range; and D column (l % 32), rows 8*(r/4) + 4*(l/32) + r%4 for its
+// 16 registers r.
+__device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8 &a, const bf16x8 &b,
+                                                const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (bf16)lo;
+  v[1] = (bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Workgroups are dealt to the 8 XCDs round-robin (bid % 8).  Remap so that
+// each XCD receives a contiguous range of logical work items, which keeps one
+// head's neighbouring query tiles -- and so its K/V blocks -- in one L2.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  const int xcd = bid % kNumXcd;
+  const int slot = bid / kNumXcd;
+  const int q = total / kNumXcd, r = total % kNumXcd;
+  return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+__device__ __forceinline__ int clamp_i(int x, int lo, int hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
+}  // namespace attn

@@ -1,0 +1,79 @@
+// Internal launcher interface between the C ABI (api.cpp) and the HIP kernels.
+// Every launcher assumes its arguments were validated by the ABI layer and
+// returns a hipError_t from the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+constexpr int kBlock = 64;   // tokens per sparse block (the only size built)
+constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, workgroups dealt round-robin
+
+struct IndexView {
+  const int32_t *row_ptr;
+  const int32_t *col_idx;
+  const int32_t *col_ptr;
+  const int32_t *row_idx;
+  int32_t n_heads;     // 1 (broadcast) or H
+  int32_t n_qblocks;
+  int32_t n_kblocks;
+  int32_t nnz;
+};
+
+struct FwdArgs {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  IndexView ix;
+  int32_t B, H, L, d;
+  float scale;
+  int32_t causal;
+};
+
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  void *dq, *dk, *dv;
+  float *delta;        // workspace: D = rowsum(dO * O), [B,H,L] fp32
+  IndexView ix;
+  int32_t B, H, L, d;
+  float scale;
+  int32_t causal;
+};
+
+struct DecodeArgs {
+  const void *q, *k_new, *v_new;
+  void *k_cache, *v_cache;
+  void *o;
+  float *lse;
+  const int64_t *pos;
+  float *part;         // workspace: [B*H, n_split, d + 2] fp32 partials
+  int32_t B, H, d;
+  int64_t cap;         // slots per (b, h) in the cache
+  int32_t sink, window;  // sparse layers; sink < 0 marks a full layer
+  int64_t max_pos;     // full layers: host bound on positions
+  int32_t n_split, split_len;
+  float scale;
+};
+
+struct RingFillArgs {
+  const void *k_src, *v_src;
+  void *k_cache, *v_cache;
+  const int64_t *len;
+  int64_t src_len;
+  int32_t B, H, d, sink, window;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_ring_fill_bf16(const RingFillArgs &a, hipStream_t s);
+
+// Split-KV sizing shared by the workspace query and the decode launcher.
+void decode_split_plan(int32_t B, int32_t H, int64_t n_keys, int32_t *n_split,
+                       int32_t *split_len);
+
+}  // namespace attn

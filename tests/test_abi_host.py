@@ -1,0 +1,211 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol,
+its host-side index builder matches the oracle's brute-force block lists
+bit-exactly, and argument validation rejects bad calls before any launch."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import long_context_sparse_static_amd as lcs
+from oracle import ATTNSINK, BLOCKSPARSE, FULL, block_lists, transpose_lists
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_sparse.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 11
+    assert sorted(lcs.EXPORTED) == names
+    L = lcs.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    # the shared object itself exports them (nm-free check through dlsym)
+    raw = ctypes.CDLL(lcs.LIB_PATH)
+    for n in names:
+        assert ctypes.cast(getattr(raw, n), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert lcs.attn_status_str(s)
+    assert lcs.attn_status_str(-99) == "unknown status"
+
+
+# ------------------------------------------------------------------ index
+PATTERNS = {
+    # (pattern, oracle kind, kwargs, heads, L)
+    "attnsink_1k": (lcs.attnsink_pattern(1, 4), ATTNSINK, dict(sink_blocks=1, local_blocks=4), 1, 1024),
+    "attnsink_8k": (lcs.attnsink_pattern(1, 64), ATTNSINK, dict(sink_blocks=1, local_blocks=64), 1, 8192),
+    "blocksparse_32k": (lcs.blocksparse_pattern(1, 16, 8), BLOCKSPARSE,
+                        dict(sink_blocks=1, local_blocks=16, stride=8), 32, 32768),
+    "attnsink_64k": (lcs.attnsink_pattern(1, 64), ATTNSINK, dict(sink_blocks=1, local_blocks=64), 1, 65536),
+    "attnsink_128k": (lcs.attnsink_pattern(1, 64), ATTNSINK, dict(sink_blocks=1, local_blocks=64), 1, 131072),
+    "full_32k": (lcs.full_pattern(), FULL, dict(), 1, 32768),
+    "odd_sink2": (lcs.attnsink_pattern(2, 3), ATTNSINK, dict(sink_blocks=2, local_blocks=3), 1, 64 * 37),
+    "odd_bs": (lcs.blocksparse_pattern(3, 5, 7), BLOCKSPARSE, dict(sink_blocks=3, local_blocks=5, stride=7), 9, 64 * 50),
+}
+
+
+@pytest.mark.parametrize("name", list(PATTERNS))
+def test_index_matches_oracle_bit_exact(name):
+    pat, kind, kw, heads, L = PATTERNS[name]
+    nb = L // 64
+    ix = lcs.attn_index_build(pat, heads, L, with_csc=True)
+    lcs.attn_index_validate(ix)
+    for h in range(heads):
+        want = block_lists(kind, nb, head=h, **kw)
+        base = h * (nb + 1)
+        got_rows = np.split(ix.col_idx[ix.row_ptr[base]:ix.row_ptr[base + nb]],
+                            ix.row_ptr[base + 1:base + nb] - ix.row_ptr[base])
+        assert [r.tolist() for r in got_rows] == want, (name, h)
+        cols = transpose_lists(want, nb)
+        cbase = h * (nb + 1)
+        got_cols = np.split(ix.row_idx[ix.col_ptr[cbase]:ix.col_ptr[cbase + nb]],
+                            ix.col_ptr[cbase + 1:cbase + nb] - ix.col_ptr[cbase])
+        assert [c.tolist() for c in got_cols] == cols, (name, h)
+
+
+def test_index_nnz_closed_forms():
+    assert lcs.attn_index_nnz(lcs.attnsink_pattern(1, 4), 1, 1024) == 70
+    assert lcs.attn_index_nnz(lcs.attnsink_pattern(1, 64), 1, 8192) == 6240
+    assert lcs.attn_index_nnz(lcs.attnsink_pattern(1, 64), 1, 65536) == 64480
+    assert lcs.attn_index_nnz(lcs.attnsink_pattern(1, 64), 1, 131072) == 131040
+    assert lcs.attn_index_nnz(lcs.attnsink_pattern(1, 64), 32, 131072) == 32 * 131040
+    assert lcs.attn_index_nnz(lcs.blocksparse_pattern(1, 16, 8), 32, 32768) == 765216
+    assert lcs.attn_index_nnz(lcs.full_pattern(), 1, 131072) == 2048 * 2049 // 2
+
+
+def test_index_rejects_bad_arguments():
+    with pytest.raises(lcs.AttnError):
+        lcs.attn_index_nnz(lcs.attnsink_pattern(1, 4), 1, 1000)          # L % 64
+    with pytest.raises(lcs.AttnError):
+        lcs.attn_index_nnz(lcs.attnsink_pattern(1, 0), 1, 1024)          # local < 1
+    with pytest.raises(lcs.AttnError):
+        lcs.attn_index_nnz(lcs.blocksparse_pattern(1, 4, 0), 1, 1024)    # stride < 1
+    with pytest.raises(lcs.AttnError):
+        lcs.attn_index_nnz(lcs.Pattern(7), 1, 1024)                      # unknown kind
+    with pytest.raises(lcs.AttnError):
+        lcs.attn_index_nnz(lcs.attnsink_pattern(1, 4), 0, 1024)          # heads < 1
+
+
+def _corrupt(ix, field, fn):
+    import copy
+    bad = copy.deepcopy(ix)
+    arr = getattr(bad, field).copy()
+    fn(arr)
+    setattr(bad, field, arr)
+    return bad
+
+
+@pytest.mark.parametrize("field,fn", [
+    ("row_ptr", lambda a: a.__setitem__(3, a[4] + 1)),          # non-monotone
+    ("row_ptr", lambda a: a.__setitem__(-1, 10 ** 6)),          # beyond nnz
+    ("col_idx", lambda a: a.__setitem__(5, 999)),               # block id out of range
+    ("col_idx", lambda a: a.__setitem__(slice(1, 3), a[2:0:-1])),  # unsorted row
+    ("row_idx", lambda a: a.__setitem__(7, (a[7] + 1) % 16)),   # CSC not the transpose
+    ("col_ptr", lambda a: a.__setitem__(2, a[2] + 1)),          # CSC pointer shifted
+])
+def test_validate_rejects_malformed_index(field, fn):
+    ix = lcs.attn_index_build(lcs.attnsink_pattern(1, 4), 1, 1024)
+    lcs.attn_index_validate(ix)
+    bad = _corrupt(ix, field, fn)
+    with pytest.raises(lcs.AttnError) as e:
+        lcs.attn_index_validate(bad)
+    assert e.value.status == lcs.ATTN_ERR_BAD_INDEX
+
+
+def test_layer_map_middle_third():
+    m = lcs.attn_layer_map(32, 11, 21)
+    assert m.tolist() == [0] * 11 + [1] * 11 + [0] * 10
+    assert m.sum() == 11
+
+
+def test_workspace_sizes():
+    assert lcs.attn_workspace_bytes(lcs.ATTN_OP_FWD, lcs.ATTN_BF16, 1, 32, 8192, 128) == 0
+    assert lcs.attn_workspace_bytes(lcs.ATTN_OP_BWD, lcs.ATTN_BF16, 1, 32, 65536, 128) == 32 * 65536 * 4
+    ws = lcs.attn_workspace_bytes(lcs.ATTN_OP_FULL_DECODE, lcs.ATTN_BF16, 16, 32, 131073, 128)
+    assert ws > 0 and ws % (16 * 32 * 130 * 4) == 0
+    ws2 = lcs.attn_workspace_bytes(lcs.ATTN_OP_SPARSE_DECODE, lcs.ATTN_BF16, 16, 32, 4160, 128)
+    assert 0 < ws2 <= ws
+
+
+# --------------------------------------------- validation before any launch
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+def _fwd(dtype=lcs.ATTN_BF16, B=1, H=2, L=256, d=128, scale=0.1, pattern=None, ix=None,
+         q=FAKE, lse=FAKE):
+    p = pattern or lcs.attnsink_pattern(1, 2).c_struct()
+    if ix is None:
+        ix = lcs.attn_index_t(1, L // 64, L // 64, 10, FAKE, FAKE, None, None)
+    return lcs.lib().attn_sparse_fwd(dtype, B, H, L, d, scale, ctypes.byref(p), ctypes.byref(ix),
+                                     q, FAKE, FAKE, FAKE, lse, None, 0, None)
+
+
+def test_forward_validation_errors():
+    assert _fwd(L=1000) == lcs.ATTN_ERR_INVALID_ARG                   # L % 64
+    assert _fwd(B=0) == lcs.ATTN_ERR_INVALID_ARG
+    assert _fwd(scale=0.0) == lcs.ATTN_ERR_INVALID_ARG
+    assert _fwd(scale=float("nan")) == lcs.ATTN_ERR_INVALID_ARG
+    assert _fwd(q=None) == lcs.ATTN_ERR_INVALID_ARG
+    assert _fwd(d=96) == lcs.ATTN_ERR_UNSUPPORTED
+    assert _fwd(dtype=7) == lcs.ATTN_ERR_UNSUPPORTED
+    bad_blocks = lcs.attn_index_t(1, 3, 4, 10, FAKE, FAKE, None, None)
+    assert _fwd(ix=bad_blocks) == lcs.ATTN_ERR_INVALID_ARG           # index shape vs L
+    bad_heads = lcs.attn_index_t(3, 4, 4, 10, FAKE, FAKE, None, None)
+    assert _fwd(ix=bad_heads) == lcs.ATTN_ERR_INVALID_ARG            # n_heads not 1 or H
+    p = lcs.attn_pattern_t(1, 32, 1, 2, 0, 1)
+    assert _fwd(pattern=p) == lcs.ATTN_ERR_INVALID_ARG               # block != 64
+
+
+def test_backward_validation_errors():
+    L_ = lcs.lib()
+    p = lcs.attnsink_pattern(1, 2).c_struct()
+    no_csc = lcs.attn_index_t(1, 4, 4, 10, FAKE, FAKE, None, None)
+    csc = lcs.attn_index_t(1, 4, 4, 10, FAKE, FAKE, FAKE, FAKE)
+    args = lambda ix, dtype=lcs.ATTN_BF16, ws=FAKE, wsb=1 << 20: (
+        dtype, 1, 2, 256, 128, 0.1, ctypes.byref(p), ctypes.byref(ix), FAKE, FAKE, FAKE, FAKE,
+        FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb, None)
+    assert L_.attn_sparse_bwd(*args(no_csc)) == lcs.ATTN_ERR_INVALID_ARG
+    assert L_.attn_sparse_bwd(*args(csc, dtype=lcs.ATTN_F32)) == lcs.ATTN_ERR_UNSUPPORTED
+    assert L_.attn_sparse_bwd(*args(csc, ws=None)) == lcs.ATTN_ERR_WORKSPACE
+    assert L_.attn_sparse_bwd(*args(csc, wsb=100)) == lcs.ATTN_ERR_WORKSPACE
+
+
+def test_decode_validation_errors():
+    L_ = lcs.lib()
+    base = lambda **kw: dict(dtype=lcs.ATTN_BF16, B=2, H=4, d=128, scale=0.1, sink=64, window=4096,
+                             pos=FAKE, ws=FAKE, wsb=1 << 30) | kw
+    def sp(**kw):
+        a = base(**kw)
+        return L_.attn_sparse_decode(a["dtype"], a["B"], a["H"], a["d"], a["scale"], a["sink"],
+                                     a["window"], a["pos"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, a["ws"], a["wsb"], None)
+    assert sp(window=0) == lcs.ATTN_ERR_INVALID_ARG
+    assert sp(sink=-1) == lcs.ATTN_ERR_INVALID_ARG
+    assert sp(pos=None) == lcs.ATTN_ERR_INVALID_ARG
+    assert sp(d=80) == lcs.ATTN_ERR_UNSUPPORTED
+    assert sp(dtype=lcs.ATTN_F32) == lcs.ATTN_ERR_UNSUPPORTED
+    assert sp(ws=None) == lcs.ATTN_ERR_WORKSPACE
+    assert sp(wsb=16) == lcs.ATTN_ERR_WORKSPACE
+
+    def fd(cap=1000, max_pos=999, wsb=1 << 30):
+        return L_.attn_full_decode(lcs.ATTN_BF16, 2, 4, 128, 0.1, cap, max_pos, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wsb, None)
+    assert fd(max_pos=1000) == lcs.ATTN_ERR_INVALID_ARG       # max_pos >= capacity
+    assert fd(max_pos=-1) == lcs.ATTN_ERR_INVALID_ARG
+    assert fd(wsb=8) == lcs.ATTN_ERR_WORKSPACE
+
+    rf = L_.attn_ring_fill
+    assert rf(lcs.ATTN_BF16, 1, 1, 128, 64, 0, FAKE, FAKE, FAKE, 10, FAKE, FAKE, None) == lcs.ATTN_ERR_INVALID_ARG
+    assert rf(lcs.ATTN_BF16, 1, 1, 100, 64, 64, FAKE, FAKE, FAKE, 10, FAKE, FAKE, None) == lcs.ATTN_ERR_UNSUPPORTED

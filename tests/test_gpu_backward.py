@@ -1,0 +1,78 @@
+"""GPU parity of the training backward (attn_sparse_bwd) against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_static_amd as lcs
+from _parity import assert_bf16_close, need_gpu, oracle_pattern, sample_backward
+from oracle import sparse_backward
+from synth_inputs import as_f64, randn, seed_for
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(shape, workload, big=False):
+    dev = "cuda" if big else "cpu"
+    return [randn(shape, seed_for(workload, 0, t), torch.bfloat16, dev).cuda()
+            for t in ("q", "k", "v", "do")]
+
+
+def _fwd_bwd(q, k, v, do, pattern):
+    B, H, L, d = q.shape
+    ix = lcs.build_device_index(pattern, H, L, q.device, with_csc=True)
+    o, lse = lcs.attn_sparse_fwd(q, k, v, ix, pattern)
+    dq, dk, dv = lcs.attn_sparse_bwd(q, k, v, o, lse, do, ix, pattern)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+SMALL = [
+    (lcs.attnsink_pattern(1, 3), 128, 1, 2, 9),
+    (lcs.attnsink_pattern(1, 4), 64, 2, 2, 10),
+    (lcs.blocksparse_pattern(1, 3, 4), 128, 1, 8, 19),
+    (lcs.full_pattern(), 128, 1, 2, 7),
+    (lcs.attnsink_pattern(2, 2), 128, 1, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_bf16_backward_small_full_oracle(case):
+    need_gpu()
+    pat, d, B, H, nb = SMALL[case]
+    q, k, v, do = _inputs((B, H, 64 * nb, d), 400 + case)
+    dq, dk, dv = _fwd_bwd(q, k, v, do, pat)
+    wq, wk, wv, _, _ = sparse_backward(as_f64(q), as_f64(k), as_f64(v), as_f64(do), oracle_pattern(pat))
+    for name, g, w in (("dq", dq, wq), ("dk", dk, wk), ("dv", dv, wv)):
+        print(case, name, assert_bf16_close(as_f64(g), w, name))
+
+
+def test_backward_deterministic():
+    need_gpu()
+    pat = lcs.blocksparse_pattern(1, 4, 8)
+    q, k, v, do = _inputs((1, 4, 64 * 24, 128), 450)
+    a = _fwd_bwd(q, k, v, do, pat)
+    b = _fwd_bwd(q, k, v, do, pat)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_64k_sampled_blocks():
+    """The 64K-token AttnSink training workload (32 heads, d 128) in the launch
+    configuration the benchmark times; the oracle checks sampled query blocks
+    (dQ) and key blocks (dK, dV) of sampled heads on their exact
+    sub-problems -- including the sink block, read by every query block."""
+    need_gpu()
+    pat = lcs.attnsink_pattern(1, 64)
+    L = 65536
+    q, k, v, do = _inputs((1, 32, L, 128), 4, big=True)
+    dq, dk, dv = _fwd_bwd(q, k, v, do, pat)
+    nb = L // 64
+    for h in (0, 21):
+        qblocks = [0, 1, 63, 64, 500, nb - 1]
+        kblocks = ([0] if h == 0 else []) + [1, 37, 700, nb - 2, nb - 1]
+        want = sample_backward(q, k, v, do, pat, h, 0, qblocks, kblocks)
+        for (name, blk), w in want.items():
+            g = {"dq": dq, "dk": dk, "dv": dv}[name][0, h, 64 * blk:64 * (blk + 1)]
+            mx, mean = assert_bf16_close(as_f64(g), w, f"{name} head {h} block {blk}")
+            print(name, h, blk, mx, mean)

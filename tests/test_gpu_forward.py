@@ -1,0 +1,182 @@
+"""GPU parity of the prefill forward (attn_sparse_fwd) against the oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_static_amd as lcs
+from _parity import (assert_bf16_close, assert_f32_close, errors, need_gpu, oracle_pattern,
+                     sample_rows_forward)
+from oracle import sparse_forward
+from synth_inputs import as_f64, randn, seed_for
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(shape, workload, dtype, device="cuda", big=False):
+    gen_dev = "cuda" if big else "cpu"
+    return [randn(shape, seed_for(workload, 0, t), dtype, gen_dev).to(device) for t in ("q", "k", "v")]
+
+
+def _run(q, k, v, pattern):
+    B, H, L, d = q.shape
+    ix = lcs.build_device_index(pattern, H, L, q.device, with_csc=False)
+    o, lse = lcs.attn_sparse_fwd(q, k, v, ix, pattern)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def test_fp32_attnsink_1k_exact_workload():
+    """1024 tokens, d 64, fp32, sink 1 block + 4 most recent blocks: full oracle."""
+    need_gpu()
+    pat = lcs.attnsink_pattern(1, 4)
+    q, k, v = _inputs((1, 1, 1024, 64), 1, torch.float32)
+    o, lse = _run(q, k, v, pat)
+    wo, wl = sparse_forward(as_f64(q), as_f64(k), as_f64(v), oracle_pattern(pat))
+    print("fp32 1k O", assert_f32_close(as_f64(o), wo, "O"))
+    print("fp32 1k LSE", assert_f32_close(as_f64(lse), wl, "LSE"))
+
+
+@pytest.mark.parametrize("pat,d,H,nb", [
+    (lcs.blocksparse_pattern(1, 3, 4), 128, 4, 13),
+    (lcs.full_pattern(), 64, 2, 9),
+])
+def test_fp32_other_patterns(pat, d, H, nb):
+    need_gpu()
+    q, k, v = _inputs((2, H, 64 * nb, d), 90, torch.float32)
+    o, lse = _run(q, k, v, pat)
+    wo, wl = sparse_forward(as_f64(q), as_f64(k), as_f64(v), oracle_pattern(pat))
+    assert_f32_close(as_f64(o), wo, "O")
+    assert_f32_close(as_f64(lse), wl, "LSE")
+
+
+SMALL_BF16 = [
+    # (pattern, d, B, H, n_blocks): odd block counts leave a half-filled last tile
+    (lcs.attnsink_pattern(1, 4), 128, 2, 3, 11),
+    (lcs.attnsink_pattern(1, 4), 64, 1, 2, 12),
+    (lcs.attnsink_pattern(2, 3), 128, 1, 2, 9),
+    (lcs.blocksparse_pattern(1, 5, 4), 128, 1, 8, 37),
+    (lcs.blocksparse_pattern(1, 3, 8), 64, 1, 9, 21),
+    (lcs.full_pattern(), 128, 1, 2, 13),
+    (lcs.attnsink_pattern(1, 1), 128, 1, 1, 1),          # a single block
+    (lcs.attnsink_pattern(1, 64), 128, 1, 2, 70),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL_BF16)))
+def test_bf16_small_full_oracle(case):
+    need_gpu()
+    pat, d, B, H, nb = SMALL_BF16[case]
+    q, k, v = _inputs((B, H, 64 * nb, d), 100 + case, torch.bfloat16)
+    o, lse = _run(q, k, v, pat)
+    wo, wl = sparse_forward(as_f64(q), as_f64(k), as_f64(v), oracle_pattern(pat))
+    print(case, "O", assert_bf16_close(as_f64(o), wo, "O"))
+    print(case, "LSE", assert_bf16_close(as_f64(lse), wl, "LSE"))
+
+
+@pytest.mark.parametrize("pat,d", [(lcs.attnsink_pattern(1, 4), 128), (lcs.blocksparse_pattern(1, 2, 3), 128),
+                                   (lcs.full_pattern(), 64), (lcs.attnsink_pattern(1, 4), 64)])
+def test_zero_query_lse_counts(pat, d):
+    """Q = 0: every allowed score is 0, so LSE = ln(#allowed keys) exactly and O
+    is the mean of the allowed V rows -- pins the mask on the GPU."""
+    need_gpu()
+    B, H, nb = 1, 8, 10
+    L = 64 * nb
+    q = torch.zeros((B, H, L, d), dtype=torch.bfloat16, device="cuda")
+    _, k, v = _inputs((B, H, L, d), 7, torch.bfloat16)
+    o, lse = _run(q, k, v, pat)
+    ix = lcs.attn_index_build(pat, H if pat.head_dependent else 1, L, with_csc=False)
+    lse_h = lse.cpu().numpy()
+    for h in range(H):
+        hh = h if pat.head_dependent else 0
+        for i in range(nb):
+            n_blocks = len(ix.row(hh, i))
+            counts = 64 * (n_blocks - 1) + np.arange(1, 65)
+            np.testing.assert_allclose(lse_h[0, h, 64 * i:64 * (i + 1)], np.log(counts), rtol=0, atol=2e-6)
+    wo, _ = sparse_forward(np.zeros((B, H, L, d)), as_f64(k), as_f64(v), oracle_pattern(pat))
+    assert_bf16_close(as_f64(o), wo, "O")
+
+
+def test_empty_rows_give_zero_and_minus_inf():
+    need_gpu()
+    L, d = 256, 128
+    q, k, v = _inputs((1, 2, L, d), 8, torch.bfloat16)
+    # query block 1 lists nothing; block 3 lists only block 0
+    row_ptr = np.array([0, 1, 1, 3, 4], dtype=np.int32)
+    col_idx = np.array([0, 0, 2, 0], dtype=np.int32)
+    host = lcs.HostIndex(1, 4, 4, row_ptr, col_idx, None, None)
+    lcs.attn_index_validate(host)
+    ix = lcs.DeviceIndex(host, q.device)
+    o, lse = lcs.attn_sparse_fwd(q, k, v, ix, lcs.attnsink_pattern(1, 1))
+    torch.cuda.synchronize()
+    assert torch.all(o[:, :, 64:128] == 0)
+    assert torch.all(torch.isneginf(lse[:, :, 64:128]))
+    assert torch.all(torch.isfinite(lse[:, :, :64])) and torch.all(torch.isfinite(lse[:, :, 128:]))
+
+
+def test_out_of_range_index_entries_are_skipped():
+    """A malformed device index must not cause out-of-bounds reads: bad ids are
+    skipped and row pointers clamped."""
+    need_gpu()
+    L, d = 256, 128
+    q, k, v = _inputs((1, 1, L, d), 9, torch.bfloat16)
+    good = lcs.attn_index_build(lcs.attnsink_pattern(1, 1), 1, L, with_csc=False)
+    o_ref, l_ref = lcs.attn_sparse_fwd(q, k, v, lcs.DeviceIndex(good, q.device), lcs.attnsink_pattern(1, 1))
+    # same lists with junk ids (-5, 4, 1000) interleaved, and a final pointer past nnz
+    rows = [good.row(0, i) for i in range(4)]
+    junk = [[-5] + r + [1000] for r in rows]
+    row_ptr = np.cumsum([0] + [len(r) for r in junk]).astype(np.int32)
+    row_ptr[-1] += 50                                   # clamped to nnz by the kernel
+    col_idx = np.array([x for r in junk for x in r], dtype=np.int32)
+    ix = lcs.attn_index_t(1, 4, 4, len(col_idx), None, None, None, None)
+    rp = torch.from_numpy(row_ptr).cuda()
+    ci = torch.from_numpy(col_idx).cuda()
+    ix.row_ptr, ix.col_idx = rp.data_ptr(), ci.data_ptr()
+
+    class Raw:
+        def c_struct(self):
+            return ix
+    o, lse = lcs.attn_sparse_fwd(q, k, v, Raw(), lcs.attnsink_pattern(1, 1))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+
+
+def test_deterministic_repeat():
+    need_gpu()
+    pat = lcs.blocksparse_pattern(1, 4, 8)
+    q, k, v = _inputs((1, 4, 64 * 20, 128), 11, torch.bfloat16)
+    o1, l1 = _run(q, k, v, pat)
+    o2, l2 = _run(q, k, v, pat)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------
+# Full-size workloads, in the launch configuration the benchmark times; the
+# oracle checks sampled rows of sampled heads on their exact sub-problems.
+# ----------------------------------------------------------------------------
+FULL_SIZE = {
+    "attnsink_8k": (lcs.attnsink_pattern(1, 64), 8192, 2),
+    "blocksparse_32k": (lcs.blocksparse_pattern(1, 16, 8), 32768, 3),
+    "attnsink_128k": (lcs.attnsink_pattern(1, 64), 131072, 5),
+    "full_128k": (lcs.full_pattern(), 131072, 5),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_SIZE))
+def test_bf16_full_size_sampled(name):
+    need_gpu()
+    pat, L, wl = FULL_SIZE[name]
+    H, d = 32, 128
+    q, k, v = _inputs((1, H, L, d), wl, torch.bfloat16, big=True)
+    o, lse = _run(q, k, v, pat)
+    rng = np.random.default_rng(L)
+    heads = [0, 7, 31] if name != "blocksparse_32k" else [0, 3, 12, 29]
+    for h in heads:
+        rows = np.unique(np.concatenate([[0, 63, 64, L - 1, L - 64], rng.integers(0, L, 40)]))
+        wo, wlse = sample_rows_forward(q, k, v, pat, h, 0, rows)
+        idx = torch.as_tensor(rows, device=q.device)
+        mx, mean = assert_bf16_close(as_f64(o[0, h, idx]), wo, f"{name} O head {h}")
+        assert_bf16_close(as_f64(lse[0, h, idx]), wlse, f"{name} LSE head {h}")
+        print(name, h, mx, mean)
