@@ -1,0 +1,372 @@
+"""Benchmark of the static block-sparse attention hot path on one MI355X.
+
+Default workload ("hybrid128k"): Llama-2-7B-shaped attention (32 layers,
+32 heads, d 128, bf16) at 131072 tokens, LongGen's hybrid layer map -- layers
+11..21 full causal attention, the other 21 layers AttnSink (sink 64 tokens,
+window 4096 tokens = 64 blocks).  One step =
+  prefill forward of all 32 layers (batch 1),
+  ring fill of every sparse layer's sink+window cache from its prefill K/V,
+  decode of 16 sequences (one new token each at position 131072) through all
+  32 layers: sparse layers read their 64+4096-slot ring caches, full layers
+  their 131073-slot caches.
+Inputs are synthetic (seeded N(0,1), bf16) and resident in HBM before timing.
+
+Printed: one JSON line.  ``value`` is the effective TFLOP/s of the sparse
+(AttnSink) prefill layers -- algorithmic FLOPs of the computed 64x64 blocks
+(4*64*64*d per block pair) divided by their kernel time.  Decode tokens/s,
+the full-layer and whole-hybrid prefill rates, the roofline of the dominant
+kernel and the CPU oracle baseline are reported alongside.
+
+Other workloads (--workload): attnsink8k, blocksparse32k, blocksparse128k,
+train64k (forward + backward), decode128k.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import long_context_sparse_static_amd as lcs  # noqa: E402
+from synth_inputs import randn, seed_for  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+H, D, BLK = 32, 128, 64
+SINK_BLOCKS, WINDOW_BLOCKS = 1, 64
+SINK_TOK, WINDOW_TOK = 64, 4096
+N_LAYERS, FULL_FIRST, FULL_LAST = 32, 11, 21
+DEC_BATCH = 16
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def pair_flops(d=D):
+    return 4.0 * BLK * BLK * d
+
+
+class Timer:
+    """hipEvent pairs on the current stream, summed per label."""
+
+    def __init__(self):
+        self.pending = []
+
+    def span(self, label):
+        t = self
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+
+        class _Ctx:
+            def __enter__(self_):
+                s.record()
+
+            def __exit__(self_, *a):
+                e.record()
+                t.pending.append((label, s, e))
+        return _Ctx()
+
+    def collect(self):
+        torch.cuda.synchronize()
+        out = {}
+        for label, s, e in self.pending:
+            out.setdefault(label, []).append(s.elapsed_time(e))
+        self.pending = []
+        return out
+
+
+def fill_randn(shape, seed):
+    """Large bf16 tensor of seeded N(0,1) values, generated on the device."""
+    return randn(shape, seed, torch.bfloat16, "cuda")
+
+
+# ----------------------------------------------------------------------------
+# hybrid 128K workload
+# ----------------------------------------------------------------------------
+class Hybrid128k:
+    name = "hybrid128k"
+    L = 131072
+
+    def __init__(self, n_sets=4, n_full_caches=2):
+        dev = torch.device("cuda")
+        L = self.L
+        self.layer_full = lcs.attn_layer_map(N_LAYERS, FULL_FIRST, FULL_LAST)
+        self.sparse_pat = lcs.attnsink_pattern(SINK_BLOCKS, WINDOW_BLOCKS)
+        self.full_pat = lcs.full_pattern()
+        t0 = time.time()
+        self.ix_sparse = lcs.build_device_index(self.sparse_pat, H, L, dev, with_csc=False)
+        self.ix_full = lcs.build_device_index(self.full_pat, H, L, dev, with_csc=False)
+        self.index_build_s = time.time() - t0
+        # distinct input sets, cycled over layers (each set 3.2 GB >> 256 MB MALL)
+        self.sets = []
+        for s in range(n_sets):
+            self.sets.append([fill_randn((1, H, L, D), seed_for(5, s, t)) for t in ("q", "k", "v")])
+        self.outs = [(torch.empty((1, H, L, D), dtype=torch.bfloat16, device=dev),
+                      torch.empty((1, H, L), dtype=torch.float32, device=dev)) for _ in range(2)]
+        # decode state
+        B = DEC_BATCH
+        self.t = L
+        self.pos = torch.full((B,), self.t, dtype=torch.int64, device=dev)
+        self.len0 = torch.full((1,), L, dtype=torch.int64, device=dev)
+        self.q_dec = fill_randn((B, H, 1, D), seed_for(5, 0, "q_dec"))
+        self.k_new = fill_randn((B, H, 1, D), seed_for(5, 0, "k_new"))
+        self.v_new = fill_randn((B, H, 1, D), seed_for(5, 0, "v_new"))
+        S = SINK_TOK + WINDOW_TOK
+        self.rings = {}
+        for layer in range(N_LAYERS):
+            if not self.layer_full[layer]:
+                self.rings[layer] = (fill_randn((B, H, S, D), seed_for(5, layer, "cache")),
+                                     fill_randn((B, H, S, D), seed_for(5, layer, "cache_v")))
+        self.cap = self.t + 1
+        self.full_caches = [(fill_randn((B, H, self.cap, D), seed_for(5, 40 + c, "cache")),
+                             fill_randn((B, H, self.cap, D), seed_for(5, 40 + c, "cache_v")))
+                            for c in range(n_full_caches)]
+        self.dec_o = torch.empty((B, H, 1, D), dtype=torch.bfloat16, device=dev)
+        self.dec_lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        self.ws_sparse = torch.empty(lcs.attn_workspace_bytes(lcs.ATTN_OP_SPARSE_DECODE, lcs.ATTN_BF16,
+                                                              B, H, S, D), dtype=torch.uint8, device=dev)
+        self.ws_full = torch.empty(lcs.attn_workspace_bytes(lcs.ATTN_OP_FULL_DECODE, lcs.ATTN_BF16,
+                                                            B, H, self.cap, D), dtype=torch.uint8,
+                                   device=dev)
+        torch.cuda.synchronize()
+        self.nnz_sparse = self.ix_sparse.host.nnz * H      # block pairs per layer
+        self.nnz_full = self.ix_full.host.nnz * H
+
+    def step(self, timer: Timer):
+        L = self.L
+        B = DEC_BATCH
+        for layer in range(N_LAYERS):
+            q, k, v = self.sets[layer % len(self.sets)]
+            o, lse = self.outs[layer % 2]
+            full = bool(self.layer_full[layer])
+            with timer.span("prefill_full" if full else "prefill_sparse"):
+                lcs.attn_sparse_fwd(q, k, v, self.ix_full if full else self.ix_sparse,
+                                    self.full_pat if full else self.sparse_pat, o=o, lse=lse)
+            if not full:
+                # sequence 0 of this layer's decode batch continues the prefill
+                rk, rv = self.rings[layer]
+                with timer.span("ring_fill"):
+                    lcs.attn_ring_fill(k, v, self.len0, rk[:1], rv[:1], SINK_TOK, WINDOW_TOK)
+        for layer in range(N_LAYERS):
+            if self.layer_full[layer]:
+                kc, vc = self.full_caches[layer % len(self.full_caches)]
+                with timer.span("decode_full"):
+                    lcs.attn_full_decode(self.q_dec, self.k_new, self.v_new, kc, vc, self.pos,
+                                         max_pos=self.t, o=self.dec_o, lse=self.dec_lse,
+                                         workspace=self.ws_full)
+            else:
+                rk, rv = self.rings[layer]
+                with timer.span("decode_sparse"):
+                    lcs.attn_sparse_decode(self.q_dec, self.k_new, self.v_new, rk, rv, self.pos,
+                                           SINK_TOK, WINDOW_TOK, o=self.dec_o, lse=self.dec_lse,
+                                           workspace=self.ws_sparse)
+
+    def report(self, times, steps):
+        n_sparse = int((self.layer_full == 0).sum())
+        n_full = int(self.layer_full.sum())
+        per = lambda k: sum(times.get(k, [])) / steps            # ms per step
+        fl_sparse = n_sparse * self.nnz_sparse * pair_flops()
+        fl_full = n_full * self.nnz_full * pair_flops()
+        t_sp, t_fu = per("prefill_sparse"), per("prefill_full")
+        t_ds, t_df = per("decode_sparse"), per("decode_full")
+        S = SINK_TOK + WINDOW_TOK
+        # algorithmic decode bytes: every attended K and V row read once, plus q, o
+        bytes_sparse = n_sparse * DEC_BATCH * H * (S * 2 * D * 2)
+        bytes_full = n_full * DEC_BATCH * H * ((self.t + 1) * 2 * D * 2)
+        dec_ms = t_ds + t_df
+        launches_fwd = len(times.get("prefill_sparse", [])) + len(times.get("prefill_full", []))
+        fwd_ms_total = sum(times.get("prefill_sparse", [])) + sum(times.get("prefill_full", []))
+        flops_per_launch = (fl_sparse + fl_full) * steps / launches_fwd
+        avg_ms = fwd_ms_total / launches_fwd
+        achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
+        return dict(
+            value=fl_sparse / (t_sp * 1e-3) / 1e12,
+            extra=dict(
+                sparse_prefill_tflops=fl_sparse / (t_sp * 1e-3) / 1e12,
+                full_prefill_tflops=fl_full / (t_fu * 1e-3) / 1e12,
+                hybrid_prefill_tflops=(fl_sparse + fl_full) / ((t_sp + t_fu) * 1e-3) / 1e12,
+                decode_tok_s=DEC_BATCH / (dec_ms * 1e-3),
+                decode_sparse_gbps=bytes_sparse / (t_ds * 1e-3) / 1e9,
+                decode_full_gbps=bytes_full / (t_df * 1e-3) / 1e9,
+                decode_hbm_frac=(bytes_sparse + bytes_full) / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                ms=dict(prefill_sparse=t_sp, prefill_full=t_fu, ring_fill=per("ring_fill"),
+                        decode_sparse=t_ds, decode_full=t_df),
+                sparse_prefill_frac_of_peak=fl_sparse / (t_sp * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                tflop_per_step=dict(sparse=fl_sparse / 1e12, full=fl_full / 1e12),
+                index_build_s=self.index_build_s,
+            ),
+            roofline=dict(bound="mfma", kernel="fwd_bf16_kernel<128>", achieved=achieved,
+                          peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=achieved / PEAK_BF16_TFLOPS,
+                          traffic=None, flop_per_launch=flops_per_launch, avg_launch_ms=avg_ms),
+            config=dict(workload="hybrid128k: 32 layers (11..21 full, 21 AttnSink sink 64 + window 4096), "
+                        "prefill B=1 L=131072 H=32 d=128 + decode 16 seqs at t=131072",
+                        global_batch=DEC_BATCH, seq_len=self.L, layers=N_LAYERS,
+                        full_layers=f"{FULL_FIRST}-{FULL_LAST}", heads=H, head_dim=D,
+                        block=BLK, parallelism="single GPU",
+                        input_sets=len(self.sets), full_decode_cache_buffers=len(self.full_caches)),
+        )
+
+
+# ----------------------------------------------------------------------------
+# single-kernel workloads
+# ----------------------------------------------------------------------------
+class Prefill:
+    def __init__(self, name, pattern, L, wl, backward=False):
+        self.name, self.pattern, self.L, self.backward = name, pattern, L, backward
+        dev = torch.device("cuda")
+        self.ix = lcs.build_device_index(pattern, H, L, dev, with_csc=backward)
+        self.q, self.k, self.v = (fill_randn((1, H, L, D), seed_for(wl, 0, t)) for t in ("q", "k", "v"))
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((1, H, L), dtype=torch.float32, device=dev)
+        if backward:
+            self.do = fill_randn((1, H, L, D), seed_for(wl, 0, "do"))
+            self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
+            self.ws = torch.empty(lcs.attn_workspace_bytes(lcs.ATTN_OP_BWD, lcs.ATTN_BF16, 1, H, L, D),
+                                  dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        self.pairs = self.ix.host.nnz * (H if not pattern.head_dependent else 1)
+
+    def step(self, timer):
+        with timer.span("fwd"):
+            lcs.attn_sparse_fwd(self.q, self.k, self.v, self.ix, self.pattern, o=self.o, lse=self.lse)
+        if self.backward:
+            with timer.span("bwd"):
+                lcs.attn_sparse_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, self.ix,
+                                    self.pattern, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
+
+    def report(self, times, steps):
+        fl = self.pairs * pair_flops()
+        t_f = sum(times["fwd"]) / steps
+        extra = dict(fwd_tflops=fl / (t_f * 1e-3) / 1e12, fwd_ms=t_f, block_pairs=self.pairs)
+        value = extra["fwd_tflops"]
+        kernel, per_launch, avg = "fwd_bf16_kernel<128>", fl, t_f
+        if self.backward:
+            t_b = sum(times["bwd"]) / steps
+            extra.update(bwd_tflops=2.5 * fl / (t_b * 1e-3) / 1e12, bwd_ms=t_b)
+            value = 3.5 * fl / ((t_f + t_b) * 1e-3) / 1e12
+            kernel, per_launch, avg = "attn_sparse_bwd (delta + dkdv + dq)", 2.5 * fl, t_b
+        ach = per_launch / (avg * 1e-3) / 1e12
+        return dict(value=value, extra=extra,
+                    roofline=dict(bound="mfma", kernel=kernel, achieved=ach, peak=PEAK_BF16_TFLOPS,
+                                  unit="TFLOP/s", frac=ach / PEAK_BF16_TFLOPS, traffic=None),
+                    config=dict(workload=f"{self.name}: B=1 H=32 L={self.L} d=128 bf16",
+                                global_batch=1, seq_len=self.L, parallelism="single GPU"))
+
+
+def make_workload(name):
+    if name == "hybrid128k":
+        return Hybrid128k()
+    if name == "attnsink8k":
+        return Prefill(name, lcs.attnsink_pattern(1, 64), 8192, 2)
+    if name == "blocksparse32k":
+        return Prefill(name, lcs.blocksparse_pattern(1, 16, 8), 32768, 3)
+    if name == "blocksparse128k":
+        return Prefill(name, lcs.blocksparse_pattern(1, 16, 8), 131072, 3)
+    if name == "attnsink128k":
+        return Prefill(name, lcs.attnsink_pattern(1, 64), 131072, 5)
+    if name == "train64k":
+        return Prefill(name, lcs.attnsink_pattern(1, 64), 65536, 4, backward=True)
+    raise SystemExit(f"unknown workload {name}")
+
+
+# ----------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample of the same workload)
+# ----------------------------------------------------------------------------
+def cpu_baseline(budget_s=15.0):
+    """Times the oracle on sampled query rows of one 128K AttnSink layer and
+    scales to effective TFLOP/s over the computed blocks of those rows."""
+    from oracle import sparse_forward
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    L = 131072
+    g = torch.Generator().manual_seed(seed_for(5, 0, "q"))
+    # one head's Q/K/V, generated on the host (the sample needs the whole key range)
+    q = torch.randn((1, 1, L, D), generator=g).to(torch.bfloat16).double().numpy()
+    k = torch.randn((1, 1, L, D), generator=g).to(torch.bfloat16).double().numpy()
+    v = torch.randn((1, 1, L, D), generator=g).to(torch.bfloat16).double().numpy()
+    pat = dict(kind="attnsink", block=BLK, sink_blocks=SINK_BLOCKS, local_blocks=WINDOW_BLOCKS, causal=True)
+    rng = np.random.default_rng(0)
+    rows_done, pairs_done, t_used, batch = 0, 0.0, 0.0, 64
+    while t_used < budget_s and rows_done < 4096:
+        rows = np.sort(rng.choice(np.arange(WINDOW_BLOCKS * BLK, L), size=batch, replace=False))
+        t0 = time.perf_counter()
+        sparse_forward(q, k, v, pat, rows=rows)
+        t_used += time.perf_counter() - t0
+        rows_done += batch
+        pairs_done += batch * (SINK_BLOCKS + WINDOW_BLOCKS) / BLK   # block pairs per query row
+    flops = pairs_done * pair_flops()
+    return dict(value=flops / t_used / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"{rows_done} query rows (random, past the first window) of one head of one "
+                       f"128K AttnSink layer, float64 dense-masked NumPy; {t_used:.1f} s",
+                affinity_cpus=len(os.sched_getaffinity(0)))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="hybrid128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        raise SystemExit(2)
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    lcs.lib()
+    log(f"[bench] setting up {args.workload}")
+    wl = make_workload(args.workload)
+    timer = Timer()
+    for i in range(args.warmup):
+        wl.step(timer)
+        timer.collect()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        wl.step(timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times = timer.collect()
+    log(f"[bench] timed {args.steps} steps in {wall:.2f} s")
+    rep = wl.report(times, args.steps)
+    line = {
+        "metric": "effective TFLOP/s (computed blocks) sparse prefill @128K; decode tok/s",
+        "value": rep["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": rep["config"],
+        "roofline": rep["roofline"],
+        **rep["extra"],
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
