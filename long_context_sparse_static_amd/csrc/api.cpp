@@ -81,6 +81,8 @@ attn_status_t attn_sparse_fwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t 
   if (!index_shape_ok(dev_index, H, L, false)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_BF16 && attn::fwd_bf16_lds_bytes(d, dev_index->n_kblocks) > attn::kMaxLdsPerWorkgroup)
+    return ATTN_ERR_UNSUPPORTED;  // union bitmap of more than ~3.4M key blocks
   attn::FwdArgs a;
   a.q = q;
   a.k = k;
@@ -109,6 +111,8 @@ attn_status_t attn_sparse_bwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t 
   if (!index_shape_ok(dev_index, H, L, true)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (attn::bwd_bf16_lds_bytes(d, dev_index->n_qblocks) > attn::kMaxLdsPerWorkgroup)
+    return ATTN_ERR_UNSUPPORTED;
   const size_t need = attn_workspace_bytes(ATTN_OP_BWD, dtype, B, H, L, d);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   attn::BwdArgs a;

@@ -63,12 +63,18 @@ __device__ __forceinline__ void load_rows16(const float *lds, int tile, int hh, 
 //   S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - D), dQ^T += K^T dS^T
 // ----------------------------------------------------------------------------
 template <int D>
+struct DqBuf {
+  bf16 k[TileGeom<D>::ROW_ELEMS];
+  bf16 v[TileGeom<D>::ROW_ELEMS];
+  bf16 kt[TileGeom<D>::T_ELEMS];
+};
+
+template <int D>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   using G = TileGeom<D>;
   constexpr int KS = D / 16, MT = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 klds[G::ROW_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 vlds[G::ROW_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 ktlds[G::T_ELEMS];
+  __shared__ __attribute__((aligned(16))) DqBuf<D> lds[2];
+  extern __shared__ uint32_t dyn_lds[];
 
   const int nqb = a.ix.n_qblocks;
   const int n_tiles = (nqb + kBwdTB - 1) / kBwdTB;
@@ -80,18 +86,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const bf16 *kg = (const bf16 *)a.k + base;
   const bf16 *vg = (const bf16 *)a.v + base;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int n = lane & 31, hh = lane >> 5;
   const int my_r = wave >> 1;
   const int qb = tile * kBwdTB + my_r;
   const bool q_valid = qb < nqb;
   const int q_tok = qb * kBlock + (wave & 1) * 32 + n;
   const size_t qrow = base + (size_t)q_tok * D;
-
-  PairWalk walk;
-  walk.ids = a.ix.col_idx;
-  walk.n_ids = a.ix.n_kblocks;
-  walk.init(a.ix.row_ptr + (size_t)hidx * (nqb + 1), tile * kBwdTB, nqb, a.ix.nnz);
 
   bf16x8 bq[KS], bdo[KS];
 #pragma unroll
@@ -107,40 +109,51 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     dlt = a.delta[(size_t)bh * a.L + q_tok];
   }
 
+  PairBitmap pb;
+  pb.init(dyn_lds, a.ix.n_kblocks);
+  pb.build(a.ix.row_ptr + (size_t)hidx * (nqb + 1), tile * kBwdTB, nqb, a.ix.nnz, a.ix.col_idx,
+           a.ix.n_kblocks, kBwdThreads);
+  PairIter it;
+  it.start();
+
   f32x16 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
 
   RowStage<D, kBwdThreads> sk, sv;
   TStage<D, kBwdThreads> skt;
-  int j = walk.next();
-  if (j != INT32_MAX) {
-    sk.load(kg + (size_t)j * kBlock * D);
-    sv.load(vg + (size_t)j * kBlock * D);
-    skt.load(kg + (size_t)j * kBlock * D);
+  auto load = [&](int jj) {
+    const size_t off = (size_t)jj * kBlock * D;
+    sk.load(kg + off);
+    sv.load(vg + off);
+    skt.load(kg + off);
+  };
+  auto store = [&](DqBuf<D> &b) {
+    sk.store(b.k);
+    sv.store(b.v);
+    skt.store(b.kt);
+  };
+  bool have = it.next(pb);
+  int j = it.j;
+  bool act = q_valid && (my_r == 0 ? it.in0 : it.in1);
+  if (have) {
+    load(j);
+    store(lds[0]);
   }
-  while (j != INT32_MAX) {
+  bool have_next = have && it.next(pb);
+  if (have_next) load(it.j);
+  int buf = 0;
+  while (have) {
     __syncthreads();
-    sk.store(klds);
-    sv.store(vlds);
-    skt.store(ktlds);
-    __syncthreads();
-    const bool active = q_valid && walk.has(my_r, j);
-    walk.advance(j);
-    const int jn = walk.next();
-    if (jn != INT32_MAX) {
-      sk.load(kg + (size_t)jn * kBlock * D);
-      sv.load(vg + (size_t)jn * kBlock * D);
-      skt.load(kg + (size_t)jn * kBlock * D);
-    }
-    if (active) {
+    if (act) {
+      const DqBuf<D> &bb = lds[buf];
       f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const bf16x8 ak = *(const bf16x8 *)(klds + (32 * t + n) * G::ROW + ks * 16 + hh * 8);
-          const bf16x8 av = *(const bf16x8 *)(vlds + (32 * t + n) * G::ROW + ks * 16 + hh * 8);
+          const bf16x8 ak = *(const bf16x8 *)(bb.k + (32 * t + n) * G::ROW + ks * 16 + hh * 8);
+          const bf16x8 av = *(const bf16x8 *)(bb.v + (32 * t + n) * G::ROW + ks * 16 + hh * 8);
           s[t] = mfma_32x32x16(ak, bq[ks], s[t]);
           dp[t] = mfma_32x32x16(av, bdo[ks], dp[t]);
         }
@@ -161,12 +174,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
         const bf16x8 bds = pack_acc_operand(s[ks >> 1], ks & 1);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const bf16x8 akt = *(const bf16x8 *)(ktlds + (32 * mt + n) * G::TROW + ks * 16 + hh * 8);
+          const bf16x8 akt = *(const bf16x8 *)(bb.kt + t_off(32 * mt + n, 2 * ks + hh));
           acc[mt] = mfma_32x32x16(akt, bds, acc[mt]);
         }
       }
     }
-    j = jn;
+    if (have_next) store(lds[buf ^ 1]);
+    have = have_next;
+    j = it.j;
+    act = q_valid && (my_r == 0 ? it.in0 : it.in1);
+    have_next = have && it.next(pb);
+    if (have_next) load(it.j);
+    buf ^= 1;
   }
   if (!q_valid) return;
   bf16 *out = (bf16 *)a.dq + qrow;
@@ -189,15 +208,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 //   dV^T += dO^T P,  dK^T += Q^T dS
 // ----------------------------------------------------------------------------
 template <int D>
+struct DkvBuf {
+  bf16 q[TileGeom<D>::ROW_ELEMS];
+  bf16 dout[TileGeom<D>::ROW_ELEMS];
+  bf16 qt[TileGeom<D>::T_ELEMS];
+  bf16 dot[TileGeom<D>::T_ELEMS];
+  float lse2[kBlock];
+  float dlt[kBlock];
+};
+
+template <int D>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using G = TileGeom<D>;
   constexpr int KS = D / 16, MT = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 qlds[G::ROW_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 dolds[G::ROW_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 qtlds[G::T_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 dotlds[G::T_ELEMS];
-  __shared__ __attribute__((aligned(16))) float lse_lds[kBlock];
-  __shared__ __attribute__((aligned(16))) float dlt_lds[kBlock];
+  __shared__ __attribute__((aligned(16))) DkvBuf<D> lds[2];
+  extern __shared__ uint32_t dyn_lds[];
 
   const int nkb = a.ix.n_kblocks, nqb = a.ix.n_qblocks;
   const int n_tiles = (nkb + kBwdTB - 1) / kBwdTB;
@@ -229,18 +254,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const float *lseg = a.lse + (size_t)bh * a.L;
   const float *dltg = a.delta + (size_t)bh * a.L;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int n = lane & 31, hh = lane >> 5;
   const int my_r = wave >> 1;
   const int kb = tile * kBwdTB + my_r;
   const bool k_valid = kb < nkb;
   const int k_tok = kb * kBlock + (wave & 1) * 32 + n;
   const size_t krow = base + (size_t)k_tok * D;
-
-  PairWalk walk;
-  walk.ids = a.ix.row_idx;
-  walk.n_ids = nqb;
-  walk.init(a.ix.col_ptr + (size_t)hidx * (nkb + 1), tile * kBwdTB, nkb, a.ix.nnz);
 
   bf16x8 bk[KS], bv[KS];
 #pragma unroll
@@ -253,52 +274,65 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) dk[mt] = dv[mt] = f32x16{};
 
+  PairBitmap pb;
+  pb.init(dyn_lds, nqb);
+  pb.build(a.ix.col_ptr + (size_t)hidx * (nkb + 1), tile * kBwdTB, nkb, a.ix.nnz, a.ix.row_idx, nqb,
+           kBwdThreads);
+  PairIter it;
+  it.start();
+
   RowStage<D, kBwdThreads> sq, sdo;
   TStage<D, kBwdThreads> sqt, sdot;
   float lse_st = 0.f, dlt_st = 0.f;
-  auto load_block = [&](int i) {
-    const size_t off = (size_t)i * kBlock * D;
+  auto load = [&](int ii) {
+    const size_t off = (size_t)ii * kBlock * D;
     sq.load(qg + off);
     sdo.load(dog + off);
     sqt.load(qg + off);
     sdot.load(dog + off);
     if (threadIdx.x < kBlock) {
-      lse_st = lseg[(size_t)i * kBlock + threadIdx.x];
-      dlt_st = dltg[(size_t)i * kBlock + threadIdx.x];
+      lse_st = lseg[(size_t)ii * kBlock + threadIdx.x];
+      dlt_st = dltg[(size_t)ii * kBlock + threadIdx.x];
     }
   };
-  int i = walk.next();
-  if (i != INT32_MAX) load_block(i);
-  while (i != INT32_MAX) {
-    __syncthreads();
-    sq.store(qlds);
-    sdo.store(dolds);
-    sqt.store(qtlds);
-    sdot.store(dotlds);
+  auto store = [&](DkvBuf<D> &b) {
+    sq.store(b.q);
+    sdo.store(b.dout);
+    sqt.store(b.qt);
+    sdot.store(b.dot);
     if (threadIdx.x < kBlock) {
-      lse_lds[threadIdx.x] = lse_st == -INFINITY ? INFINITY : lse_st * kLog2e;
-      dlt_lds[threadIdx.x] = dlt_st;
+      b.lse2[threadIdx.x] = lse_st == -INFINITY ? INFINITY : lse_st * kLog2e;
+      b.dlt[threadIdx.x] = dlt_st;
     }
+  };
+  bool have = it.next(pb);
+  int i = it.j;
+  bool act = k_valid && (my_r == 0 ? it.in0 : it.in1);
+  if (have) {
+    load(i);
+    store(lds[0]);
+  }
+  bool have_next = have && it.next(pb);
+  if (have_next) load(it.j);
+  int buf = 0;
+  while (have) {
     __syncthreads();
-    const bool active = k_valid && walk.has(my_r, i);
-    walk.advance(i);
-    const int in = walk.next();
-    if (in != INT32_MAX) load_block(in);
-    if (active) {
+    if (act) {
+      const DkvBuf<D> &bb = lds[buf];
       const bool diag = a.causal && kb >= i;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 aq = *(const bf16x8 *)(qlds + (32 * m + n) * G::ROW + ks * 16 + hh * 8);
-          const bf16x8 ado = *(const bf16x8 *)(dolds + (32 * m + n) * G::ROW + ks * 16 + hh * 8);
+          const bf16x8 aq = *(const bf16x8 *)(bb.q + (32 * m + n) * G::ROW + ks * 16 + hh * 8);
+          const bf16x8 ado = *(const bf16x8 *)(bb.dout + (32 * m + n) * G::ROW + ks * 16 + hh * 8);
           s = mfma_32x32x16(aq, bk[ks], s);
           dp = mfma_32x32x16(ado, bv[ks], dp);
         }
         float l2[16], dl[16];
-        load_rows16(lse_lds, m, hh, l2);
-        load_rows16(dlt_lds, m, hh, dl);
+        load_rows16(bb.lse2, m, hh, l2);
+        load_rows16(bb.dlt, m, hh, dl);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = fast_exp2(__builtin_fmaf(s[r], c, -l2[r]));
@@ -316,15 +350,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
           const bf16x8 bds = pack_acc_operand(dp, half);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            const bf16x8 adot = *(const bf16x8 *)(dotlds + (32 * mt + n) * G::TROW + ks * 16 + hh * 8);
-            const bf16x8 aqt = *(const bf16x8 *)(qtlds + (32 * mt + n) * G::TROW + ks * 16 + hh * 8);
+            const bf16x8 adot = *(const bf16x8 *)(bb.dot + t_off(32 * mt + n, 2 * ks + hh));
+            const bf16x8 aqt = *(const bf16x8 *)(bb.qt + t_off(32 * mt + n, 2 * ks + hh));
             dv[mt] = mfma_32x32x16(adot, bp, dv[mt]);
             dk[mt] = mfma_32x32x16(aqt, bds, dk[mt]);
           }
         }
       }
     }
-    i = in;
+    if (have_next) store(lds[buf ^ 1]);
+    have = have_next;
+    i = it.j;
+    act = k_valid && (my_r == 0 ? it.in0 : it.in1);
+    have_next = have && it.next(pb);
+    if (have_next) load(it.j);
+    buf ^= 1;
   }
   if (!k_valid) return;
   bf16 *dko = (bf16 *)a.dk + krow;
@@ -343,25 +383,37 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 
-}  // namespace
-
-hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s) {
+template <int D>
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const size_t rows = (size_t)a.B * a.H * a.L;
-  const int rpb = 256 / (a.d / 8);
+  const int rpb = 256 / (D / 8);
   const int grid_delta = (int)((rows + rpb - 1) / rpb);
   const int q_tiles = (a.ix.n_qblocks + kBwdTB - 1) / kBwdTB;
   const int k_tiles = (a.ix.n_kblocks + kBwdTB - 1) / kBwdTB;
   const int BH = a.B * a.H;
-  if (a.d == 128) {
-    hipLaunchKernelGGL(bwd_delta_kernel<128>, dim3(grid_delta), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(BH * k_tiles), dim3(kBwdThreads), 0, s, a);
-    hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(BH * q_tiles), dim3(kBwdThreads), 0, s, a);
-  } else {
-    hipLaunchKernelGGL(bwd_delta_kernel<64>, dim3(grid_delta), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(BH * k_tiles), dim3(kBwdThreads), 0, s, a);
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(BH * q_tiles), dim3(kBwdThreads), 0, s, a);
-  }
+  const size_t dyn_k = PairBitmap::lds_bytes(a.ix.n_qblocks);
+  const size_t dyn_q = PairBitmap::lds_bytes(a.ix.n_kblocks);
+  hipError_t e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel<D>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_k);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute((const void *)bwd_dq_kernel<D>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_q);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3(grid_delta), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(BH * k_tiles), dim3(kBwdThreads), dyn_k, s, a);
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(BH * q_tiles), dim3(kBwdThreads), dyn_q, s, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_bf16_lds_bytes(int d, int n_blocks) {
+  const size_t buf = d == 128 ? sizeof(DkvBuf<128>) : sizeof(DkvBuf<64>);
+  return 2 * buf + PairBitmap::lds_bytes(n_blocks);
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s) {
+  return a.d == 128 ? launch_bwd<128>(a, s) : launch_bwd<64>(a, s);
 }
 
 }  // namespace attn

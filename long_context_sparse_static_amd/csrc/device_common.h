@@ -54,7 +54,20 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
-__device__ __forceinline__ int clamp_i(int x, int lo, int hi) {
+// max / sum of x over lane l and lane l ^ 32 (the two halves of a wave64).
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A wave-uniform copy of a value every lane holds (kept in an SGPR).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__host__ __device__ __forceinline__ int clamp_i(int x, int lo, int hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }
 

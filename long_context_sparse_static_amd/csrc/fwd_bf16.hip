@@ -11,12 +11,12 @@
 //
 // Work decomposition (one workgroup = 4 wave64s = 128 query tokens = two
 // adjacent 64-token query blocks of one (batch, head)):
-//   * the workgroup walks the ascending union of its query blocks' KV-block
-//     lists; each wave computes a KV block only if its own query block lists
-//     it (no wasted MFMA work on the other block's entries);
+//   * the workgroup first marks both query blocks' KV-block lists in an LDS
+//     bitmap and then walks their ascending union with scalar bit scans; a
+//     wave computes a KV block only if its own query block lists it;
 //   * per KV block, K (row-major) and V (transposed, [d][key]) are staged in
-//     LDS once and shared by the 4 waves; the next block's global loads are
-//     in flight while the current one is computed;
+//     LDS once for the 4 waves, double-buffered: one barrier per block, the
+//     next block's global loads in flight during the current block's math;
 //   * each wave owns 32 query rows and computes S^T = K Q^T (keys x queries)
 //     so that a lane owns one query: row max / row sum need no cross-lane
 //     traffic except one swap between the two lane halves;
@@ -34,18 +34,18 @@ namespace {
 
 constexpr int kFwdWaves = 4;                 // waves per workgroup
 constexpr int kFwdThreads = kFwdWaves * 64;
-constexpr int kFwdQB = kFwdWaves / 2;        // 64-token query blocks per tile
 
 template <int D>
 __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   using G = TileGeom<D>;
   constexpr int KS = D / 16;   // k-steps of S^T = K Q^T
   constexpr int MT = D / 32;   // 32-row tiles of O^T
-  __shared__ __attribute__((aligned(16))) bf16 klds[G::ROW_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 vlds[G::T_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 klds[2][G::ROW_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 vlds[2][G::T_ELEMS];
+  extern __shared__ uint32_t dyn_lds[];
 
   const int nqb = a.ix.n_qblocks;
-  const int n_tiles = (nqb + kFwdQB - 1) / kFwdQB;
+  const int n_tiles = (nqb + 1) / 2;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = lin / n_tiles;
   const int tile = n_tiles - 1 - lin % n_tiles;  // heaviest (latest) tiles first
@@ -59,23 +59,26 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   bf16 *og = (bf16 *)a.o + base;
   float *lg = a.lse + (size_t)bh * a.L;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int n = lane & 31, hh = lane >> 5;
   const int my_r = wave >> 1;
-  const int qb = tile * kFwdQB + my_r;
+  const int qb = tile * 2 + my_r;
   const bool q_valid = qb < nqb;
   const int q_tok = qb * kBlock + (wave & 1) * 32 + n;
-
-  PairWalk walk;
-  walk.ids = a.ix.col_idx;
-  walk.n_ids = a.ix.n_kblocks;
-  walk.init(a.ix.row_ptr + (size_t)hidx * (nqb + 1), tile * kFwdQB, nqb, a.ix.nnz);
 
   // Q^T operand of S^T = K Q^T: lane holds query n, d = 16 ks + 8 hh .. +7.
   bf16x8 bq[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     bq[ks] = q_valid ? *(const bf16x8 *)(qg + (size_t)q_tok * D + ks * 16 + hh * 8) : bf16x8{};
+
+  PairBitmap pb;
+  pb.init(dyn_lds, a.ix.n_kblocks);
+  pb.build(a.ix.row_ptr + (size_t)hidx * (nqb + 1), tile * 2, nqb, a.ix.nnz, a.ix.col_idx,
+           a.ix.n_kblocks, kFwdThreads);
+  PairIter it;
+  it.start();
 
   f32x16 oacc[MT];
 #pragma unroll
@@ -85,33 +88,35 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   RowStage<D, kFwdThreads> sk;
   TStage<D, kFwdThreads> sv;
-  int j = walk.next();
-  if (j != INT32_MAX) {
+  bool have = it.next(pb);
+  int j = it.j;
+  bool act = q_valid && (my_r == 0 ? it.in0 : it.in1);
+  if (have) {
     sk.load(kg + (size_t)j * kBlock * D);
     sv.load(vg + (size_t)j * kBlock * D);
+    sk.store(klds[0]);
+    sv.store(vlds[0]);
   }
+  bool have_next = have && it.next(pb);
+  if (have_next) {
+    sk.load(kg + (size_t)it.j * kBlock * D);
+    sv.load(vg + (size_t)it.j * kBlock * D);
+  }
+  int buf = 0;
 
-  while (j != INT32_MAX) {
+  while (have) {
+    // Block j is in buffer `buf`; every wave is done with the other buffer.
     __syncthreads();
-    sk.store(klds);
-    sv.store(vlds);
-    __syncthreads();
-    const bool active = q_valid && walk.has(my_r, j);
-    walk.advance(j);
-    const int jn = walk.next();
-    if (jn != INT32_MAX) {
-      sk.load(kg + (size_t)jn * kBlock * D);
-      sv.load(vg + (size_t)jn * kBlock * D);
-    }
-
-    if (active) {
+    if (act) {
+      const bf16 *kl = klds[buf];
+      const bf16 *vl = vlds[buf];
       // S^T (64 keys x 32 queries) as two 32x32 tiles.
       f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const bf16x8 ak = *(const bf16x8 *)(klds + (32 * t + n) * G::ROW + ks * 16 + hh * 8);
+          const bf16x8 ak = *(const bf16x8 *)(kl + (32 * t + n) * G::ROW + ks * 16 + hh * 8);
           s[t] = mfma_32x32x16(ak, bq[ks], s[t]);
         }
       }
@@ -129,7 +134,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = xor32_max(mx);
       const float mc = mx * c;
       const bool need = mc > m_run + 8.0f;
       if (__any(need)) {
@@ -152,18 +157,30 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
       // O^T (D x 32 queries) += V^T (D x 64 keys) P^T (64 keys x 32 queries).
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 pb = pack_acc_operand(s[ks >> 1], ks & 1);
+        const bf16x8 pbk = pack_acc_operand(s[ks >> 1], ks & 1);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const bf16x8 av = *(const bf16x8 *)(vlds + (32 * mt + n) * G::TROW + ks * 16 + hh * 8);
-          oacc[mt] = mfma_32x32x16(av, pb, oacc[mt]);
+          const bf16x8 av = *(const bf16x8 *)(vl + t_off(32 * mt + n, 2 * ks + hh));
+          oacc[mt] = mfma_32x32x16(av, pbk, oacc[mt]);
         }
       }
     }
-    j = jn;
+    if (have_next) {
+      sk.store(klds[buf ^ 1]);
+      sv.store(vlds[buf ^ 1]);
+    }
+    have = have_next;
+    j = it.j;
+    act = q_valid && (my_r == 0 ? it.in0 : it.in1);
+    have_next = have && it.next(pb);
+    if (have_next) {
+      sk.load(kg + (size_t)it.j * kBlock * D);
+      sv.load(vg + (size_t)it.j * kBlock * D);
+    }
+    buf ^= 1;
   }
 
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float l_tot = xor32_sum(l_part);
   if (!q_valid) return;
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   bf16 *orow = og + (size_t)q_tok * D;
@@ -179,16 +196,27 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   if (hh == 0) lg[q_tok] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
 }
 
+template <int D>
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
+  const int n_tiles = (a.ix.n_qblocks + 1) / 2;
+  const int grid = a.B * a.H * n_tiles;
+  const size_t dyn = PairBitmap::lds_bytes(a.ix.n_kblocks);
+  hipError_t e = hipFuncSetAttribute((const void *)fwd_bf16_kernel<D>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(grid), dim3(kFwdThreads), dyn, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+size_t fwd_bf16_lds_bytes(int d, int n_kblocks) {
+  const size_t stat = 2 * (kBlock * (d + 8) + d * kBlock) * sizeof(uint16_t);
+  return stat + PairBitmap::lds_bytes(n_kblocks);
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s) {
-  const int n_tiles = (a.ix.n_qblocks + kFwdQB - 1) / kFwdQB;
-  const int grid = a.B * a.H * n_tiles;
-  if (a.d == 128)
-    hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(grid), dim3(kFwdThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3(grid), dim3(kFwdThreads), 0, s, a);
-  return hipGetLastError();
+  return a.d == 128 ? launch_fwd<128>(a, s) : launch_fwd<64>(a, s);
 }
 
 }  // namespace attn

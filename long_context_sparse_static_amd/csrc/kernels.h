@@ -72,6 +72,11 @@ hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_ring_fill_bf16(const RingFillArgs &a, hipStream_t s);
 
+// LDS bytes one forward workgroup needs (static tiles + union bitmap).
+size_t fwd_bf16_lds_bytes(int d, int n_kblocks);
+size_t bwd_bf16_lds_bytes(int d, int n_blocks);  // the larger (dK/dV) backward kernel
+constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024;
+
 // Split-KV sizing shared by the workspace query and the decode launcher.
 void decode_split_plan(int32_t B, int32_t H, int64_t n_keys, int32_t *n_split,
                        int32_t *split_len);

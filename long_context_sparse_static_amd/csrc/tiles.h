@@ -4,14 +4,18 @@
 // Two LDS layouts of a 64 x D bf16 tile (64 tokens, D head dims):
 //   row-major   [token][d], rows padded to D + 8 elements, read as the
 //               row-operand of a 32x32x16 MFMA (16 contiguous bytes per lane);
-//   transposed  [d][pos(token)], rows padded to 64 + 8 elements, read as the
-//               operand whose k index runs over tokens.  pos() swaps bits 2
-//               and 3 of the token index so that the 8 tokens one lane feeds
-//               into a k-step sit in 16 contiguous bytes (they match the
-//               register order of a 32x32 accumulator reused as an operand,
-//               see pack_acc_operand()).
-// Both paddings make 16 consecutive lanes of a 16-byte read hit distinct
-// banks.
+//               the padding puts 16 consecutive lanes on distinct banks.
+//   transposed  [d][token], 128-byte rows (64 tokens) without padding, read
+//               as the operand whose k index runs over tokens.  Within a row
+//               the tokens are permuted by tpos() (bits 2 and 3 swapped) so
+//               that the 8 tokens one lane feeds into a k-step are 16
+//               contiguous bytes, matching the register order of a 32x32
+//               accumulator reused as an operand (pack_acc_operand()); and
+//               the eight 16-byte chunks of row d are XOR-swizzled by
+//               tswz(d) so that both the 16-lane operand reads and the
+//               transposing 8-byte writes spread over all 64 banks.  (With
+//               plain padding the transposing writes ran ~25x slower than the
+//               reads on gfx950 and stalled the whole CU's LDS.)
 #pragma once
 
 #include "device_common.h"
@@ -19,17 +23,22 @@
 
 namespace attn {
 
-__device__ __forceinline__ int tpos(int u) {
+__host__ __device__ __forceinline__ int tpos(int u) {
   return (u & ~0xC) | ((u & 4) << 1) | ((u & 8) >> 1);
 }
+
+// XOR key of the 16-byte chunks of transposed row d (0..7).
+__host__ __device__ __forceinline__ int tswz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
+
+// Element offset of logical 16-byte chunk q (0..7) of transposed row d.
+__host__ __device__ __forceinline__ int t_off(int d, int q) { return d * kBlock + ((q ^ tswz(d)) << 3); }
 
 template <int D>
 struct TileGeom {
   static constexpr int ROW = D + 8;        // row-major LDS row (elements)
-  static constexpr int TROW = kBlock + 8;  // transposed LDS row (elements)
   static constexpr int CPR = D / 8;        // 16-byte chunks per token row
   static constexpr int ROW_ELEMS = kBlock * ROW;
-  static constexpr int T_ELEMS = D * TROW;
+  static constexpr int T_ELEMS = D * kBlock;
 };
 
 // Row-major staging of one 64 x D tile by NT threads.
@@ -57,8 +66,9 @@ struct RowStage {
 };
 
 // Transposed staging of one 64 x D tile by NT threads: each thread loads KPT
-// consecutive token rows of one 8-dim chunk and writes 8 transposed rows of
-// KPT tokens.
+// consecutive token rows of one 8-dim chunk c and writes 8 transposed rows
+// (dims 8c..8c+7) of KPT tokens.  Lanes with odd c write each pair of rows in
+// the opposite order, so every store instruction covers both bank halves.
 template <int D, int NT>
 struct TStage {
   static constexpr int CPR = D / 8;
@@ -71,23 +81,37 @@ struct TStage {
 #pragma unroll
     for (int kk = 0; kk < KPT; ++kk) r[kk] = *(const u32x4 *)(g + (grp * KPT + kk) * D + c * 8);
   }
+  // byte offset of this thread's KPT tokens inside transposed row d
+  __device__ __forceinline__ static int unit_off(int d, int grp) {
+    if constexpr (KPT == 4) {
+      const int u = tpos(grp * 4) >> 2;               // 8-byte unit 0..15
+      return (((u >> 1) ^ tswz(d)) << 4) + ((u & 1) << 3);
+    } else {
+      const int u = tpos(grp * 2) >> 1;               // 4-byte unit 0..31
+      return (((u >> 2) ^ tswz(d)) << 4) + ((u & 3) << 2);
+    }
+  }
   __device__ __forceinline__ void store(bf16 *lds) const {
-    constexpr int TR = TileGeom<D>::TROW;
     const int c = threadIdx.x % CPR, grp = threadIdx.x / CPR;
-    const int pos = tpos(grp * KPT);
+    const bool odd = c & 1;
+    char *base = (char *)lds;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {  // word w holds dims 8c+2w (low half), 8c+2w+1 (high half)
+      const int dA = c * 8 + 2 * w + (odd ? 1 : 0);
+      const int dB = dA ^ 1;
       if constexpr (KPT == 4) {
         u32x2 lo, hi;
         lo[0] = (r[0][w] & 0xffffu) | (r[1][w] << 16);
         lo[1] = (r[2][w] & 0xffffu) | (r[3][w] << 16);
         hi[0] = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
         hi[1] = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
-        *(u32x2 *)(lds + (c * 8 + 2 * w) * TR + pos) = lo;
-        *(u32x2 *)(lds + (c * 8 + 2 * w + 1) * TR + pos) = hi;
+        *(u32x2 *)(base + dA * (kBlock * 2) + unit_off(dA, grp)) = odd ? hi : lo;
+        *(u32x2 *)(base + dB * (kBlock * 2) + unit_off(dB, grp)) = odd ? lo : hi;
       } else {
-        *(uint32_t *)(lds + (c * 8 + 2 * w) * TR + pos) = (r[0][w] & 0xffffu) | (r[1][w] << 16);
-        *(uint32_t *)(lds + (c * 8 + 2 * w + 1) * TR + pos) = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
+        const uint32_t lo = (r[0][w] & 0xffffu) | (r[1][w] << 16);
+        const uint32_t hi = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
+        *(uint32_t *)(base + dA * (kBlock * 2) + unit_off(dA, grp)) = odd ? hi : lo;
+        *(uint32_t *)(base + dB * (kBlock * 2) + unit_off(dB, grp)) = odd ? lo : hi;
       }
     }
   }
@@ -104,42 +128,86 @@ __device__ __forceinline__ bf16x8 pack_acc_operand(const f32x16 &t, int half) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// Ascending union of two sorted CSR (or CSC) lists -- the two 64-token
-// blocks of a 128-token tile -- with defensive skipping of out-of-range ids.
-// Every step advances at least one list, so the walk ends after at most the
-// total list length.  Plain scalars (no arrays) keep the cursors in SGPRs.
-struct PairWalk {
-  int p0, e0, p1, e1;
-  const int32_t *ids;
-  int n_ids;
+// Union of two CSR (or CSC) rows -- the two 64-token blocks of a 128-token
+// tile -- held as two LDS bitmaps over block ids plus a summary bitmap of the
+// non-empty words.  Built once per workgroup (atomicOr per list entry, so row
+// order, duplicates and out-of-range ids cannot matter: bad ids are dropped),
+// then walked in ascending order by every wave with scalar bit tricks.
+//   LDS layout (32-bit words): bm[0..nw) row 0, bm[nw..2nw) row 1,
+//   sm[0..nsw) summary (bit w set when word w of either row is non-zero).
+struct PairBitmap {
+  uint32_t *bm;
+  uint32_t *sm;
+  int nw, nsw;
 
-  __device__ __forceinline__ void init(const int32_t *ptr, int first, int n_rows, int nnz) {
-    p0 = e0 = p1 = e1 = 0;
-    if (first < n_rows) {
-      p0 = clamp_i(ptr[first], 0, nnz);
-      e0 = clamp_i(ptr[first + 1], p0, nnz);
+  __host__ __device__ static int words(int n_ids) { return (n_ids + 31) / 32; }
+  __host__ __device__ static int summary_words(int n_ids) { return (words(n_ids) + 31) / 32; }
+  __host__ __device__ static size_t lds_bytes(int n_ids) {
+    return (size_t)(2 * words(n_ids) + summary_words(n_ids)) * sizeof(uint32_t);
+  }
+
+  __device__ __forceinline__ void init(uint32_t *lds, int n_ids) {
+    nw = words(n_ids);
+    nsw = summary_words(n_ids);
+    bm = lds;
+    sm = lds + 2 * nw;
+  }
+
+  // Caller: every thread of the workgroup, nt threads.  Ends with a barrier.
+  __device__ void build(const int32_t *ptr, int first, int n_rows, int nnz, const int32_t *ids,
+                        int n_ids, int nt) {
+    for (int i = threadIdx.x; i < 2 * nw + nsw; i += nt) bm[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = first + r;
+      if (row < n_rows) {
+        const int p = clamp_i(ptr[row], 0, nnz);
+        const int e = clamp_i(ptr[row + 1], p, nnz);
+        for (int x = p + threadIdx.x; x < e; x += nt) {
+          const int j = ids[x];
+          if (j >= 0 && j < n_ids) atomicOr(&bm[r * nw + (j >> 5)], 1u << (j & 31));
+        }
+      }
     }
-    if (first + 1 < n_rows) {
-      p1 = clamp_i(ptr[first + 1], 0, nnz);
-      e1 = clamp_i(ptr[first + 2], p1, nnz);
+    __syncthreads();
+    for (int w = threadIdx.x; w < nw; w += nt)
+      if (bm[w] | bm[nw + w]) atomicOr(&sm[w >> 5], 1u << (w & 31));
+    __syncthreads();
+  }
+};
+
+// Ascending walk over a PairBitmap.  All state is wave-uniform (SGPRs).
+struct PairIter {
+  int sw, w;
+  uint32_t sbits, rem, b0, b1;
+  int j;          // current block id
+  bool in0, in1;  // listed by row 0 / row 1
+
+  __device__ __forceinline__ void start() {
+    sw = -1;
+    w = 0;
+    sbits = rem = b0 = b1 = 0u;
+  }
+  __device__ __forceinline__ bool next(const PairBitmap &pb) {
+    while (rem == 0u) {
+      while (sbits == 0u) {
+        if (++sw >= pb.nsw) return false;
+        sbits = __builtin_amdgcn_readfirstlane(pb.sm[sw]);
+      }
+      const int wb = __builtin_ctz(sbits);
+      sbits &= sbits - 1u;
+      w = sw * 32 + wb;
+      b0 = __builtin_amdgcn_readfirstlane(pb.bm[w]);
+      b1 = __builtin_amdgcn_readfirstlane(pb.bm[pb.nw + w]);
+      rem = b0 | b1;
     }
-  }
-  __device__ __forceinline__ bool ok(int x) const { return x >= 0 && x < n_ids; }
-  __device__ __forceinline__ int next() {
-    while (p0 < e0 && !ok(ids[p0])) ++p0;
-    while (p1 < e1 && !ok(ids[p1])) ++p1;
-    int j = INT32_MAX;
-    if (p0 < e0) j = ids[p0];
-    if (p1 < e1) j = min(j, (int)ids[p1]);
-    return j;
-  }
-  // Whether list `which` (0 or 1) holds j at its cursor.
-  __device__ __forceinline__ bool has(int which, int j) const {
-    return which == 0 ? (p0 < e0 && ids[p0] == j) : (p1 < e1 && ids[p1] == j);
-  }
-  __device__ __forceinline__ void advance(int j) {
-    if (p0 < e0 && ids[p0] == j) ++p0;
-    if (p1 < e1 && ids[p1] == j) ++p1;
+    const int bit = __builtin_ctz(rem);
+    rem &= rem - 1u;
+    j = w * 32 + bit;
+    in0 = (b0 >> bit) & 1u;
+    in1 = (b1 >> bit) & 1u;
+    return true;
   }
 };
 
