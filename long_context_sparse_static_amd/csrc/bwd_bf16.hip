@@ -109,6 +109,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     dlt = a.delta[(size_t)bh * a.L + q_tok];
   }
 
+  TReadBases tb;
+  tb.init(n, hh);
+
   PairBitmap pb;
   pb.init(dyn_lds, a.ix.n_kblocks);
   pb.build(a.ix.row_ptr + (size_t)hidx * (nqb + 1), tile * kBwdTB, nqb, a.ix.nnz, a.ix.col_idx,
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
         const bf16x8 bds = pack_acc_operand(s[ks >> 1], ks & 1);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const bf16x8 akt = *(const bf16x8 *)(bb.kt + t_off(32 * mt + n, 2 * ks + hh));
+          const bf16x8 akt = *(const bf16x8 *)((const char *)bb.kt + tb.at(mt, ks));
           acc[mt] = mfma_32x32x16(akt, bds, acc[mt]);
         }
       }
@@ -274,6 +277,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) dk[mt] = dv[mt] = f32x16{};
 
+  TReadBases tb;
+  tb.init(n, hh);
+
   PairBitmap pb;
   pb.init(dyn_lds, nqb);
   pb.build(a.ix.col_ptr + (size_t)hidx * (nkb + 1), tile * kBwdTB, nkb, a.ix.nnz, a.ix.row_idx, nqb,
@@ -350,8 +356,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
           const bf16x8 bds = pack_acc_operand(dp, half);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            const bf16x8 adot = *(const bf16x8 *)(bb.dot + t_off(32 * mt + n, 2 * ks + hh));
-            const bf16x8 aqt = *(const bf16x8 *)(bb.qt + t_off(32 * mt + n, 2 * ks + hh));
+            const bf16x8 adot = *(const bf16x8 *)((const char *)bb.dot + tb.at(mt, ks));
+            const bf16x8 aqt = *(const bf16x8 *)((const char *)bb.qt + tb.at(mt, ks));
             dv[mt] = mfma_32x32x16(adot, bp, dv[mt]);
             dk[mt] = mfma_32x32x16(aqt, bds, dk[mt]);
           }

@@ -14,9 +14,11 @@
 //   * the workgroup first marks both query blocks' KV-block lists in an LDS
 //     bitmap and then walks their ascending union with scalar bit scans; a
 //     wave computes a KV block only if its own query block lists it;
-//   * per KV block, K (row-major) and V (transposed, [d][key]) are staged in
-//     LDS once for the 4 waves, double-buffered: one barrier per block, the
-//     next block's global loads in flight during the current block's math;
+//   * per KV block, K and V are staged row-major in LDS once for the 4
+//     waves, double-buffered: one barrier per block, the next block's global
+//     loads in flight during the current block's math; V reaches the matrix
+//     cores through the transposing LDS read (ds_read_b64_tr_b16), so no
+//     transposition is ever written;
 //   * each wave owns 32 query rows and computes S^T = K Q^T (keys x queries)
 //     so that a lane owns one query: row max / row sum need no cross-lane
 //     traffic except one swap between the two lane halves;
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int KS = D / 16;   // k-steps of S^T = K Q^T
   constexpr int MT = D / 32;   // 32-row tiles of O^T
   __shared__ __attribute__((aligned(16))) bf16 klds[2][G::ROW_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 vlds[2][G::T_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 vlds[2][TrRead<D>::ELEMS];
   extern __shared__ uint32_t dyn_lds[];
 
   const int nqb = a.ix.n_qblocks;
@@ -73,6 +75,9 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   for (int ks = 0; ks < KS; ++ks)
     bq[ks] = q_valid ? *(const bf16x8 *)(qg + (size_t)q_tok * D + ks * 16 + hh * 8) : bf16x8{};
 
+  TrRead<D> vr;
+  vr.init(lane);
+
   PairBitmap pb;
   pb.init(dyn_lds, a.ix.n_kblocks);
   pb.build(a.ix.row_ptr + (size_t)hidx * (nqb + 1), tile * 2, nqb, a.ix.nnz, a.ix.col_idx,
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const float c = a.scale * kLog2e;
 
   RowStage<D, kFwdThreads> sk;
-  TStage<D, kFwdThreads> sv;
+  RowStage<D, kFwdThreads, TrRead<D>::TRS> sv;
   bool have = it.next(pb);
   int j = it.j;
   bool act = q_valid && (my_r == 0 ? it.in0 : it.in1);
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
         const bf16x8 pbk = pack_acc_operand(s[ks >> 1], ks & 1);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const bf16x8 av = *(const bf16x8 *)(vl + t_off(32 * mt + n, 2 * ks + hh));
+          const bf16x8 av = vr.load(vl, mt, ks);
           oacc[mt] = mfma_32x32x16(av, pbk, oacc[mt]);
         }
       }
@@ -211,7 +216,7 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
 }  // namespace
 
 size_t fwd_bf16_lds_bytes(int d, int n_kblocks) {
-  const size_t stat = 2 * (kBlock * (d + 8) + d * kBlock) * sizeof(uint16_t);
+  const size_t stat = 2 * (kBlock * (d + 8) + kBlock * (d + 32)) * sizeof(uint16_t);
   return stat + PairBitmap::lds_bytes(n_kblocks);
 }
 

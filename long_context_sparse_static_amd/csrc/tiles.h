@@ -41,8 +41,9 @@ struct TileGeom {
   static constexpr int T_ELEMS = D * kBlock;
 };
 
-// Row-major staging of one 64 x D tile by NT threads.
-template <int D, int NT>
+// Row-major staging of one 64 x D tile by NT threads into LDS rows of RS
+// elements (RS >= D).
+template <int D, int NT, int RS = TileGeom<D>::ROW>
 struct RowStage {
   static constexpr int CPR = D / 8;
   static constexpr int N = kBlock * CPR / NT;
@@ -60,7 +61,7 @@ struct RowStage {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int ch = threadIdx.x + i * NT;
-      *(u32x4 *)(lds + (ch / CPR) * TileGeom<D>::ROW + (ch % CPR) * 8) = r[i];
+      *(u32x4 *)(lds + (ch / CPR) * RS + (ch % CPR) * 8) = r[i];
     }
   }
 };
@@ -94,27 +95,78 @@ struct TStage {
   __device__ __forceinline__ void store(bf16 *lds) const {
     const int c = threadIdx.x % CPR, grp = threadIdx.x / CPR;
     const bool odd = c & 1;
+    // v_perm selectors: the low halves (dims 8c+2w) or the high halves
+    // (dims 8c+2w+1) of two 32-bit words; odd lanes take them swapped.
+    const uint32_t sel_a = odd ? 0x07060302u : 0x05040100u;
+    const uint32_t sel_b = odd ? 0x05040100u : 0x07060302u;
     char *base = (char *)lds;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {  // word w holds dims 8c+2w (low half), 8c+2w+1 (high half)
       const int dA = c * 8 + 2 * w + (odd ? 1 : 0);
       const int dB = dA ^ 1;
       if constexpr (KPT == 4) {
-        u32x2 lo, hi;
-        lo[0] = (r[0][w] & 0xffffu) | (r[1][w] << 16);
-        lo[1] = (r[2][w] & 0xffffu) | (r[3][w] << 16);
-        hi[0] = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
-        hi[1] = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
-        *(u32x2 *)(base + dA * (kBlock * 2) + unit_off(dA, grp)) = odd ? hi : lo;
-        *(u32x2 *)(base + dB * (kBlock * 2) + unit_off(dB, grp)) = odd ? lo : hi;
+        u32x2 va, vb;
+        va[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], sel_a);
+        va[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], sel_a);
+        vb[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], sel_b);
+        vb[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], sel_b);
+        *(u32x2 *)(base + dA * (kBlock * 2) + unit_off(dA, grp)) = va;
+        *(u32x2 *)(base + dB * (kBlock * 2) + unit_off(dB, grp)) = vb;
       } else {
-        const uint32_t lo = (r[0][w] & 0xffffu) | (r[1][w] << 16);
-        const uint32_t hi = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
-        *(uint32_t *)(base + dA * (kBlock * 2) + unit_off(dA, grp)) = odd ? hi : lo;
-        *(uint32_t *)(base + dB * (kBlock * 2) + unit_off(dB, grp)) = odd ? lo : hi;
+        *(uint32_t *)(base + dA * (kBlock * 2) + unit_off(dA, grp)) = __builtin_amdgcn_perm(r[1][w], r[0][w], sel_a);
+        *(uint32_t *)(base + dB * (kBlock * 2) + unit_off(dB, grp)) = __builtin_amdgcn_perm(r[1][w], r[0][w], sel_b);
       }
     }
   }
+};
+
+// Row-major 64 x D tile read through the gfx950 transposing LDS load
+// (ds_read_b64_tr_b16) as the A operand of a 32x32x16 MFMA whose k index
+// runs over the 64 tokens: A[m = d][k = token].  Within each 16-lane group
+// the instruction hands output lane i element i%4 of the 8-byte chunks that
+// source lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4 address.  Source lane s of
+// group gi (lane = 16*gi + s, plus 32*hh) therefore addresses token
+// 16*ks + 8*r + 4*hh + s/4 at dims 32*mt + 16*gi + 4*(s%4); two reads
+// (r = 0, 1) give the lane d = 32*mt + lane%32 and the 8 tokens that the
+// register order of pack_acc_operand() assigns to logical k = 8*hh .. +7.
+// Row stride TRS = D + 32 elements puts the 32 lanes of one read phase on
+// all 64 banks (row r starts at bank 16*r mod 64).
+template <int D>
+struct TrRead {
+  static constexpr int TRS = D + 32;           // row stride (elements)
+  static constexpr int ELEMS = kBlock * TRS;
+  int base;                                    // byte offset of this lane
+  __device__ __forceinline__ void init(int lane) {
+    const int s = lane & 15, gi = (lane >> 4) & 1, hh = lane >> 5;
+    base = ((s >> 2) + 4 * hh) * TRS * 2 + (16 * gi + 4 * (s & 3)) * 2;
+  }
+  __device__ __forceinline__ bf16x8 load(const bf16 *tile, int mt, int ks) const {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4 lds_s4;
+    const char *p = (const char *)tile + base + (16 * ks) * TRS * 2 + 64 * mt;
+    const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)p);
+    const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(p + 8 * TRS * 2));
+    typedef short s8 __attribute__((ext_vector_type(8)));
+    const s8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
+// Byte offsets of one lane's reads of a transposed tile as the A operand of
+// a 32x32x16 MFMA: row d = 32*mt + n (n = lane % 32), logical chunk
+// q = 2*ks + hh.  Because tswz(32*mt + n) = tswz(n) ^ 2*mt for mt < 4, the
+// physical chunk is (2*(ks ^ mt)) ^ sigma with a per-lane sigma, so four
+// per-lane bases (one per value of ks ^ mt) plus the immediate mt * 4096
+// cover every read: no address arithmetic inside the loop.
+struct TReadBases {
+  int b[4];
+  __device__ __forceinline__ void init(int n, int hh) {
+    const int sigma = (hh ^ tswz(n)) & 7;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) b[x] = n * (kBlock * 2) + (((2 * x) ^ sigma) << 4);
+  }
+  // byte offset of (mt, ks)
+  __device__ __forceinline__ int at(int mt, int ks) const { return b[ks ^ mt] + mt * 32 * kBlock * 2; }
 };
 
 // Rows of a 32x32 accumulator pair (64 tokens x 32 columns, fp32) converted to
