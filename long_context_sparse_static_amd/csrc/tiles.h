@@ -180,14 +180,16 @@ __device__ __forceinline__ bf16x8 pack_acc_operand(const f32x16 &t, int half) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// Union of two CSR (or CSC) rows -- the two 64-token blocks of a 128-token
-// tile -- held as two LDS bitmaps over block ids plus a summary bitmap of the
-// non-empty words.  Built once per workgroup (atomicOr per list entry, so row
-// order, duplicates and out-of-range ids cannot matter: bad ids are dropped),
-// then walked in ascending order by every wave with scalar bit tricks.
-//   LDS layout (32-bit words): bm[0..nw) row 0, bm[nw..2nw) row 1,
-//   sm[0..nsw) summary (bit w set when word w of either row is non-zero).
-struct PairBitmap {
+// Union of R consecutive CSR (or CSC) rows -- the 64-token blocks of one
+// workgroup tile -- held as R LDS bitmaps over block ids plus a summary
+// bitmap of the non-empty words.  Built once per workgroup (atomicOr per list
+// entry, so row order, duplicates and out-of-range ids cannot matter: bad ids
+// are dropped), then walked in ascending order by every wave with scalar bit
+// tricks.
+//   LDS layout (32-bit words): bm[r*nw .. r*nw+nw) row r, then sm[0..nsw)
+//   (bit w set when word w of any row is non-zero).
+template <int R>
+struct RowsBitmap {
   uint32_t *bm;
   uint32_t *sm;
   int nw, nsw;
@@ -195,23 +197,23 @@ struct PairBitmap {
   __host__ __device__ static int words(int n_ids) { return (n_ids + 31) / 32; }
   __host__ __device__ static int summary_words(int n_ids) { return (words(n_ids) + 31) / 32; }
   __host__ __device__ static size_t lds_bytes(int n_ids) {
-    return (size_t)(2 * words(n_ids) + summary_words(n_ids)) * sizeof(uint32_t);
+    return (size_t)(R * words(n_ids) + summary_words(n_ids)) * sizeof(uint32_t);
   }
 
   __device__ __forceinline__ void init(uint32_t *lds, int n_ids) {
     nw = words(n_ids);
     nsw = summary_words(n_ids);
     bm = lds;
-    sm = lds + 2 * nw;
+    sm = lds + R * nw;
   }
 
   // Caller: every thread of the workgroup, nt threads.  Ends with a barrier.
   __device__ void build(const int32_t *ptr, int first, int n_rows, int nnz, const int32_t *ids,
                         int n_ids, int nt) {
-    for (int i = threadIdx.x; i < 2 * nw + nsw; i += nt) bm[i] = 0u;
+    for (int i = threadIdx.x; i < R * nw + nsw; i += nt) bm[i] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < R; ++r) {
       const int row = first + r;
       if (row < n_rows) {
         const int p = clamp_i(ptr[row], 0, nnz);
@@ -223,25 +225,33 @@ struct PairBitmap {
       }
     }
     __syncthreads();
-    for (int w = threadIdx.x; w < nw; w += nt)
-      if (bm[w] | bm[nw + w]) atomicOr(&sm[w >> 5], 1u << (w & 31));
+    for (int w = threadIdx.x; w < nw; w += nt) {
+      uint32_t any = 0u;
+#pragma unroll
+      for (int r = 0; r < R; ++r) any |= bm[r * nw + w];
+      if (any) atomicOr(&sm[w >> 5], 1u << (w & 31));
+    }
     __syncthreads();
   }
 };
 
-// Ascending walk over a PairBitmap.  All state is wave-uniform (SGPRs).
-struct PairIter {
+// Ascending walk over a RowsBitmap.  All state is wave-uniform (SGPRs).
+template <int R>
+struct RowsIter {
   int sw, w;
-  uint32_t sbits, rem, b0, b1;
+  uint32_t sbits, rem;
+  uint32_t b[R];
   int j;          // current block id
-  bool in0, in1;  // listed by row 0 / row 1
+  uint32_t mask;  // bit r set: listed by row r
 
   __device__ __forceinline__ void start() {
     sw = -1;
     w = 0;
-    sbits = rem = b0 = b1 = 0u;
+    sbits = rem = 0u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) b[r] = 0u;
   }
-  __device__ __forceinline__ bool next(const PairBitmap &pb) {
+  __device__ __forceinline__ bool next(const RowsBitmap<R> &pb) {
     while (rem == 0u) {
       while (sbits == 0u) {
         if (++sw >= pb.nsw) return false;
@@ -250,16 +260,32 @@ struct PairIter {
       const int wb = __builtin_ctz(sbits);
       sbits &= sbits - 1u;
       w = sw * 32 + wb;
-      b0 = __builtin_amdgcn_readfirstlane(pb.bm[w]);
-      b1 = __builtin_amdgcn_readfirstlane(pb.bm[pb.nw + w]);
-      rem = b0 | b1;
+      rem = 0u;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        b[r] = __builtin_amdgcn_readfirstlane(pb.bm[r * pb.nw + w]);
+        rem |= b[r];
+      }
     }
     const int bit = __builtin_ctz(rem);
     rem &= rem - 1u;
     j = w * 32 + bit;
-    in0 = (b0 >> bit) & 1u;
-    in1 = (b1 >> bit) & 1u;
+    mask = 0u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) mask |= ((b[r] >> bit) & 1u) << r;
     return true;
+  }
+};
+
+// Two-row forms used by the backward kernels.
+using PairBitmap = RowsBitmap<2>;
+struct PairIter : RowsIter<2> {
+  bool in0, in1;
+  __device__ __forceinline__ bool next(const PairBitmap &pb) {
+    const bool ok = RowsIter<2>::next(pb);
+    in0 = mask & 1u;
+    in1 = (mask >> 1) & 1u;
+    return ok;
   }
 };
 
