@@ -18,12 +18,14 @@ the full-layer and whole-hybrid prefill rates, the roofline of the dominant
 kernel and the CPU oracle baseline are reported alongside.
 
 Other workloads (--workload): attnsink8k, blocksparse32k, blocksparse128k,
-train64k (forward + backward), decode128k.
+attnsink128k, train64k (forward + backward), and copy1g (a plain 1 GiB device
+copy, the calibration kernel for the HBM byte counters).
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -46,6 +48,26 @@ SINK_BLOCKS, WINDOW_BLOCKS = 1, 64
 SINK_TOK, WINDOW_TOK = 64, 4096
 N_LAYERS, FULL_FIRST, FULL_LAST = 32, 11, 21
 DEC_BATCH = 16
+
+# HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc runs of
+# the same workload (FETCH_SIZE, then WRITE_SIZE), each scaled by what the
+# counter reads for copy1g (1 GiB read + 1 GiB written).  Keyed by workload and
+# a hash of the kernel's sources: a changed kernel reports null until its
+# counters are taken again.
+KERNEL_SOURCES = ("fwd_bf16.hip", "tiles.h", "device_common.h", "kernels.h")
+TRAFFIC = {}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "long_context_sparse_static_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload):
+    return TRAFFIC.get((workload, kernel_source_hash()))
 
 
 def log(msg):
@@ -207,7 +229,8 @@ class Hybrid128k:
             ),
             roofline=dict(bound="mfma", kernel="fwd_bf16_kernel<128>", achieved=achieved,
                           peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=achieved / PEAK_BF16_TFLOPS,
-                          traffic=None, flop_per_launch=flops_per_launch, avg_launch_ms=avg_ms),
+                          traffic=traffic_for(self.name), flop_per_launch=flops_per_launch,
+                          avg_launch_ms=avg_ms, kernel_source_hash=kernel_source_hash()),
             config=dict(workload="hybrid128k: 32 layers (11..21 full, 21 AttnSink sink 64 + window 4096), "
                         "prefill B=1 L=131072 H=32 d=128 + decode 16 seqs at t=131072",
                         global_batch=DEC_BATCH, seq_len=self.L, layers=N_LAYERS,
@@ -250,17 +273,45 @@ class Prefill:
         extra = dict(fwd_tflops=fl / (t_f * 1e-3) / 1e12, fwd_ms=t_f, block_pairs=self.pairs)
         value = extra["fwd_tflops"]
         kernel, per_launch, avg = "fwd_bf16_kernel<128>", fl, t_f
+        traffic = traffic_for(self.name)
         if self.backward:
             t_b = sum(times["bwd"]) / steps
             extra.update(bwd_tflops=2.5 * fl / (t_b * 1e-3) / 1e12, bwd_ms=t_b)
             value = 3.5 * fl / ((t_f + t_b) * 1e-3) / 1e12
             kernel, per_launch, avg = "attn_sparse_bwd (delta + dkdv + dq)", 2.5 * fl, t_b
+            traffic = None
         ach = per_launch / (avg * 1e-3) / 1e12
         return dict(value=value, extra=extra,
                     roofline=dict(bound="mfma", kernel=kernel, achieved=ach, peak=PEAK_BF16_TFLOPS,
-                                  unit="TFLOP/s", frac=ach / PEAK_BF16_TFLOPS, traffic=None),
+                                  unit="TFLOP/s", frac=ach / PEAK_BF16_TFLOPS, traffic=traffic,
+                                  kernel_source_hash=kernel_source_hash()),
                     config=dict(workload=f"{self.name}: B=1 H=32 L={self.L} d=128 bf16",
                                 global_batch=1, seq_len=self.L, parallelism="single GPU"))
+
+
+class Copy1G:
+    """Calibration: one elementwise kernel that reads 1 GiB and writes 1 GiB."""
+    name = "copy1g"
+    BYTES = 1 << 30
+
+    def __init__(self):
+        self.src = torch.ones(self.BYTES // 2, dtype=torch.bfloat16, device="cuda")
+        self.dst = torch.empty_like(self.src)
+        torch.cuda.synchronize()
+
+    def step(self, timer):
+        with timer.span("copy"):
+            torch.neg(self.src, out=self.dst)
+
+    def report(self, times, steps):
+        t = sum(times["copy"]) / steps
+        gbps = 2 * self.BYTES / (t * 1e-3) / 1e9
+        return dict(value=gbps, extra=dict(copy_ms=t, bytes_read=self.BYTES, bytes_written=self.BYTES),
+                    roofline=dict(bound="hbm", kernel="torch neg (elementwise copy)", achieved=gbps,
+                                  peak=PEAK_HBM_GBPS, unit="GB/s", frac=gbps / PEAK_HBM_GBPS,
+                                  traffic=None),
+                    config=dict(workload="copy1g: read 1 GiB, write 1 GiB", global_batch=1,
+                                parallelism="single GPU"))
 
 
 def make_workload(name):
@@ -276,6 +327,8 @@ def make_workload(name):
         return Prefill(name, lcs.attnsink_pattern(1, 64), 131072, 5)
     if name == "train64k":
         return Prefill(name, lcs.attnsink_pattern(1, 64), 65536, 4, backward=True)
+    if name == "copy1g":
+        return Copy1G()
     raise SystemExit(f"unknown workload {name}")
 
 

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   pb.build(a.ix.row_ptr + (size_t)hidx * (nqb + 1), tile * kBwdTB, nqb, a.ix.nnz, a.ix.col_idx,
            a.ix.n_kblocks, kBwdThreads);
   PairIter it;
-  it.start();
+  it.start(a.ix.n_kblocks);
 
   f32x16 acc[MT];
 #pragma unroll
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   pb.build(a.ix.col_ptr + (size_t)hidx * (nkb + 1), tile * kBwdTB, nkb, a.ix.nnz, a.ix.row_idx, nqb,
            kBwdThreads);
   PairIter it;
-  it.start();
+  it.start(nqb);
 
   RowStage<D, kBwdThreads> sq, sdo;
   TStage<D, kBwdThreads> sqt, sdot;

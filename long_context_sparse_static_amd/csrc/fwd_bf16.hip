@@ -30,7 +30,12 @@
 //   * Online softmax in base 2 with scale*log2(e) folded into one FMA; the
 //     running max is only moved when a block raises it by more than 2^8, so
 //     the O rescale is skipped on most blocks (exact: the final O / l uses
-//     the same reference point for both sums).
+//     the same reference point for both sums).  The row sum l adds the same
+//     bf16-rounded P that enters the P V product (two per dot2 instruction),
+//     so numerator and denominator see identical weights.
+//   * The union walk starts at the 64-block boundary below the workgroup's
+//     last query block and wraps around, so neighbouring workgroups stream
+//     the same key blocks at the same time and L2 serves the repeats.
 #include "device_common.h"
 #include "kernels.h"
 #include "tiles.h"
@@ -183,13 +188,22 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   };
   auto softmax_exp = [&](f32x16 (&s)[2], float msub, int e) {
     const int t = e >> 4, r = e & 15;
-    const float p = fast_exp2(__builtin_fmaf(s[t][r], c, -msub));
-    l_part += p;
-    s[t][r] = p;
+    s[t][r] = fast_exp2(__builtin_fmaf(s[t][r], c, -msub));
   };
   // k-step ks of O^T (D x 32 queries) += V^T (D x 64 keys) P^T (64 keys x 32 q)
   auto pv_ks = [&](f32x16 (&p)[2], const char *vt, int ks) {
-    const bf16x8 pbk = pack_acc_operand(p[ks >> 1], ks & 1);
+    // The packed words are built here, not read back out of the bf16x8:
+    // extracting 32-bit words of a bit-cast bf16x8 for the dot2 compiled to
+    // four reads of word 0 (hipcc, ROCm 7.2).
+    u32x4 pw;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 8 * (ks & 1) + 2 * e;
+      const uint32_t w = pack_bf16x2(p[ks >> 1][r], p[ks >> 1][r + 1]);
+      l_part = sum_bf16x2(w, l_part);
+      pw[e] = w;
+    }
+    const bf16x8 pbk = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) oacc[mt] = mfma_32x32x16(v_operand(vt, mt, ks), pbk, oacc[mt]);
   };
@@ -214,7 +228,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   pb.build(a.ix.row_ptr + (size_t)hidx * (nqb + 1), tile * 2, nqb, a.ix.nnz, a.ix.col_idx,
            a.ix.n_kblocks, kFwdThreads);
   RowsIter<2> it;
-  it.start();
+  it.start(a.ix.n_kblocks, min(tile * 2 + 1, nqb - 1) & ~63);
   auto listed_by_me = [&](uint32_t mask) { return q_valid && ((mask >> my_r) & 1u); };
 
   // ---- double-buffered walk: block j in buffers [ib] while block j+1 loads

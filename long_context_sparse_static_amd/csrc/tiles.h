@@ -235,35 +235,66 @@ struct RowsBitmap {
   }
 };
 
-// Ascending walk over a RowsBitmap.  All state is wave-uniform (SGPRs).
+// Walk over a RowsBitmap: ids rot..n_ids-1 ascending, then 0..rot-1
+// ascending (rot = 0: plain ascending order).  All state is wave-uniform
+// (SGPRs).  A rotation shared by the workgroups that run side by side makes
+// them touch the same key blocks at about the same time, so the tiles they
+// stream are served from L2 instead of being refetched.
 template <int R>
 struct RowsIter {
-  int sw, w;
+  int sw, sw_last, w, lo, hi, rot;
+  bool second;
   uint32_t sbits, rem;
   uint32_t b[R];
   int j;          // current block id
   uint32_t mask;  // bit r set: listed by row r
 
-  __device__ __forceinline__ void start() {
-    sw = -1;
-    w = 0;
-    sbits = rem = 0u;
+  __device__ __forceinline__ void start(int n_ids, int rotate = 0) {
+    rot = rotate < 0 ? 0 : (rotate > n_ids ? n_ids : rotate);
+    second = false;
+    begin(rot, n_ids);
 #pragma unroll
     for (int r = 0; r < R; ++r) b[r] = 0u;
+  }
+  // next pass covers ids [l, h)
+  __device__ __forceinline__ void begin(int l, int h) {
+    lo = l;
+    hi = h;
+    sbits = rem = 0u;
+    if (l >= h) {
+      sw = 0;
+      sw_last = -1;
+    } else {
+      sw = ((l >> 5) >> 5) - 1;
+      sw_last = ((h - 1) >> 5) >> 5;
+    }
+  }
+  // bits of [first, last] inside the 32-bit word covering ids 32*word ..
+  __device__ __forceinline__ static uint32_t span_mask(int word, int first, int last) {
+    uint32_t m = ~0u;
+    if (word == (first >> 5)) m &= ~0u << (first & 31);
+    if (word == (last >> 5)) m &= (last & 31) == 31 ? ~0u : ((2u << (last & 31)) - 1u);
+    return m;
   }
   __device__ __forceinline__ bool next(const RowsBitmap<R> &pb) {
     while (rem == 0u) {
       while (sbits == 0u) {
-        if (++sw >= pb.nsw) return false;
-        sbits = __builtin_amdgcn_readfirstlane(pb.sm[sw]);
+        if (++sw > sw_last) {
+          if (second) return false;
+          second = true;
+          begin(0, rot);
+          continue;
+        }
+        sbits = __builtin_amdgcn_readfirstlane(pb.sm[sw]) & span_mask(sw, lo >> 5, (hi - 1) >> 5);
       }
       const int wb = __builtin_ctz(sbits);
       sbits &= sbits - 1u;
       w = sw * 32 + wb;
+      const uint32_t wm = span_mask(w, lo, hi - 1);
       rem = 0u;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        b[r] = __builtin_amdgcn_readfirstlane(pb.bm[r * pb.nw + w]);
+        b[r] = __builtin_amdgcn_readfirstlane(pb.bm[r * pb.nw + w]) & wm;
         rem |= b[r];
       }
     }
