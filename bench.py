@@ -55,7 +55,10 @@ DEC_BATCH = 16
 # a hash of the kernel's sources: a changed kernel reports null until its
 # counters are taken again.
 KERNEL_SOURCES = ("fwd_bf16.hip", "tiles.h", "device_common.h", "kernels.h")
-TRAFFIC = {}
+TRAFFIC = {
+    # fwd_bf16_kernel<128>, average over the 32 launches of one hybrid128k step
+    ("hybrid128k", "91b6a88d43fcea70"): 10.898e9,
+}
 
 
 def kernel_source_hash():
@@ -367,6 +370,61 @@ def cpu_baseline(budget_s=15.0):
                 affinity_cpus=len(os.sched_getaffinity(0)))
 
 
+# ----------------------------------------------------------------------------
+# rocprofv3 CSV summaries (the text kept next to the measurements)
+# ----------------------------------------------------------------------------
+def _short(name, width=72):
+    name = name.replace("(anonymous namespace)::", "")
+    return name if len(name) <= width else name[:width - 3] + "..."
+
+
+def summarize_stats(path, top=12):
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    out = [f"{'kernel':72s} {'calls':>6s} {'total ms':>10s} {'avg ms':>10s} {'min ms':>9s} "
+           f"{'max ms':>9s} {'%':>6s}"]
+    for r in rows[:top]:
+        out.append(f"{_short(r['Name']):72s} {int(r['Calls']):6d} {float(r['TotalDurationNs']) / 1e6:10.3f} "
+                   f"{float(r['AverageNs']) / 1e6:10.4f} {float(r['MinNs']) / 1e6:9.4f} "
+                   f"{float(r['MaxNs']) / 1e6:9.4f} {float(r['Percentage']):6.2f}")
+    return "\n".join(out)
+
+
+def _counter_means(path, counter):
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return acc
+
+
+def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel, scaled so that
+    the copy1g kernel reads 1 GiB and writes 1 GiB."""
+    cf = _counter_means(copy_fetch_csv, "FETCH_SIZE")
+    cw = _counter_means(copy_write_csv, "WRITE_SIZE")
+    neg = lambda d: max(d.items(), key=lambda kv: len(kv[1]))[1]   # the repeated copy kernel
+    copy_kib = Copy1G.BYTES / 1024
+    f_copy, w_copy = np.median(neg(cf)), np.median(neg(cw))
+    kf, kw = copy_kib / f_copy, copy_kib / w_copy
+    fe = _counter_means(fetch_csv, "FETCH_SIZE")
+    wr = _counter_means(write_csv, "WRITE_SIZE")
+    out = [f"calibration (copy1g, 1 GiB read + 1 GiB written): FETCH_SIZE {f_copy:.0f} KiB -> factor {kf:.4f}; "
+           f"WRITE_SIZE {w_copy:.0f} KiB -> factor {kw:.4f}",
+           f"{'kernel':72s} {'n':>4s} {'fetch KiB':>12s} {'write KiB':>12s} {'scaled GB/launch':>17s}"]
+    per_kernel = {}
+    for name in fe:
+        if name not in wr or not name.startswith("void attn::"):
+            continue
+        f, w = float(np.mean(fe[name])), float(np.mean(wr[name]))
+        gb = (f * kf + w * kw) * 1024 / 1e9
+        per_kernel[name] = gb
+        out.append(f"{_short(name):72s} {len(fe[name]):4d} {f:12.0f} {w:12.0f} {gb:17.3f}")
+    return "\n".join(out), per_kernel
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,7 +433,19 @@ def main():
     ap.add_argument("--workload", default="hybrid128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
+                    help="print a summary of a rocprofv3 --stats kernel_stats.csv and exit")
+    ap.add_argument("--summarize-traffic", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="print per-kernel HBM bytes from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
+                         "counter_collection.csv files of a workload and of copy1g, and exit")
     args = ap.parse_args()
+    if args.summarize_stats:
+        print(summarize_stats(args.summarize_stats))
+        return
+    if args.summarize_traffic:
+        print(summarize_traffic(*args.summarize_traffic)[0])
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
         raise SystemExit(2)
