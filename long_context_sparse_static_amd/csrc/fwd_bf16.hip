@@ -9,33 +9,40 @@
 // (atlas.scime.ai summary, "Approach").  Outputs O (bf16) and LSE (fp32,
 // natural log of the sum of exp of the scaled scores).
 //
-// Work decomposition: one workgroup = 4 wave64s = 2 adjacent 64-token query
-// blocks of one (batch, head); each wave owns 32 query rows; two workgroups
-// per CU (two waves per SIMD).
-//   * The workgroup marks both query blocks' KV-block lists in an LDS bitmap
-//     and walks their ascending union with scalar bit scans; a wave computes
-//     a union block only if its own query block lists it.
+// Work decomposition: one workgroup = 8 wave64s = 4 adjacent 64-token query
+// blocks of one (batch, head); each wave owns 32 query rows.  Waves 0-3
+// (group A, query blocks 0-1) and 4-7 (group B, query blocks 2-3) sit in
+// pairs on the four SIMDs (wave w and w+4 share SIMD w).
+//   * Ping-pong: per key block a wave runs a matrix-core step (P V of the
+//     previous block and S of this block: 32 MFMAs) and a vector step
+//     (mask, max, exp, pack: ~120 VALU).  Group B runs one step behind group
+//     A and every step ends at a workgroup barrier, so on each SIMD one wave
+//     is in its matrix-core step while the other is in its vector step: the
+//     two kinds of work overlap instead of queueing behind each other.
+//   * The workgroup marks its four query blocks' KV-block lists in LDS
+//     bitmaps and walks their union with scalar bit scans; a wave computes a
+//     union block only if its own query block lists it.  The walk starts at
+//     the 64-block boundary below the last query block and wraps around, so
+//     the workgroups on one XCD stream the same key blocks at the same time
+//     and L2 serves the repeats.
 //   * K and V tiles go straight from global memory into LDS
 //     (global_load_lds_dwordx4: no staging registers, no LDS store
 //     instructions) into unpadded rows whose 16-byte chunks are XOR-swizzled
-//     so the operand reads below hit all 64 banks.
+//     so the operand reads below hit all 64 banks.  Two K and two V slots;
+//     the tiles of key block t+1 (K) and t (V) are issued two steps before
+//     they are read, by the group that is in its vector step.
 //   * Each wave computes S^T = K Q^T (keys x queries): a lane owns one query,
 //     so row max / row sum need one swap between the two lane halves only.
 //     V reaches the matrix cores through the transposing LDS read
 //     (ds_read_b64_tr_b16) for O^T += V^T P^T; P goes fp32 -> bf16 (RNE).
-//   * Double buffering: the next block's tiles load while the current one is
-//     computed.  Within a block the second half of the exps is interleaved
-//     with the first half of P V; across the two waves of a SIMD the
-//     matrix-core work of one overlaps the softmax of the other.
 //   * Online softmax in base 2 with scale*log2(e) folded into one FMA; the
 //     running max is only moved when a block raises it by more than 2^8, so
 //     the O rescale is skipped on most blocks (exact: the final O / l uses
 //     the same reference point for both sums).  The row sum l adds the same
 //     bf16-rounded P that enters the P V product (two per dot2 instruction),
 //     so numerator and denominator see identical weights.
-//   * The union walk starts at the 64-block boundary below the workgroup's
-//     last query block and wraps around, so neighbouring workgroups stream
-//     the same key blocks at the same time and L2 serves the repeats.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "tiles.h"
@@ -43,8 +50,10 @@
 namespace attn {
 namespace {
 
-constexpr int kFwdWaves = 4;                 // waves per workgroup
+constexpr int kFwdWaves = 8;                 // waves per workgroup
 constexpr int kFwdThreads = kFwdWaves * 64;
+constexpr int kFwdQB = 4;                    // query blocks per workgroup
+constexpr int kLoadWaves = 4;                // waves that issue the tile loads (group B)
 
 // LDS tile layout for direct global->LDS loads: 64 token rows of RB bytes,
 // no padding; 16-byte chunk c of row r is stored at chunk c ^ swz(r).
@@ -54,7 +63,7 @@ struct FwdLayout {
   static constexpr int CPR = RB / 16;                   // chunks per row
   static constexpr int TILE = kBlock * RB;              // bytes per tile
   static constexpr int RPI = 1024 / RB;                 // rows per wave load instruction
-  static constexpr int LPW = kBlock / kFwdWaves / RPI;  // load instructions per wave per tile
+  static constexpr int LPW = kBlock / kLoadWaves / RPI; // load instructions per loading wave per tile
   static_assert(LPW >= 1, "layout");
   // K is read as 16-byte row operands: 16 consecutive rows must use 16
   // distinct bank groups.
@@ -64,19 +73,33 @@ struct FwdLayout {
   __host__ __device__ static int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
+// One position of the union walk.
+struct WalkPos {
+  bool valid;
+  int j;          // key block
+  uint32_t mask;  // bit r: listed by query block r of the workgroup
+};
+
 template <int D>
-__global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   using Lay = FwdLayout<D>;
   constexpr int KS = D / 16;   // k-steps of S^T = K Q^T
   constexpr int MT = D / 32;   // 32-row tiles of O^T
   constexpr int RB = Lay::RB;
-  constexpr int NS = 2 * KS;   // MFMAs of one block's scores
-  __shared__ __attribute__((aligned(1024))) char klds[2][Lay::TILE];
-  __shared__ __attribute__((aligned(1024))) char vlds[2][Lay::TILE];
+  constexpr int NS = 2 * KS;   // MFMAs of one block's scores (== MFMAs of its P V)
+  static_assert(NS == 4 * MT, "step shape");
+  // Two K and two V slots as four distinct objects: every load and read
+  // below names its slot at compile time, so the compiler can see that the
+  // tile loads in flight never touch the tile being read and does not wait
+  // for them (a runtime-indexed slot made it wait for every load at once).
+  __shared__ __attribute__((aligned(1024))) char k0[Lay::TILE];
+  __shared__ __attribute__((aligned(1024))) char k1[Lay::TILE];
+  __shared__ __attribute__((aligned(1024))) char v0[Lay::TILE];
+  __shared__ __attribute__((aligned(1024))) char v1[Lay::TILE];
   extern __shared__ uint32_t dyn_lds[];
 
   const int nqb = a.ix.n_qblocks;
-  const int n_tiles = (nqb + 1) / 2;
+  const int n_tiles = (nqb + kFwdQB - 1) / kFwdQB;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = lin / n_tiles;
   const int tile = n_tiles - 1 - lin % n_tiles;  // heaviest (latest) tiles first
@@ -88,10 +111,11 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const bf16 *vg = (const bf16 *)a.v + base;
 
   const int wave = uniform(threadIdx.x >> 6);
+  const int grp = wave >> 2;                 // 0: group A, 1: group B (one step behind)
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, hh = lane >> 5;
-  const int my_r = wave >> 1;
-  const int qb = tile * 2 + my_r;
+  const int my_r = 2 * grp + ((wave >> 1) & 1);
+  const int qb = tile * kFwdQB + my_r;
   const bool q_valid = qb < nqb;
   const int q_tok = qb * kBlock + (wave & 1) * 32 + n;
 
@@ -101,11 +125,13 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   for (int ks = 0; ks < KS; ++ks)
     bq[ks] = q_valid ? *(const bf16x8 *)(qg + (size_t)q_tok * D + ks * 16 + hh * 8) : bf16x8{};
 
-  // Per-lane global element offsets of this wave's share of a tile load.
+  // Per-lane global element offsets of this wave's share of a tile load
+  // (group B waves load; a wave's share is 16 token rows).
+  const int lw = wave & (kLoadWaves - 1);
   int goff_k[Lay::LPW], goff_v[Lay::LPW];
 #pragma unroll
   for (int i = 0; i < Lay::LPW; ++i) {
-    const int r = wave * (kBlock / kFwdWaves) + i * Lay::RPI + lane / Lay::CPR;
+    const int r = lw * (kBlock / kLoadWaves) + i * Lay::RPI + lane / Lay::CPR;
     const int pc = lane % Lay::CPR;
     goff_k[i] = r * D + ((pc ^ Lay::kswz(r)) << 3);
     goff_v[i] = r * D + ((pc ^ Lay::vswz(r)) << 3);
@@ -115,7 +141,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
     for (int i = 0; i < Lay::LPW; ++i)
       __builtin_amdgcn_global_load_lds(
           (const void *)(g + goff[i]),
-          (__attribute__((address_space(3))) void *)(lds + (wave * (kBlock / kFwdWaves) + i * Lay::RPI) * RB),
+          (__attribute__((address_space(3))) void *)(lds + (lw * (kBlock / kLoadWaves) + i * Lay::RPI) * RB),
           16, 0, 0);
   };
 
@@ -123,31 +149,26 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   // logical chunk 2 ks + hh.  V through the transposing read: source lane s
   // of 16-lane group gi addresses token 16 ks + 8 r + 4 hh + s/4 at dims
   // 32 mt + 16 gi + 4 (s % 4) (see TrRead in tiles.h for the lane algebra).
-  int kofs[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) kofs[ks] = n * RB + (((2 * ks + hh) ^ Lay::kswz(n)) << 4);
-  int vofs[MT];
+  // The swizzles only touch chunk bits, so the offset of k-step ks (V:
+  // dim tile mt) is one per-lane base XOR a constant: kofs(ks) = kbase ^
+  // 32 ks, vofs(mt) = vbase ^ 64 mt (D = 128; D = 64 analogously).
+  const int kbase = n * RB + ((hh ^ Lay::kswz(n)) << 4);
+  auto kofs = [&](int ks) { return kbase ^ (ks << 5); };
+  int vbase;
   {
     const int s = lane & 15, gi = (lane >> 4) & 1;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      vofs[mt] = (4 * hh + (s >> 2)) * RB +
-                 (((4 * mt + 2 * gi + ((s & 3) >> 1)) ^ Lay::vswz(s >> 2)) << 4) + ((s & 1) << 3);
+    vbase = (4 * hh + (s >> 2)) * RB + (((2 * gi + ((s & 3) >> 1)) ^ Lay::vswz(s >> 2)) << 4) +
+            ((s & 1) << 3);
   }
+  auto vofs = [&](int mt) { return vbase ^ (mt << 6); };
   auto v_operand = [&](const char *vt, int mt, int ks) -> bf16x8 {
     typedef short s4 __attribute__((ext_vector_type(4)));
     typedef short s8 __attribute__((ext_vector_type(8)));
     typedef __attribute__((address_space(3))) s4 lds_s4;
-    const char *p = vt + vofs[mt] + 16 * ks * RB;
+    const char *p = vt + vofs(mt) + 16 * ks * RB;
     const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)p);
     const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(p + 8 * RB));
     return __builtin_bit_cast(bf16x8, (s8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-  // i-th MFMA of S^T = K Q^T (i = 2 ks + t)
-  auto s_step = [&](f32x16 (&s)[2], const char *kt, int i) {
-    const int ks = i >> 1, t = i & 1;
-    const bf16x8 ak = *(const bf16x8 *)(kt + kofs[ks] + t * 32 * RB);
-    s[t] = mfma_32x32x16(ak, bq[ks], s[t]);
   };
 
   f32x16 oacc[MT];
@@ -156,23 +177,56 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   float m_run = -INFINITY, l_part = 0.f;
   const float c = a.scale * kLog2e;
 
-  // Block j's causal mask, running max and rare rescale.  Returns the
-  // exponent offset for the block's exps.
-  auto softmax_pre = [&](f32x16 (&s)[2], int j) -> float {
+  f32x16 sc[2];   // S^T of the current block (matrix-core step -> vector step)
+  bf16x8 pk[4];   // packed P of the previous block (vector step -> matrix-core step)
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) pk[ks] = bf16x8{};
+
+  // Matrix-core step: P V of the previous block (V tile vt, P in pk) and
+  // S^T of the current block (K tile kt), interleaved.  It always issues all
+  // 2 NS MFMAs, so the loop has no branches around matrix-core code: when
+  // the previous block is not this wave's, pk is zero (P V adds zeros, as
+  // the masked entries of a dense P would), and scores of a block that is
+  // not this wave's are computed but never read.  The LDS operands of MFMA
+  // pair i + PF are read while pair i runs; a scheduling barrier per pair
+  // keeps the compiler from hoisting every read.
+  auto mfma_step = [&](const char *vt, const char *kt) {
+    constexpr int PF = 2;  // prefetch distance in MFMA pairs
+    bf16x8 ak[PF + 1], av[PF + 1];
+    auto fetch = [&](int i) {
+      ak[i % (PF + 1)] = *(const bf16x8 *)(kt + kofs(i >> 1) + (i & 1) * 32 * RB);
+      av[i % (PF + 1)] = v_operand(vt, i % MT, i / MT);
+    };
+    sc[0] = sc[1] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < PF; ++i) fetch(i);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (i + PF < NS) fetch(i + PF);
+      sc[i & 1] = mfma_32x32x16(ak[i % (PF + 1)], bq[i >> 1], sc[i & 1]);
+      oacc[i % MT] = mfma_32x32x16(av[i % (PF + 1)], pk[i / MT], oacc[i % MT]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Vector step of block j: causal mask, running max with rare rescale,
+  // exps, packing of P and the row sum.
+  auto vector_step = [&](int j) {
     if (a.causal && j >= qb) {
+      // key offset in the block = 32 t + 8 (r / 4) + 4 hh + r % 4; compared
+      // against a per-lane limit so the per-register part stays an immediate
+      const int lim = q_tok - j * kBlock - 4 * hh;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j * kBlock + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key > q_tok) s[t][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * t + 8 * (r >> 2) + (r & 3) > lim) sc[t][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
     mx = xor32_max(mx);
     const float mc = mx * c;
     const bool need = mc > m_run + 8.0f;
@@ -184,85 +238,119 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
       for (int mt = 0; mt < MT; ++mt) oacc[mt] *= alpha;
       m_run = m_new;
     }
-    return m_run == -INFINITY ? 0.f : m_run;
-  };
-  auto softmax_exp = [&](f32x16 (&s)[2], float msub, int e) {
-    const int t = e >> 4, r = e & 15;
-    s[t][r] = fast_exp2(__builtin_fmaf(s[t][r], c, -msub));
-  };
-  // k-step ks of O^T (D x 32 queries) += V^T (D x 64 keys) P^T (64 keys x 32 q)
-  auto pv_ks = [&](f32x16 (&p)[2], const char *vt, int ks) {
-    // The packed words are built here, not read back out of the bf16x8:
-    // extracting 32-bit words of a bit-cast bf16x8 for the dot2 compiled to
-    // four reads of word 0 (hipcc, ROCm 7.2).
-    u32x4 pw;
+    const float msub = m_run == -INFINITY ? 0.f : m_run;
+    // k-step ks of P V takes registers 8 (ks % 2) .. +7 of tile ks / 2.
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 8 * (ks & 1) + 2 * e;
-      const uint32_t w = pack_bf16x2(p[ks >> 1][r], p[ks >> 1][r + 1]);
-      l_part = sum_bf16x2(w, l_part);
-      pw[e] = w;
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 8 * (ks & 1) + 2 * e;
+        const float p0 = fast_exp2(__builtin_fmaf(sc[ks >> 1][r], c, -msub));
+        const float p1 = fast_exp2(__builtin_fmaf(sc[ks >> 1][r + 1], c, -msub));
+        // The packed words are built here, not read back out of a bf16x8:
+        // extracting 32-bit words of a bit-cast bf16x8 for the dot2 compiled
+        // to four reads of word 0 (hipcc, ROCm 7.2).
+        w[e] = pack_bf16x2(p0, p1);
+        l_part = sum_bf16x2(w[e], l_part);
+      }
+      pk[ks] = __builtin_bit_cast(bf16x8, w);
     }
-    const bf16x8 pbk = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) oacc[mt] = mfma_32x32x16(v_operand(vt, mt, ks), pbk, oacc[mt]);
-  };
-  // Softmax + P V of block j (scores in s, V tile in vt): the exps of the
-  // second 32 keys are interleaved with the first half of P V.
-  auto block_work = [&](f32x16 (&s)[2], int j, const char *vt) {
-    const float msub = softmax_pre(s, j);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) softmax_exp(s, msub, e);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      pv_ks(s, vt, ks);
-#pragma unroll
-      for (int e = 16 + ks * 8; e < 24 + ks * 8; ++e) softmax_exp(s, msub, e);
-    }
-    pv_ks(s, vt, 2);
-    pv_ks(s, vt, 3);
   };
 
-  PairBitmap pb;
+  // The first matrix-core step multiplies pk = 0 by slot v1 before any
+  // tile reached it: start it at zero so that product is exactly zero.
+  for (int i = threadIdx.x; i < Lay::TILE / 16; i += kFwdThreads) ((u32x4 *)v1)[i] = u32x4{};
+  RowsBitmap<kFwdQB> pb;
   pb.init(dyn_lds, a.ix.n_kblocks);
-  pb.build(a.ix.row_ptr + (size_t)hidx * (nqb + 1), tile * 2, nqb, a.ix.nnz, a.ix.col_idx,
+  pb.build(a.ix.row_ptr + (size_t)hidx * (nqb + 1), tile * kFwdQB, nqb, a.ix.nnz, a.ix.col_idx,
            a.ix.n_kblocks, kFwdThreads);
-  RowsIter<2> it;
-  it.start(a.ix.n_kblocks, min(tile * 2 + 1, nqb - 1) & ~63);
-  auto listed_by_me = [&](uint32_t mask) { return q_valid && ((mask >> my_r) & 1u); };
+  RowsIter<kFwdQB> it;
+  it.start(a.ix.n_kblocks, min(tile * kFwdQB + kFwdQB - 1, nqb - 1) & ~63);
+  auto advance = [&]() -> WalkPos {
+    WalkPos p;
+    p.valid = it.next(pb);
+    p.j = it.j;
+    p.mask = it.mask;
+    return p;
+  };
+  auto listed = [&](const WalkPos &p) { return p.valid && q_valid && ((p.mask >> my_r) & 1u); };
 
-  // ---- double-buffered walk: block j in buffers [ib] while block j+1 loads
-  // straight into buffers [ib ^ 1] ----
-  bool have = it.next(pb);
-  int j = it.j;
-  bool listed = listed_by_me(it.mask);
-  if (have) {
-    load_tile(kg + (size_t)j * kBlock * D, klds[0], goff_k);
-    load_tile(vg + (size_t)j * kBlock * D, vlds[0], goff_v);
+  // Walk window at even phase 2t: prev = block t-1, cur = t, nxt = t+1.
+  WalkPos prev{false, 0, 0u}, cur = advance(), nxt{false, 0, 0u};
+  if (cur.valid) {
+    nxt = advance();
+    if (grp == 1) load_tile(kg + (size_t)cur.j * kBlock * D, k0, goff_k);
   }
-  int ib = 0;
-  while (have) {
-    // every wave's loads of block j have landed and every wave is done with
-    // the other buffers
+  // Phases 2t and 2t+1 for t = 0 .. n (n = walk length): group A runs the
+  // matrix-core step of walk block t in phase 2t and its vector step in
+  // 2t+1; group B one phase later.  Both groups pass the same n+1 even and
+  // n+1 odd barriers.  With P = t & 1, K of block t lives in slot k<P> and
+  // V of block t in slot v<P>; K(t+1) and V(t) are issued at the start of
+  // phase 2t and waited for at the start of phase 2t+2, where the barrier
+  // also ends every read of the slots they overwrite.  The odd-phase barrier
+  // only keeps the two groups a step apart: it orders no memory, so it does
+  // not wait for tile loads in flight.  Each group has its own loop, unrolled
+  // by two so that every slot is named at compile time, whose body is
+  // "matrix-core step, then vector step": the register allocator then sees
+  // straight-line state updates (a shared loop that switched roles by wave
+  // made it copy the accumulators on every step).
+  auto shift = [&]() {
+    prev = cur;
+    cur = nxt;
+    if (nxt.valid) nxt = advance();
+  };
+  auto even_phase = [&]() {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const bool have_n = it.next(pb);
-    const int jn = it.j;
-    const bool listed_n = listed_by_me(it.mask);
-    if (have_n) {
-      load_tile(kg + (size_t)jn * kBlock * D, klds[ib ^ 1], goff_k);
-      load_tile(vg + (size_t)jn * kBlock * D, vlds[ib ^ 1], goff_v);
-    }
-    if (listed) {
-      f32x16 sc[2] = {f32x16{}, f32x16{}};
+  };
+  // Tile loads of even phase 2t, issued by group B (in its vector step, so
+  // the matrix-core waves never queue behind the address unit).
+  auto issue_loads = [&](auto PAR) {
+    constexpr int P = decltype(PAR)::value;
+    if (nxt.valid) load_tile(kg + (size_t)nxt.j * kBlock * D, P ? k0 : k1, goff_k);
+    if (cur.valid) load_tile(vg + (size_t)cur.j * kBlock * D, P ? v1 : v0, goff_v);
+  };
+  auto matrix_phase = [&](auto PAR) {
+    constexpr int P = decltype(PAR)::value;
+    mfma_step(P ? v0 : v1, P ? k1 : k0);
+  };
+  // vector step of a listed block; otherwise P = 0 for the next P V
+  auto vector_or_zero = [&](const WalkPos &p) {
+    if (listed(p)) {
+      vector_step(p.j);
+    } else {
 #pragma unroll
-      for (int i = 0; i < NS; ++i) s_step(sc, klds[ib], i);
-      block_work(sc, j, vlds[ib]);
+      for (int ks = 0; ks < 4; ++ks) pk[ks] = bf16x8{};
     }
-    have = have_n;
-    j = jn;
-    listed = listed_n;
-    ib ^= 1;
+  };
+  auto step_a = [&](auto PAR, int t) -> bool {
+    if (t > 0) shift();
+    if (!prev.valid && !cur.valid) return false;
+    even_phase();
+    matrix_phase(PAR);
+    __builtin_amdgcn_s_barrier();
+    vector_or_zero(cur);
+    return true;
+  };
+  auto step_b = [&](auto PAR, int t) -> bool {
+    if (t > 0) shift();
+    if (!prev.valid && !cur.valid) return false;
+    even_phase();
+    issue_loads(PAR);
+    vector_or_zero(prev);
+    __builtin_amdgcn_s_barrier();
+    matrix_phase(PAR);
+    return true;
+  };
+  const std::integral_constant<int, 0> even;
+  const std::integral_constant<int, 1> odd;
+  if (grp == 0) {
+    for (int t = 0;; t += 2)
+      if (!step_a(even, t) || !step_a(odd, t + 1)) break;
+  } else {
+    for (int t = 0;; t += 2)
+      if (!step_b(even, t) || !step_b(odd, t + 1)) break;
   }
 
   if (!q_valid) return;
@@ -284,9 +372,9 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
 template <int D>
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
-  const int n_tiles = (a.ix.n_qblocks + 1) / 2;
+  const int n_tiles = (a.ix.n_qblocks + kFwdQB - 1) / kFwdQB;
   const int grid = a.B * a.H * n_tiles;
-  const size_t dyn = PairBitmap::lds_bytes(a.ix.n_kblocks);
+  const size_t dyn = RowsBitmap<kFwdQB>::lds_bytes(a.ix.n_kblocks);
   hipError_t e = hipFuncSetAttribute((const void *)fwd_bf16_kernel<D>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
   if (e != hipSuccess) return e;
@@ -297,7 +385,8 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
 }  // namespace
 
 size_t fwd_bf16_lds_bytes(int d, int n_kblocks) {
-  return 4 * (size_t)kBlock * 2 * d + PairBitmap::lds_bytes(n_kblocks);
+  // two K slots, two V slots, the union bitmaps
+  return 4 * (size_t)kBlock * 2 * d + RowsBitmap<kFwdQB>::lds_bytes(n_kblocks);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s) {
