@@ -168,7 +168,8 @@ attn_status_t attn_sparse_fwd(attn_dtype_t dtype, int32_t B, int32_t H,
  *   dev_index: CSR and CSC (col_ptr/row_idx must be set).
  *   q, k, v, o, dout: [B,H,L,d] bf16 in; lse: [B,H,L] fp32 in (from the
  *   forward); dq, dk, dv: [B,H,L,d] bf16 out.
- *   workspace: attn_workspace_bytes(ATTN_OP_BWD, ...) bytes (device). */
+ *   workspace: attn_workspace_bytes(ATTN_OP_BWD, ...) = 2*B*H*L*4 bytes
+ *   (device; holds D and the base-2 LSE per token). */
 attn_status_t attn_sparse_bwd(attn_dtype_t dtype, int32_t B, int32_t H,
                               int64_t L, int32_t d, float scale,
                               const attn_pattern_t *pattern,

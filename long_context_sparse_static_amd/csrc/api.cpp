@@ -62,7 +62,7 @@ size_t attn_workspace_bytes(int32_t op, attn_dtype_t dtype, int32_t B, int32_t H
   if (B < 1 || H < 1 || L_or_cap < 1 || d < 1) return 0;
   switch (op) {
     case ATTN_OP_FWD: return 0;
-    case ATTN_OP_BWD: return (size_t)B * H * L_or_cap * sizeof(float);
+    case ATTN_OP_BWD: return 2 * (size_t)B * H * L_or_cap * sizeof(float);  // D, LSE2
     case ATTN_OP_SPARSE_DECODE:
     case ATTN_OP_FULL_DECODE: return decode_ws_bytes(B, H, L_or_cap, d);
   }
@@ -126,6 +126,7 @@ attn_status_t attn_sparse_bwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t 
   a.dk = dk;
   a.dv = dv;
   a.delta = (float *)workspace;
+  a.lse2 = (float *)workspace + (size_t)B * H * L;
   a.ix = view_of(dev_index);
   a.B = B;
   a.H = H;

@@ -14,6 +14,18 @@
 // P and dS are recomputed per block pair from the forward's LSE, never stored.
 // Splitting dQ into its own pass keeps every output written by exactly one
 // workgroup: no atomics, bitwise-deterministic results.
+//
+// gfx950 mapping (both MFMA kernels): the streamed tiles (K and V for dQ; Q
+// and dO for dK/dV) go straight from global memory into XOR-swizzled LDS
+// rows (global_load_lds_dwordx4), double-buffered in slots that every load
+// and read names at compile time, so the compiler never waits for a tile
+// load in flight before reading the other slot.  A tile needed both as a row
+// operand and transposed is read transposed through ds_read_b64_tr_b16;
+// nothing is transposed on the way in.  The union of the workgroup's two
+// CSR (CSC) lists is walked from a 64-block boundary, so the workgroups on
+// one XCD stream the same blocks at the same time.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "tiles.h"
@@ -25,6 +37,8 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = kBwdWaves * 64;
 constexpr int kBwdTB = kBwdWaves / 2;  // 64-token blocks per tile (32 rows per wave)
 
+// D = rowsum(dO * O) and the base-2 LSE (lse * log2 e; +inf for an empty
+// row, so that P = exp2(s - lse2) = 0 there) per token.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   constexpr int LPR = D / 8;      // lanes per row
@@ -42,7 +56,11 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
-  if (row < total && c == 0) a.delta[row] = acc;
+  if (row < total && c == 0) {
+    a.delta[row] = acc;
+    const float l = a.lse[row];
+    a.lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
 }
 
 // Reads 16 consecutive fp32 values of a per-token vector laid out in LDS as
@@ -57,30 +75,45 @@ __device__ __forceinline__ void load_rows16(const float *lds, int tile, int hh, 
   }
 }
 
-// ----------------------------------------------------------------------------
-// dQ: one workgroup per 128 query tokens (two query blocks), union of their
-// CSR lists.  Per wave (32 queries, lane = query):
-//   S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - D), dQ^T += K^T dS^T
-// ----------------------------------------------------------------------------
-template <int D>
-struct DqBuf {
-  bf16 k[TileGeom<D>::ROW_ELEMS];
-  bf16 v[TileGeom<D>::ROW_ELEMS];
-  bf16 kt[TileGeom<D>::T_ELEMS];
+// Packs registers 8 half .. 8 half + 7 of a 32x32 accumulator tile (scaled
+// by nothing) into the B operand of a 32x32x16 MFMA whose k index runs over
+// the tile's rows (see pack_acc_operand in tiles.h).
+__device__ __forceinline__ bf16x8 pack_half(const f32x16 &t, int half) {
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(t[8 * half + 2 * e], t[8 * half + 2 * e + 1]);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// One position of a union walk.
+struct BwdPos {
+  bool valid;
+  int j;
+  uint32_t mask;
 };
 
+// ----------------------------------------------------------------------------
+// dQ: one workgroup per 128 query tokens (two query blocks), union of their
+// CSR lists; two workgroups per CU.  Per wave (32 queries, lane = query):
+//   S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - D), dQ^T += K^T dS^T
+// K is read as rows and transposed (kBothRead), V as rows.
+// ----------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
-  using G = TileGeom<D>;
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+  using KT = SwzTile<D, kBothRead>;
+  using VT = SwzTile<D, kRowRead>;
   constexpr int KS = D / 16, MT = D / 32;
-  __shared__ __attribute__((aligned(16))) DqBuf<D> lds[2];
+  __shared__ __attribute__((aligned(1024))) char k0[KT::TILE];
+  __shared__ __attribute__((aligned(1024))) char k1[KT::TILE];
+  __shared__ __attribute__((aligned(1024))) char v0[VT::TILE];
+  __shared__ __attribute__((aligned(1024))) char v1[VT::TILE];
   extern __shared__ uint32_t dyn_lds[];
 
   const int nqb = a.ix.n_qblocks;
   const int n_tiles = (nqb + kBwdTB - 1) / kBwdTB;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = lin / n_tiles;
-  const int tile = n_tiles - 1 - lin % n_tiles;
+  const int tile = n_tiles - 1 - lin % n_tiles;   // heaviest tiles first
   const int hidx = a.ix.n_heads == 1 ? 0 : bh % a.H;
   const size_t base = (size_t)bh * a.L * D;
   const bf16 *kg = (const bf16 *)a.k + base;
@@ -104,92 +137,93 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const float c = a.scale * kLog2e;
   float lse2 = INFINITY, dlt = 0.f;
   if (q_valid) {
-    const float l = a.lse[(size_t)bh * a.L + q_tok];
-    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;  // empty row: P = 0
+    lse2 = a.lse2[(size_t)bh * a.L + q_tok];
     dlt = a.delta[(size_t)bh * a.L + q_tok];
   }
 
-  TReadBases tb;
-  tb.init(n, hh);
+  KT kr;
+  kr.init_reads(lane);
+  VT vr;
+  vr.init_reads(lane);
+  typename KT::template Loader<kBwdWaves> kl;
+  kl.init(wave, lane);
+  typename VT::template Loader<kBwdWaves> vl;
+  vl.init(wave, lane);
 
-  PairBitmap pb;
+  RowsBitmap<kBwdTB> pb;
   pb.init(dyn_lds, a.ix.n_kblocks);
   pb.build(a.ix.row_ptr + (size_t)hidx * (nqb + 1), tile * kBwdTB, nqb, a.ix.nnz, a.ix.col_idx,
            a.ix.n_kblocks, kBwdThreads);
-  PairIter it;
-  it.start(a.ix.n_kblocks);
+  RowsIter<kBwdTB> it;
+  it.start(a.ix.n_kblocks, min(tile * kBwdTB + kBwdTB - 1, nqb - 1) & ~63);
+  auto advance = [&]() __attribute__((always_inline)) -> BwdPos {
+    BwdPos p;
+    p.valid = it.next(pb);
+    p.j = it.j;
+    p.mask = it.mask;
+    return p;
+  };
+  auto listed = [&](const BwdPos &p) __attribute__((always_inline)) { return p.valid && q_valid && ((p.mask >> my_r) & 1u); };
 
   f32x16 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
 
-  RowStage<D, kBwdThreads> sk, sv;
-  TStage<D, kBwdThreads> skt;
-  auto load = [&](int jj) {
-    const size_t off = (size_t)jj * kBlock * D;
-    sk.load(kg + off);
-    sv.load(vg + off);
-    skt.load(kg + off);
-  };
-  auto store = [&](DqBuf<D> &b) {
-    sk.store(b.k);
-    sv.store(b.v);
-    skt.store(b.kt);
-  };
-  bool have = it.next(pb);
-  int j = it.j;
-  bool act = q_valid && (my_r == 0 ? it.in0 : it.in1);
-  if (have) {
-    load(j);
-    store(lds[0]);
-  }
-  bool have_next = have && it.next(pb);
-  if (have_next) load(it.j);
-  int buf = 0;
-  while (have) {
-    __syncthreads();
-    if (act) {
-      const DqBuf<D> &bb = lds[buf];
-      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+  auto block_work = [&](const char *kt, const char *vt, int j) __attribute__((always_inline)) {
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 ak = *(const bf16x8 *)(bb.k + (32 * t + n) * G::ROW + ks * 16 + hh * 8);
-          const bf16x8 av = *(const bf16x8 *)(bb.v + (32 * t + n) * G::ROW + ks * 16 + hh * 8);
-          s[t] = mfma_32x32x16(ak, bq[ks], s[t]);
-          dp[t] = mfma_32x32x16(av, bdo[ks], dp[t]);
-        }
-      const bool diag = a.causal && j >= qb;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(s[t][r], c, -lse2));
-          if (diag) {
-            const int key = j * kBlock + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key > q_tok) p = 0.f;
-          }
-          s[t][r] = p * (dp[t][r] - dlt);  // dS^T
-        }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 bds = pack_acc_operand(s[ks >> 1], ks & 1);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const bf16x8 akt = *(const bf16x8 *)((const char *)bb.kt + tb.at(mt, ks));
-          acc[mt] = mfma_32x32x16(akt, bds, acc[mt]);
-        }
+      for (int t = 0; t < 2; ++t) {
+        s[t] = mfma_32x32x16(kr.row(kt, t, ks), bq[ks], s[t]);
+        dp[t] = mfma_32x32x16(vr.row(vt, t, ks), bdo[ks], dp[t]);
       }
+    const bool diag = a.causal && j >= qb;
+    // key offset in the block = 32 t + 8 (r / 4) + 4 hh + r % 4
+    const int lim = q_tok - j * kBlock - 4 * hh;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(__builtin_fmaf(s[t][r], c, -lse2));
+        if (diag && 32 * t + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
+        s[t][r] = p * (dp[t][r] - dlt);  // dS^T
+      }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 bds = pack_half(s[ks >> 1], ks & 1);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_32x32x16(kr.tr(kt, mt, ks), bds, acc[mt]);
     }
-    if (have_next) store(lds[buf ^ 1]);
-    have = have_next;
-    j = it.j;
-    act = q_valid && (my_r == 0 ? it.in0 : it.in1);
-    have_next = have && it.next(pb);
-    if (have_next) load(it.j);
-    buf ^= 1;
+  };
+
+  BwdPos cur = advance(), nxt{false, 0, 0u};
+  if (cur.valid) {
+    nxt = advance();
+    kl.load(kg + (size_t)cur.j * kBlock * D, k0);
+    vl.load(vg + (size_t)cur.j * kBlock * D, v0);
   }
+  // Block of walk step t lives in slot t & 1; the next block's tiles load into
+  // the other slot while this one is computed.
+  auto step = [&](auto PAR) __attribute__((always_inline)) -> bool {
+    constexpr int P = decltype(PAR)::value;
+    if (!cur.valid) return false;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (nxt.valid) {
+      kl.load(kg + (size_t)nxt.j * kBlock * D, P ? k0 : k1);
+      vl.load(vg + (size_t)nxt.j * kBlock * D, P ? v0 : v1);
+    }
+    if (listed(cur)) block_work(P ? k1 : k0, P ? v1 : v0, cur.j);
+    cur = nxt;
+    if (nxt.valid) nxt = advance();
+    return true;
+  };
+  const std::integral_constant<int, 0> even;
+  const std::integral_constant<int, 1> odd;
+  while (step(even) && step(odd)) {
+  }
+
   if (!q_valid) return;
   bf16 *out = (bf16 *)a.dq + qrow;
 #pragma unroll
@@ -209,22 +243,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 // query block:
 //   S = Q K^T, dP = dO V^T, P = exp2(S c - LSE2), dS = P * (dP - D)
 //   dV^T += dO^T P,  dK^T += Q^T dS
+// Q and dO are read as rows and transposed (kBothRead).
 // ----------------------------------------------------------------------------
 template <int D>
-struct DkvBuf {
-  bf16 q[TileGeom<D>::ROW_ELEMS];
-  bf16 dout[TileGeom<D>::ROW_ELEMS];
-  bf16 qt[TileGeom<D>::T_ELEMS];
-  bf16 dot[TileGeom<D>::T_ELEMS];
-  float lse2[kBlock];
-  float dlt[kBlock];
-};
-
-template <int D>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  using G = TileGeom<D>;
+__global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BwdArgs a) {
+  using QT = SwzTile<D, kBothRead>;
   constexpr int KS = D / 16, MT = D / 32;
-  __shared__ __attribute__((aligned(16))) DkvBuf<D> lds[2];
+  __shared__ __attribute__((aligned(1024))) char q0[QT::TILE];
+  __shared__ __attribute__((aligned(1024))) char q1[QT::TILE];
+  __shared__ __attribute__((aligned(1024))) char o0[QT::TILE];
+  __shared__ __attribute__((aligned(1024))) char o1[QT::TILE];
+  __shared__ __attribute__((aligned(256))) float l0[kBlock];
+  __shared__ __attribute__((aligned(256))) float l1[kBlock];
+  __shared__ __attribute__((aligned(256))) float e0[kBlock];
+  __shared__ __attribute__((aligned(256))) float e1[kBlock];
   extern __shared__ uint32_t dyn_lds[];
 
   const int nkb = a.ix.n_kblocks, nqb = a.ix.n_qblocks;
@@ -254,7 +286,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const size_t base = (size_t)bh * a.L * D;
   const bf16 *qg = (const bf16 *)a.q + base;
   const bf16 *dog = (const bf16 *)a.dout + base;
-  const float *lseg = a.lse + (size_t)bh * a.L;
+  const float *lseg = a.lse2 + (size_t)bh * a.L;
   const float *dltg = a.delta + (size_t)bh * a.L;
 
   const int wave = uniform(threadIdx.x >> 6);
@@ -277,101 +309,99 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) dk[mt] = dv[mt] = f32x16{};
 
-  TReadBases tb;
-  tb.init(n, hh);
+  QT rd;
+  rd.init_reads(lane);
+  typename QT::template Loader<kBwdWaves> ld;
+  ld.init(wave, lane);
+  // the two 64-float per-token vectors of a query block: wave 0 loads LSE2,
+  // wave 1 the D values (4 bytes per lane)
+  auto load_vec = [&](int i, float *lv, float *ev) __attribute__((always_inline)) {
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds((const void *)(lseg + (size_t)i * kBlock + lane),
+                                       (__attribute__((address_space(3))) void *)lv, 4, 0, 0);
+    else if (wave == 1)
+      __builtin_amdgcn_global_load_lds((const void *)(dltg + (size_t)i * kBlock + lane),
+                                       (__attribute__((address_space(3))) void *)ev, 4, 0, 0);
+  };
+  auto load_block = [&](int i, char *qt, char *ot, float *lv, float *ev) __attribute__((always_inline)) {
+    ld.load(qg + (size_t)i * kBlock * D, qt);
+    ld.load(dog + (size_t)i * kBlock * D, ot);
+    load_vec(i, lv, ev);
+  };
 
-  PairBitmap pb;
+  RowsBitmap<kBwdTB> pb;
   pb.init(dyn_lds, nqb);
   pb.build(a.ix.col_ptr + (size_t)hidx * (nkb + 1), tile * kBwdTB, nkb, a.ix.nnz, a.ix.row_idx, nqb,
            kBwdThreads);
-  PairIter it;
-  it.start(nqb);
+  RowsIter<kBwdTB> it;
+  it.start(nqb, (tile * kBwdTB + 63) & ~63);
+  auto advance = [&]() __attribute__((always_inline)) -> BwdPos {
+    BwdPos p;
+    p.valid = it.next(pb);
+    p.j = it.j;
+    p.mask = it.mask;
+    return p;
+  };
+  auto listed = [&](const BwdPos &p) __attribute__((always_inline)) { return p.valid && k_valid && ((p.mask >> my_r) & 1u); };
 
-  RowStage<D, kBwdThreads> sq, sdo;
-  TStage<D, kBwdThreads> sqt, sdot;
-  float lse_st = 0.f, dlt_st = 0.f;
-  auto load = [&](int ii) {
-    const size_t off = (size_t)ii * kBlock * D;
-    sq.load(qg + off);
-    sdo.load(dog + off);
-    sqt.load(qg + off);
-    sdot.load(dog + off);
-    if (threadIdx.x < kBlock) {
-      lse_st = lseg[(size_t)ii * kBlock + threadIdx.x];
-      dlt_st = dltg[(size_t)ii * kBlock + threadIdx.x];
-    }
-  };
-  auto store = [&](DkvBuf<D> &b) {
-    sq.store(b.q);
-    sdo.store(b.dout);
-    sqt.store(b.qt);
-    sdot.store(b.dot);
-    if (threadIdx.x < kBlock) {
-      b.lse2[threadIdx.x] = lse_st == -INFINITY ? INFINITY : lse_st * kLog2e;
-      b.dlt[threadIdx.x] = dlt_st;
-    }
-  };
-  bool have = it.next(pb);
-  int i = it.j;
-  bool act = k_valid && (my_r == 0 ? it.in0 : it.in1);
-  if (have) {
-    load(i);
-    store(lds[0]);
-  }
-  bool have_next = have && it.next(pb);
-  if (have_next) load(it.j);
-  int buf = 0;
-  while (have) {
-    __syncthreads();
-    if (act) {
-      const DkvBuf<D> &bb = lds[buf];
-      const bool diag = a.causal && kb >= i;
+  auto block_work = [&](const char *qt, const char *ot, const float *lv, const float *ev, int i) __attribute__((always_inline)) {
+    const bool diag = a.causal && kb >= i;
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+    for (int m = 0; m < 2; ++m) {
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 aq = *(const bf16x8 *)(bb.q + (32 * m + n) * G::ROW + ks * 16 + hh * 8);
-          const bf16x8 ado = *(const bf16x8 *)(bb.dout + (32 * m + n) * G::ROW + ks * 16 + hh * 8);
-          s = mfma_32x32x16(aq, bk[ks], s);
-          dp = mfma_32x32x16(ado, bv[ks], dp);
-        }
-        float l2[16], dl[16];
-        load_rows16(bb.lse2, m, hh, l2);
-        load_rows16(bb.dlt, m, hh, dl);
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma_32x32x16(rd.row(qt, m, ks), bk[ks], s);
+        dp = mfma_32x32x16(rd.row(ot, m, ks), bv[ks], dp);
+      }
+      float l2[16], dl[16];
+      load_rows16(lv, m, hh, l2);
+      load_rows16(ev, m, hh, dl);
+      // query offset in the block = 32 m + 8 (r / 4) + 4 hh + r % 4; masked
+      // when the key is later
+      const int lim = k_tok - i * kBlock - 32 * m - 4 * hh;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(s[r], c, -l2[r]));
-          if (diag) {
-            const int q_tok = i * kBlock + 32 * m + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (k_tok > q_tok) p = 0.f;
-          }
-          s[r] = p;
-          dp[r] = p * (dp[r] - dl[r]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(__builtin_fmaf(s[r], c, -l2[r]));
+        if (diag && 8 * (r >> 2) + (r & 3) < lim) p = 0.f;
+        s[r] = p;
+        dp[r] = p * (dp[r] - dl[r]);
+      }
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int ks = 2 * m + half;
-          const bf16x8 bp = pack_acc_operand(s, half);
-          const bf16x8 bds = pack_acc_operand(dp, half);
+      for (int half = 0; half < 2; ++half) {
+        const int ks = 2 * m + half;
+        const bf16x8 bp = pack_half(s, half);
+        const bf16x8 bds = pack_half(dp, half);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const bf16x8 adot = *(const bf16x8 *)((const char *)bb.dot + tb.at(mt, ks));
-            const bf16x8 aqt = *(const bf16x8 *)((const char *)bb.qt + tb.at(mt, ks));
-            dv[mt] = mfma_32x32x16(adot, bp, dv[mt]);
-            dk[mt] = mfma_32x32x16(aqt, bds, dk[mt]);
-          }
+        for (int mt = 0; mt < MT; ++mt) {
+          dv[mt] = mfma_32x32x16(rd.tr(ot, mt, ks), bp, dv[mt]);
+          dk[mt] = mfma_32x32x16(rd.tr(qt, mt, ks), bds, dk[mt]);
         }
       }
     }
-    if (have_next) store(lds[buf ^ 1]);
-    have = have_next;
-    i = it.j;
-    act = k_valid && (my_r == 0 ? it.in0 : it.in1);
-    have_next = have && it.next(pb);
-    if (have_next) load(it.j);
-    buf ^= 1;
+  };
+
+  BwdPos cur = advance(), nxt{false, 0, 0u};
+  if (cur.valid) {
+    nxt = advance();
+    load_block(cur.j, q0, o0, l0, e0);
   }
+  auto step = [&](auto PAR) __attribute__((always_inline)) -> bool {
+    constexpr int P = decltype(PAR)::value;
+    if (!cur.valid) return false;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (nxt.valid) load_block(nxt.j, P ? q0 : q1, P ? o0 : o1, P ? l0 : l1, P ? e0 : e1);
+    if (listed(cur)) block_work(P ? q1 : q0, P ? o1 : o0, P ? l1 : l0, P ? e1 : e0, cur.j);
+    cur = nxt;
+    if (nxt.valid) nxt = advance();
+    return true;
+  };
+  const std::integral_constant<int, 0> even;
+  const std::integral_constant<int, 1> odd;
+  while (step(even) && step(odd)) {
+  }
+
   if (!k_valid) return;
   bf16 *dko = (bf16 *)a.dk + krow;
   bf16 *dvo = (bf16 *)a.dv + krow;
@@ -397,8 +427,8 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const int q_tiles = (a.ix.n_qblocks + kBwdTB - 1) / kBwdTB;
   const int k_tiles = (a.ix.n_kblocks + kBwdTB - 1) / kBwdTB;
   const int BH = a.B * a.H;
-  const size_t dyn_k = PairBitmap::lds_bytes(a.ix.n_qblocks);
-  const size_t dyn_q = PairBitmap::lds_bytes(a.ix.n_kblocks);
+  const size_t dyn_k = RowsBitmap<kBwdTB>::lds_bytes(a.ix.n_qblocks);
+  const size_t dyn_q = RowsBitmap<kBwdTB>::lds_bytes(a.ix.n_kblocks);
   hipError_t e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel<D>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_k);
   if (e == hipSuccess)
@@ -414,8 +444,9 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
 }  // namespace
 
 size_t bwd_bf16_lds_bytes(int d, int n_blocks) {
-  const size_t buf = d == 128 ? sizeof(DkvBuf<128>) : sizeof(DkvBuf<64>);
-  return 2 * buf + PairBitmap::lds_bytes(n_blocks);
+  // dK/dV kernel: two Q and two dO slots, four 64-float vectors, bitmaps
+  const size_t tiles = 4 * (size_t)kBlock * 2 * d + 4 * kBlock * sizeof(float);
+  return tiles + RowsBitmap<kBwdTB>::lds_bytes(n_blocks);
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s) {

@@ -180,6 +180,88 @@ __device__ __forceinline__ bf16x8 pack_acc_operand(const f32x16 &t, int half) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// A 64 x D bf16 tile staged straight from global memory into LDS
+// (global_load_lds_dwordx4) as 64 unpadded rows of RB = 2 D bytes whose
+// 16-byte chunks are XOR-swizzled: chunk c of row r sits at chunk
+// c ^ swz(r).  The swizzle is chosen by how the tile is read:
+//   kRowRead  as the row operand of a 32x32x16 MFMA (lane = row, 16 bytes);
+//             16 consecutive rows per phase must hit distinct bank groups.
+//   kTrRead   through ds_read_b64_tr_b16 (lane = dim, 4 tokens); 4
+//             consecutive rows x 64 bytes per phase must cover all banks.
+//   kBothRead both ways; one swizzle satisfies both conditions.
+// Every swizzle acts on the chunk index only, so one per-lane base XOR a
+// constant addresses every k-step (row reads) or dim tile (transposing
+// reads).
+enum SwzKind { kRowRead = 0, kTrRead = 1, kBothRead = 2 };
+
+template <int D, int KIND>
+struct SwzTile {
+  static constexpr int RB = 2 * D;          // bytes per token row
+  static constexpr int CPR = RB / 16;       // 16-byte chunks per row
+  static constexpr int TILE = kBlock * RB;  // bytes per tile
+  static constexpr int RPI = 1024 / RB;     // rows per wave load instruction
+
+  __host__ __device__ static int swz(int r) {
+    if (KIND == kRowRead) return D == 128 ? (r & 15) : ((r >> 1) & 7);
+    if (KIND == kTrRead) return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
+
+  // Loading: wave lw of NL loading waves fills rows lw * 64 / NL .. +64/NL.
+  template <int NL>
+  struct Loader {
+    static constexpr int LPW = kBlock / NL / RPI;  // instructions per wave
+    static_assert(LPW >= 1 && kBlock % (NL * RPI) == 0, "load shape");
+    int goff[LPW];   // per-lane global element offsets
+    int lds_row0;    // first LDS row of this wave's share
+    __device__ __forceinline__ void init(int lw, int lane) {
+      lds_row0 = lw * (kBlock / NL);
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int r = lds_row0 + i * RPI + lane / CPR;
+        goff[i] = r * D + (((lane % CPR) ^ swz(r)) << 3);
+      }
+    }
+    __device__ __forceinline__ void load(const bf16 *g, char *lds) const {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const void *)(g + goff[i]),
+            (__attribute__((address_space(3))) void *)(lds + (lds_row0 + i * RPI) * RB), 16, 0, 0);
+    }
+  };
+
+  // Row operand reads: lane (n, hh) reads row 32 t + n, dims 16 ks + 8 hh .. +7.
+  int kbase;
+  // Transposing reads: lane (hh, gi, s) = 32 hh + 16 gi + s addresses token
+  // 16 ks + 8 h + 4 hh + s / 4 (h = 0, 1) at dims 32 mt + 16 gi + 4 (s % 4);
+  // the two reads give lane d = 32 mt + lane % 32 the 8 tokens that
+  // pack_acc_operand() assigns to logical k = 8 hh .. +7.
+  int trb[2];
+  __device__ __forceinline__ void init_reads(int lane) {
+    const int n = lane & 31, hh = lane >> 5, s = lane & 15, gi = (lane >> 4) & 1;
+    kbase = n * RB + ((hh ^ swz(n)) << 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * h + 4 * hh + (s >> 2);
+      trb[h] = r * RB + (((2 * gi + ((s & 3) >> 1)) ^ swz(r)) << 4) + ((s & 1) << 3);
+    }
+  }
+  __device__ __forceinline__ bf16x8 row(const char *tile, int t, int ks) const {
+    return *(const bf16x8 *)(tile + (kbase ^ (ks << 5)) + t * 32 * RB);
+  }
+  __device__ __forceinline__ bf16x8 tr(const char *tile, int mt, int ks) const {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef short s8 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) s4 lds_s4;
+    const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s4 *)(tile + (trb[0] ^ (mt << 6)) + 16 * ks * RB));
+    const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s4 *)(tile + (trb[1] ^ (mt << 6)) + 16 * ks * RB));
+    return __builtin_bit_cast(bf16x8, (s8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
+
 // Union of R consecutive CSR (or CSC) rows -- the 64-token blocks of one
 // workgroup tile -- held as R LDS bitmaps over block ids plus a summary
 // bitmap of the non-empty words.  Built once per workgroup (atomicOr per list

@@ -132,7 +132,7 @@ def test_layer_map_middle_third():
 
 def test_workspace_sizes():
     assert lcs.attn_workspace_bytes(lcs.ATTN_OP_FWD, lcs.ATTN_BF16, 1, 32, 8192, 128) == 0
-    assert lcs.attn_workspace_bytes(lcs.ATTN_OP_BWD, lcs.ATTN_BF16, 1, 32, 65536, 128) == 32 * 65536 * 4
+    assert lcs.attn_workspace_bytes(lcs.ATTN_OP_BWD, lcs.ATTN_BF16, 1, 32, 65536, 128) == 2 * 32 * 65536 * 4
     ws = lcs.attn_workspace_bytes(lcs.ATTN_OP_FULL_DECODE, lcs.ATTN_BF16, 16, 32, 131073, 128)
     assert ws > 0 and ws % (16 * 32 * 130 * 4) == 0
     ws2 = lcs.attn_workspace_bytes(lcs.ATTN_OP_SPARSE_DECODE, lcs.ATTN_BF16, 16, 32, 4160, 128)
