@@ -344,41 +344,94 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
   };
   auto listed = [&](const BwdPos &p) __attribute__((always_inline)) { return p.valid && k_valid && ((p.mask >> my_r) & 1u); };
 
+  // One query block as one explicit stream of 8 KS MFMAs (one wave per SIMD,
+  // so the wave itself must keep the matrix core fed):
+  //   i in [0, 2KS)      S and dP of query half 0 (row operands)
+  //   i in [2KS, 4KS)    S and dP of half 1, with half 0's softmax-gradient
+  //                      VALU spread between them
+  //   i in [4KS, 6KS)    dV, dK of half 0 (transposed operands), with half
+  //                      1's VALU spread between them
+  //   i in [6KS, 8KS)    dV, dK of half 1
+  // The LDS operand of MFMA i + PF is read while MFMA i runs; a scheduling
+  // barrier after each MFMA keeps this order.
   auto block_work = [&](const char *qt, const char *ot, const float *lv, const float *ev, int i) __attribute__((always_inline)) {
+    constexpr int NM = 8 * KS;       // MFMAs per query block
+    constexpr int PF = 4;            // operand prefetch distance
     const bool diag = a.causal && kb >= i;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma_32x32x16(rd.row(qt, m, ks), bk[ks], s);
-        dp = mfma_32x32x16(rd.row(ot, m, ks), bv[ks], dp);
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    bf16x8 bp[2][2], bds[2][2];
+    float l2[16], dl[16];
+    bf16x8 opnd[PF + 1];
+    // operand of MFMA k
+    auto fetch = [&](int k) __attribute__((always_inline)) {
+      bf16x8 v;
+      if (k < 4 * KS) {                 // scores: k = 4 ks' + 2 m' + which
+        const int m = k / (2 * KS), kk = k % (2 * KS), ks = kk >> 1;
+        v = rd.row((kk & 1) ? ot : qt, m, ks);
+      } else {                          // accumulation: half, mt, which
+        const int kk = k - 4 * KS, m = kk / (4 * MT), r = kk % (4 * MT);
+        const int half = r / (2 * MT), mt = (r % (2 * MT)) >> 1;
+        v = rd.tr((r & 1) ? qt : ot, mt, 2 * m + half);
       }
-      float l2[16], dl[16];
-      load_rows16(lv, m, hh, l2);
-      load_rows16(ev, m, hh, dl);
-      // query offset in the block = 32 m + 8 (r / 4) + 4 hh + r % 4; masked
-      // when the key is later
-      const int lim = k_tok - i * kBlock - 32 * m - 4 * hh;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(__builtin_fmaf(s[r], c, -l2[r]));
-        if (diag && 8 * (r >> 2) + (r & 3) < lim) p = 0.f;
-        s[r] = p;
-        dp[r] = p * (dp[r] - dl[r]);
+      opnd[k % (PF + 1)] = v;
+    };
+    auto mfma_k = [&](int k) __attribute__((always_inline)) {
+      const bf16x8 av = opnd[k % (PF + 1)];
+      if (k < 4 * KS) {
+        const int m = k / (2 * KS), kk = k % (2 * KS), ks = kk >> 1;
+        if (kk & 1) dp[m] = mfma_32x32x16(av, bv[ks], dp[m]);
+        else s[m] = mfma_32x32x16(av, bk[ks], s[m]);
+      } else {
+        const int kk = k - 4 * KS, m = kk / (4 * MT), r = kk % (4 * MT);
+        const int half = r / (2 * MT), mt = (r % (2 * MT)) >> 1;
+        if (r & 1) dk[mt] = mfma_32x32x16(av, bds[m][half], dk[mt]);
+        else dv[mt] = mfma_32x32x16(av, bp[m][half], dv[mt]);
       }
+    };
+    // softmax-gradient VALU of half m, element r (query offset 32 m +
+    // 8 (r / 4) + 4 hh + r % 4; masked when the key is later)
+    auto grad_elem = [&](int m, int r) __attribute__((always_inline)) {
+      if ((r & 3) == 0) {
+        const f32x4 lq = *(const f32x4 *)(lv + 32 * m + 8 * (r >> 2) + 4 * hh);
+        const f32x4 dq = *(const f32x4 *)(ev + 32 * m + 8 * (r >> 2) + 4 * hh);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int ks = 2 * m + half;
-        const bf16x8 bp = pack_half(s, half);
-        const bf16x8 bds = pack_half(dp, half);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          dv[mt] = mfma_32x32x16(rd.tr(ot, mt, ks), bp, dv[mt]);
-          dk[mt] = mfma_32x32x16(rd.tr(qt, mt, ks), bds, dk[mt]);
+        for (int e = 0; e < 4; ++e) {
+          l2[r + e] = lq[e];
+          dl[r + e] = dq[e];
         }
       }
-    }
+      const int lim = k_tok - i * kBlock - 32 * m - 4 * hh;
+      float p = fast_exp2(__builtin_fmaf(s[m][r], c, -l2[r]));
+      if (diag && 8 * (r >> 2) + (r & 3) < lim) p = 0.f;
+      s[m][r] = p;
+      dp[m][r] = p * (dp[m][r] - dl[r]);
+      if (r == 7 || r == 15) {
+        const int half = r >> 3;
+        bp[m][half] = pack_half(s[m], half);
+        bds[m][half] = pack_half(dp[m], half);
+      }
+    };
+    auto stage = [&](auto STAGE) __attribute__((always_inline)) {
+      constexpr int st = decltype(STAGE)::value;
+#pragma unroll
+      for (int kk = 0; kk < 2 * KS; ++kk) {
+        const int k = st * 2 * KS + kk;
+        if (k + PF < NM) fetch(k + PF);
+        mfma_k(k);
+        // 16 VALU elements of a half spread over the 2 KS MFMAs of a stage
+        if constexpr (st == 1 || st == 2) {
+#pragma unroll
+          for (int r = kk * 16 / (2 * KS); r < (kk + 1) * 16 / (2 * KS); ++r) grad_elem(st - 1, r);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+#pragma unroll
+    for (int k = 0; k < PF; ++k) fetch(k);
+    stage(std::integral_constant<int, 0>{});
+    stage(std::integral_constant<int, 1>{});
+    stage(std::integral_constant<int, 2>{});
+    stage(std::integral_constant<int, 3>{});
   };
 
   BwdPos cur = advance(), nxt{false, 0, 0u};
