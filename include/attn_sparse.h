@@ -122,6 +122,20 @@ attn_status_t attn_index_build(const attn_pattern_t *pattern, int32_t n_heads,
                                int64_t L, int32_t *row_ptr, int32_t *col_idx,
                                int32_t *col_ptr, int32_t *row_idx);
 
+/* Per-head mix of patterns in one index (for instance full-attention
+ * retrieval heads beside sink + window streaming heads, the head split of
+ * DuoAttention on the Hugging Face paper-search page "long-context decoding
+ * latency"): head h's rows follow patterns[h] with stride phase h.
+ * patterns: n_heads host structs that share `block` and `causal` (a launch
+ * applies both to every head); otherwise ATTN_ERR_INVALID_ARG.  Buffers and
+ * the NULL-CSC rule as for attn_index_build.  Pass any of the patterns to the
+ * device ops: they read only its block and causal fields. */
+attn_status_t attn_index_nnz_mixed(const attn_pattern_t *patterns, int32_t n_heads,
+                                   int64_t L, int64_t *nnz_out);
+attn_status_t attn_index_build_mixed(const attn_pattern_t *patterns, int32_t n_heads,
+                                     int64_t L, int32_t *row_ptr, int32_t *col_idx,
+                                     int32_t *col_ptr, int32_t *row_idx);
+
 /* Checks a HOST copy of an index: monotone pointers within [0, nnz], block
  * ids in range and strictly ascending, and (when present) that the CSC is
  * exactly the transpose of the CSR.  Returns ATTN_ERR_BAD_INDEX otherwise. */

@@ -49,7 +49,8 @@ BLOCK = 64
 
 # Every symbol include/attn_sparse.h declares.
 EXPORTED = (
-    "attn_status_str", "attn_index_nnz", "attn_index_build", "attn_index_validate",
+    "attn_status_str", "attn_index_nnz", "attn_index_build", "attn_index_nnz_mixed",
+    "attn_index_build_mixed", "attn_index_validate",
     "attn_layer_map", "attn_workspace_bytes", "attn_sparse_fwd", "attn_sparse_bwd",
     "attn_sparse_decode", "attn_full_decode", "attn_ring_fill",
 )
@@ -95,6 +96,10 @@ def lib():
         L.attn_index_nnz.argtypes = [P(attn_pattern_t), i32, i64, P(i64)]
         L.attn_index_build.restype = i32
         L.attn_index_build.argtypes = [P(attn_pattern_t), i32, i64, vp, vp, vp, vp]
+        L.attn_index_nnz_mixed.restype = i32
+        L.attn_index_nnz_mixed.argtypes = [P(attn_pattern_t), i32, i64, P(i64)]
+        L.attn_index_build_mixed.restype = i32
+        L.attn_index_build_mixed.argtypes = [P(attn_pattern_t), i32, i64, vp, vp, vp, vp]
         L.attn_index_validate.restype = i32
         L.attn_index_validate.argtypes = [P(attn_index_t)]
         L.attn_layer_map.restype = i32
@@ -256,6 +261,42 @@ class DeviceIndex:
 def build_device_index(pattern: Pattern, H: int, L: int, device, with_csc: bool = True) -> DeviceIndex:
     n_heads = H if pattern.head_dependent else 1
     return DeviceIndex(attn_index_build(pattern, n_heads, L, with_csc), device)
+
+
+def _pattern_array(patterns):
+    arr = (attn_pattern_t * len(patterns))()
+    for h, pat in enumerate(patterns):
+        arr[h] = pat.c_struct()
+    return arr
+
+
+def attn_index_nnz_mixed(patterns, L: int) -> int:
+    """Entries of a per-head mix of patterns (head h follows patterns[h])."""
+    out = ctypes.c_int64(0)
+    arr = _pattern_array(patterns)
+    _check(lib().attn_index_nnz_mixed(arr, len(patterns), L, ctypes.byref(out)),
+           "attn_index_nnz_mixed")
+    return out.value
+
+
+def attn_index_build_mixed(patterns, L: int, with_csc: bool = True) -> HostIndex:
+    """CSR (and CSC) of a per-head mix of patterns, built on the host."""
+    H = len(patterns)
+    nnz = attn_index_nnz_mixed(patterns, L)
+    nb = L // patterns[0].block
+    row_ptr = np.zeros(H * (nb + 1), dtype=np.int32)
+    col_idx = np.zeros(max(nnz, 1), dtype=np.int32)[:nnz]
+    col_ptr = np.zeros(H * (nb + 1), dtype=np.int32) if with_csc else None
+    row_idx = np.zeros(max(nnz, 1), dtype=np.int32)[:nnz] if with_csc else None
+    arr = _pattern_array(patterns)
+    ptr = lambda a: None if a is None else a.ctypes.data
+    _check(lib().attn_index_build_mixed(arr, H, L, ptr(row_ptr), ptr(col_idx), ptr(col_ptr),
+                                        ptr(row_idx)), "attn_index_build_mixed")
+    return HostIndex(H, nb, nb, row_ptr, col_idx, col_ptr, row_idx)
+
+
+def build_device_index_mixed(patterns, L: int, device, with_csc: bool = True) -> DeviceIndex:
+    return DeviceIndex(attn_index_build_mixed(patterns, L, with_csc), device)
 
 
 # ----------------------------------------------------------------------------

@@ -72,31 +72,31 @@ const char *attn_status_str(attn_status_t s) {
   return "unknown status";
 }
 
-attn_status_t attn_index_nnz(const attn_pattern_t *p, int32_t n_heads, int64_t L,
-                             int64_t *nnz_out) {
-  if (!nnz_out || n_heads < 1 || !pattern_ok(p, L)) return ATTN_ERR_INVALID_ARG;
-  const int64_t nb = L / p->block;
+}  // extern "C"
+
+namespace {
+
+// Shared by the single-pattern and per-head builders: head h's rows follow
+// pattern_of(h).
+template <class PatternOf>
+attn_status_t count_nnz(PatternOf &&pattern_of, int32_t n_heads, int64_t nb, bool same_rows,
+                        int64_t *nnz_out) {
   int64_t total = 0;
-  const int32_t distinct = p->kind == ATTN_BLOCKSPARSE ? n_heads : 1;
+  const int32_t distinct = same_rows ? 1 : n_heads;
   for (int32_t h = 0; h < distinct; ++h)
-    for (int64_t i = 0; i < nb; ++i) total += emit_row(p, i, h, [](int64_t) {});
-  if (distinct == 1) total *= n_heads;
+    for (int64_t i = 0; i < nb; ++i) total += emit_row(pattern_of(h), i, h, [](int64_t) {});
+  if (same_rows) total *= n_heads;
   if (total > INT32_MAX) return ATTN_ERR_UNSUPPORTED;  // int32 offsets
   *nnz_out = total;
   return ATTN_OK;
 }
 
-attn_status_t attn_index_build(const attn_pattern_t *p, int32_t n_heads, int64_t L,
-                               int32_t *row_ptr, int32_t *col_idx, int32_t *col_ptr,
-                               int32_t *row_idx) {
-  int64_t nnz = 0;
-  attn_status_t st = attn_index_nnz(p, n_heads, L, &nnz);
-  if (st != ATTN_OK) return st;
-  if (!row_ptr || !col_idx) return ATTN_ERR_INVALID_ARG;
-  if ((col_ptr == nullptr) != (row_idx == nullptr)) return ATTN_ERR_INVALID_ARG;
-  const int64_t nb = L / p->block;
+template <class PatternOf>
+void build_lists(PatternOf &&pattern_of, int32_t n_heads, int64_t nb, int32_t *row_ptr,
+                 int32_t *col_idx, int32_t *col_ptr, int32_t *row_idx) {
   int64_t off = 0;
   for (int32_t h = 0; h < n_heads; ++h) {
+    const attn_pattern_t *p = pattern_of(h);
     const int64_t head_start = off;
     int32_t *rp = row_ptr + (int64_t)h * (nb + 1);
     for (int64_t i = 0; i < nb; ++i) {
@@ -120,6 +120,61 @@ attn_status_t attn_index_build(const attn_pattern_t *p, int32_t n_heads, int64_t
         for (int64_t e = rp[i]; e < rp[i + 1]; ++e) row_idx[count[col_idx[e]]++] = (int32_t)i;
     }
   }
+}
+
+// Per-head patterns must agree on block size and causality (one kernel
+// launch applies both to every head).
+bool mixed_ok(const attn_pattern_t *patterns, int32_t n_heads, int64_t L) {
+  if (!patterns || n_heads < 1) return false;
+  for (int32_t h = 0; h < n_heads; ++h) {
+    if (!pattern_ok(&patterns[h], L)) return false;
+    if (patterns[h].block != patterns[0].block) return false;
+    if ((patterns[h].causal != 0) != (patterns[0].causal != 0)) return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_index_nnz(const attn_pattern_t *p, int32_t n_heads, int64_t L,
+                             int64_t *nnz_out) {
+  if (!nnz_out || n_heads < 1 || !pattern_ok(p, L)) return ATTN_ERR_INVALID_ARG;
+  return count_nnz([p](int32_t) { return p; }, n_heads, L / p->block,
+                   p->kind != ATTN_BLOCKSPARSE, nnz_out);
+}
+
+attn_status_t attn_index_build(const attn_pattern_t *p, int32_t n_heads, int64_t L,
+                               int32_t *row_ptr, int32_t *col_idx, int32_t *col_ptr,
+                               int32_t *row_idx) {
+  int64_t nnz = 0;
+  attn_status_t st = attn_index_nnz(p, n_heads, L, &nnz);
+  if (st != ATTN_OK) return st;
+  if (!row_ptr || !col_idx) return ATTN_ERR_INVALID_ARG;
+  if ((col_ptr == nullptr) != (row_idx == nullptr)) return ATTN_ERR_INVALID_ARG;
+  build_lists([p](int32_t) { return p; }, n_heads, L / p->block, row_ptr, col_idx, col_ptr,
+              row_idx);
+  return ATTN_OK;
+}
+
+attn_status_t attn_index_nnz_mixed(const attn_pattern_t *patterns, int32_t n_heads, int64_t L,
+                                   int64_t *nnz_out) {
+  if (!nnz_out || !mixed_ok(patterns, n_heads, L)) return ATTN_ERR_INVALID_ARG;
+  return count_nnz([patterns](int32_t h) { return &patterns[h]; }, n_heads,
+                   L / patterns[0].block, false, nnz_out);
+}
+
+attn_status_t attn_index_build_mixed(const attn_pattern_t *patterns, int32_t n_heads, int64_t L,
+                                     int32_t *row_ptr, int32_t *col_idx, int32_t *col_ptr,
+                                     int32_t *row_idx) {
+  int64_t nnz = 0;
+  attn_status_t st = attn_index_nnz_mixed(patterns, n_heads, L, &nnz);
+  if (st != ATTN_OK) return st;
+  if (!row_ptr || !col_idx) return ATTN_ERR_INVALID_ARG;
+  if ((col_ptr == nullptr) != (row_idx == nullptr)) return ATTN_ERR_INVALID_ARG;
+  build_lists([patterns](int32_t h) { return &patterns[h]; }, n_heads, L / patterns[0].block,
+              row_ptr, col_idx, col_ptr, row_idx);
   return ATTN_OK;
 }
 

@@ -193,7 +193,16 @@ def attention_backward(q, k, v, do, mask, scale, row_chunk=1024):
 # ----------------------------------------------------------------------------
 # Batched prefill wrappers over [B,H,L,d]
 # ----------------------------------------------------------------------------
+def head_pattern(pattern, head):
+    """The pattern dict head ``head`` follows: ``pattern`` itself, or its
+    entry ``head`` when it is a per-head list (a mix such as retrieval heads
+    with full attention beside sink + window streaming heads: DuoAttention,
+    Hugging Face paper-search page "long-context decoding latency")."""
+    return pattern[head] if isinstance(pattern, (list, tuple)) else pattern
+
+
 def pattern_lists_for_head(pattern, n_qblocks, head):
+    pattern = head_pattern(pattern, head)
     return block_lists(pattern["kind"], n_qblocks,
                        sink_blocks=pattern.get("sink_blocks", 0),
                        local_blocks=pattern.get("local_blocks", 0),
@@ -201,23 +210,23 @@ def pattern_lists_for_head(pattern, n_qblocks, head):
 
 
 def sparse_forward(q, k, v, pattern, scale=None, heads=None, rows=None):
-    """Forward over [B,H,L,d] arrays for the given pattern dict.
+    """Forward over [B,H,L,d] arrays for the given pattern dict (or list of
+    dicts, one per head).
 
     ``heads``: optional list of head indices to compute (others left NaN).
     ``rows``:  optional array of query-token indices to compute (others NaN).
     Returns (o [B,H,L,d], lse [B,H,L]) in float64.
     """
     B, H, L, d = q.shape
-    block = pattern["block"]
-    nb = L // block
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = np.full((B, H, L, d), np.nan)
     lse = np.full((B, H, L), np.nan)
     heads = range(H) if heads is None else heads
     for h in heads:
-        lists = pattern_lists_for_head(pattern, nb, h)
-        causal = pattern.get("causal", True)
+        block = head_pattern(pattern, h)["block"]
+        lists = pattern_lists_for_head(pattern, L // block, h)
+        causal = head_pattern(pattern, h).get("causal", True)
         if rows is None:
             mask = dense_token_mask(lists, block, L, L, causal)
             for b in range(B):
@@ -235,8 +244,6 @@ def sparse_forward(q, k, v, pattern, scale=None, heads=None, rows=None):
 def sparse_backward(q, k, v, do, pattern, scale=None, heads=None):
     """Backward over [B,H,L,d]; returns dq, dk, dv, o, lse (float64)."""
     B, H, L, d = q.shape
-    block = pattern["block"]
-    nb = L // block
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     shp = (B, H, L, d)
@@ -244,8 +251,9 @@ def sparse_backward(q, k, v, do, pattern, scale=None, heads=None):
     lse = np.full((B, H, L), np.nan)
     heads = range(H) if heads is None else heads
     for h in heads:
-        lists = pattern_lists_for_head(pattern, nb, h)
-        mask = dense_token_mask(lists, block, L, L, pattern.get("causal", True))
+        block = head_pattern(pattern, h)["block"]
+        lists = pattern_lists_for_head(pattern, L // block, h)
+        mask = dense_token_mask(lists, block, L, L, head_pattern(pattern, h).get("causal", True))
         for b in range(B):
             dq[b, h], dk[b, h], dv[b, h], o[b, h], lse[b, h] = attention_backward(
                 q[b, h], k[b, h], v[b, h], do[b, h], mask, scale)

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     assert sorted(lcs.EXPORTED) == names
     L = lcs.lib()
     for n in names:
@@ -73,6 +73,44 @@ def test_index_matches_oracle_bit_exact(name):
         got_cols = np.split(ix.row_idx[ix.col_ptr[cbase]:ix.col_ptr[cbase + nb]],
                             ix.col_ptr[cbase + 1:cbase + nb] - ix.col_ptr[cbase])
         assert [c.tolist() for c in got_cols] == cols, (name, h)
+
+
+MIXED = [  # (pattern, oracle kind, kwargs) per head: retrieval / streaming head mix
+    (lcs.full_pattern(), FULL, dict()),
+    (lcs.attnsink_pattern(1, 4), ATTNSINK, dict(sink_blocks=1, local_blocks=4)),
+    (lcs.blocksparse_pattern(1, 3, 4), BLOCKSPARSE, dict(sink_blocks=1, local_blocks=3, stride=4)),
+    (lcs.attnsink_pattern(2, 3), ATTNSINK, dict(sink_blocks=2, local_blocks=3)),
+    (lcs.full_pattern(), FULL, dict()),
+    (lcs.blocksparse_pattern(2, 5, 3), BLOCKSPARSE, dict(sink_blocks=2, local_blocks=5, stride=3)),
+]
+
+
+def test_mixed_index_matches_oracle_bit_exact():
+    """Per-head pattern mix: head h's rows and columns are those of its own
+    pattern (with stride phase h), bit-exact against the oracle's scan."""
+    L = 64 * 37
+    nb = L // 64
+    pats = [m[0] for m in MIXED]
+    ix = lcs.attn_index_build_mixed(pats, L, with_csc=True)
+    lcs.attn_index_validate(ix)
+    total = 0
+    for h, (_, kind, kw) in enumerate(MIXED):
+        want = block_lists(kind, nb, head=h, **kw)
+        total += sum(len(r) for r in want)
+        assert [ix.row(h, i) for i in range(nb)] == want, h
+        assert [ix.col(h, j) for j in range(nb)] == transpose_lists(want, nb), h
+    assert lcs.attn_index_nnz_mixed(pats, L) == total == ix.nnz
+
+
+def test_mixed_index_rejects_inconsistent_heads():
+    L = 64 * 8
+    non_causal = lcs.Pattern(lcs.ATTN_ATTNSINK, 1, 2, causal=False)
+    with pytest.raises(lcs.AttnError):
+        lcs.attn_index_nnz_mixed([lcs.full_pattern(), non_causal], L)     # causal differs
+    with pytest.raises(lcs.AttnError):
+        lcs.attn_index_nnz_mixed([lcs.full_pattern(), lcs.Pattern(7)], L)  # unknown kind
+    with pytest.raises(lcs.AttnError):
+        lcs.attn_index_nnz_mixed([lcs.full_pattern()], 1000)              # L % 64
 
 
 def test_index_nnz_closed_forms():

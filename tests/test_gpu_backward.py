@@ -76,3 +76,21 @@ def test_backward_64k_sampled_blocks():
             g = {"dq": dq, "dk": dk, "dv": dv}[name][0, h, 64 * blk:64 * (blk + 1)]
             mx, mean = assert_bf16_close(as_f64(g), w, f"{name} head {h} block {blk}")
             print(name, h, blk, mx, mean)
+
+
+def test_bf16_backward_mixed_heads_full_oracle():
+    """Per-head pattern mix (full, AttnSink and BlockSparse heads) through one
+    index (CSR + CSC) and one backward launch."""
+    need_gpu()
+    pats = [lcs.full_pattern(), lcs.attnsink_pattern(1, 3), lcs.blocksparse_pattern(1, 2, 3),
+            lcs.attnsink_pattern(2, 2)]
+    H, L, d = len(pats), 64 * 11, 128
+    q, k, v, do = _inputs((1, H, L, d), 460)
+    ix = lcs.build_device_index_mixed(pats, L, q.device, with_csc=True)
+    o, lse = lcs.attn_sparse_fwd(q, k, v, ix, pats[0])
+    dq, dk, dv = lcs.attn_sparse_bwd(q, k, v, o, lse, do, ix, pats[0])
+    torch.cuda.synchronize()
+    wq, wk, wv, _, _ = sparse_backward(as_f64(q), as_f64(k), as_f64(v), as_f64(do),
+                                       [oracle_pattern(p) for p in pats])
+    for name, g, w in (("dq", dq, wq), ("dk", dk, wk), ("dv", dv, wv)):
+        print("mixed", name, assert_bf16_close(as_f64(g), w, name))

@@ -180,3 +180,43 @@ def test_bf16_full_size_sampled(name):
         mx, mean = assert_bf16_close(as_f64(o[0, h, idx]), wo, f"{name} O head {h}")
         assert_bf16_close(as_f64(lse[0, h, idx]), wlse, f"{name} LSE head {h}")
         print(name, h, mx, mean)
+
+
+# ----------------------------------------------------------------------------
+# Per-head pattern mix (retrieval heads with full attention beside sink +
+# window streaming heads) through one index and one launch.
+# ----------------------------------------------------------------------------
+MIXED_HEADS = [lcs.full_pattern(), lcs.attnsink_pattern(1, 4), lcs.blocksparse_pattern(1, 3, 4),
+               lcs.attnsink_pattern(2, 3), lcs.full_pattern(), lcs.blocksparse_pattern(2, 5, 3)]
+
+
+def test_bf16_mixed_heads_full_oracle():
+    need_gpu()
+    H, L, d = len(MIXED_HEADS), 64 * 19, 128
+    q, k, v = _inputs((1, H, L, d), 130, torch.bfloat16)
+    ix = lcs.build_device_index_mixed(MIXED_HEADS, L, q.device, with_csc=False)
+    o, lse = lcs.attn_sparse_fwd(q, k, v, ix, MIXED_HEADS[0])
+    torch.cuda.synchronize()
+    pats = [oracle_pattern(p) for p in MIXED_HEADS]
+    wo, wl = sparse_forward(as_f64(q), as_f64(k), as_f64(v), pats)
+    print("mixed O", assert_bf16_close(as_f64(o), wo, "O"))
+    print("mixed LSE", assert_bf16_close(as_f64(lse), wl, "LSE"))
+
+
+def test_bf16_mixed_heads_32k_sampled():
+    """32 heads at 32K tokens, every fourth head full attention and the rest
+    AttnSink (sink 64, window 4096), as one launch; sampled rows per head."""
+    need_gpu()
+    H, L, d = 32, 32768, 128
+    pats = [lcs.full_pattern() if h % 4 == 0 else lcs.attnsink_pattern(1, 64) for h in range(H)]
+    q, k, v = _inputs((1, H, L, d), 131, torch.bfloat16, big=True)
+    ix = lcs.build_device_index_mixed(pats, L, q.device, with_csc=False)
+    o, lse = lcs.attn_sparse_fwd(q, k, v, ix, pats[1])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    for h in (0, 1, 4, 30):
+        rows = np.unique(np.concatenate([[0, 63, 64, L - 1], rng.integers(0, L, 24)]))
+        wo, wlse = sample_rows_forward(q, k, v, pats[h], h, 0, rows)
+        idx = torch.as_tensor(rows, device=q.device)
+        assert_bf16_close(as_f64(o[0, h, idx]), wo, f"mixed O head {h}")
+        assert_bf16_close(as_f64(lse[0, h, idx]), wlse, f"mixed LSE head {h}")
