@@ -64,7 +64,8 @@ typedef enum {
   ATTN_OP_FWD = 0,
   ATTN_OP_BWD = 1,
   ATTN_OP_SPARSE_DECODE = 2,
-  ATTN_OP_FULL_DECODE = 3
+  ATTN_OP_FULL_DECODE = 3,
+  ATTN_OP_BLOCKSPARSE_DECODE = 4
 } attn_op_t;
 
 /* Static pattern description (host struct, passed by pointer).
@@ -229,6 +230,52 @@ attn_status_t attn_full_decode(attn_dtype_t dtype, int32_t B, int32_t H,
                                const void *v_new, void *k_cache, void *v_cache,
                                void *o, float *lse, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/* Decode one new token per sequence in a BlockSparse layer against its
+ * compacted cache (the block-wise sparse layers of LongGen: mlsanity index
+ * page, "Abstract (arXiv)"; their reduced KV cache: atlas.scime.ai summary,
+ * "Key results").  The token at position t (block i = t / 64) reads exactly
+ * the keys of its row of the prefill mask: sink blocks j < sink_blocks, the
+ * local blocks i-local_blocks+1 .. i (keys <= t inside block i) and the
+ * strided blocks sink_blocks <= j < i-local_blocks+1 with
+ * (j + h) % stride == 0, h = head index.
+ *   pattern: kind ATTN_BLOCKSPARSE, block 64 (sink_blocks s, local_blocks w,
+ *   stride st).  strided_blocks C: capacity of the strided area.
+ *   Cache layout: k_cache, v_cache [B,H,S,d], S = 64 (s + w + C):
+ *     slots [0, 64 s)            sink blocks;
+ *     slots [64 s, 64 (s + w))   ring of the w most recent blocks, block j at
+ *                                ring block j mod w;
+ *     slots [64 (s + w), S)      strided blocks that left the window, in
+ *                                ascending order.
+ *   When t starts a block (t % 64 == 0) and block j = t/64 - w is a strided
+ *   block, it is first copied from the ring to the strided area; then
+ *   k_new / v_new ([B,H,1,d]) are written to the new token's slot and q
+ *   ([B,H,1,d]) attends.  dev_pos: [B] int64 device.  A position whose
+ *   strided blocks exceed C (or t < 0) gives lse = NaN and touches nothing.
+ *   o: [B,H,1,d] bf16, lse: [B,H] fp32.  workspace:
+ *   attn_workspace_bytes(ATTN_OP_BLOCKSPARSE_DECODE, ..., S, d).
+ *   dtype: ATTN_BF16, d in {64, 128}. */
+attn_status_t attn_blocksparse_decode(attn_dtype_t dtype, int32_t B, int32_t H,
+                                      int32_t d, float scale,
+                                      const attn_pattern_t *pattern,
+                                      int32_t strided_blocks,
+                                      const int64_t *dev_pos, const void *q,
+                                      const void *k_new, const void *v_new,
+                                      void *k_cache, void *v_cache, void *o,
+                                      float *lse, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/* Fills a BlockSparse compacted cache (layout as in attn_blocksparse_decode)
+ * from prefill K/V [B,H,src_len,d]: the state decode would have reached
+ * after appending tokens 0 .. len_b-1 of sequence b (len_b = dev_len[b],
+ * int64 device, clamped to src_len).  Slots that hold no token yet are left
+ * untouched.  dtype: ATTN_BF16. */
+attn_status_t attn_blocksparse_cache_fill(attn_dtype_t dtype, int32_t B, int32_t H,
+                                          int32_t d, const attn_pattern_t *pattern,
+                                          int32_t strided_blocks,
+                                          const int64_t *dev_len, const void *k_src,
+                                          const void *v_src, int64_t src_len,
+                                          void *k_cache, void *v_cache, void *stream);
 
 /* Fills a sparse layer's ring cache from prefill K/V (the reduced cache of
  * the LongGen sparse layers: atlas.scime.ai summary, "Key results").

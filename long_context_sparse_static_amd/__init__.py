@@ -44,6 +44,7 @@ ATTN_OP_FWD = 0
 ATTN_OP_BWD = 1
 ATTN_OP_SPARSE_DECODE = 2
 ATTN_OP_FULL_DECODE = 3
+ATTN_OP_BLOCKSPARSE_DECODE = 4
 
 BLOCK = 64
 
@@ -52,7 +53,8 @@ EXPORTED = (
     "attn_status_str", "attn_index_nnz", "attn_index_build", "attn_index_nnz_mixed",
     "attn_index_build_mixed", "attn_index_validate",
     "attn_layer_map", "attn_workspace_bytes", "attn_sparse_fwd", "attn_sparse_bwd",
-    "attn_sparse_decode", "attn_full_decode", "attn_ring_fill",
+    "attn_sparse_decode", "attn_full_decode", "attn_ring_fill", "attn_blocksparse_decode",
+    "attn_blocksparse_cache_fill",
 )
 
 
@@ -122,6 +124,12 @@ def lib():
         L.attn_ring_fill.restype = i32
         L.attn_ring_fill.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp, vp,
                                      vp]
+        L.attn_blocksparse_decode.restype = i32
+        L.attn_blocksparse_decode.argtypes = [i32, i32, i32, i32, f32, P(attn_pattern_t), i32, vp,
+                                              vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_blocksparse_cache_fill.restype = i32
+        L.attn_blocksparse_cache_fill.argtypes = [i32, i32, i32, i32, P(attn_pattern_t), i32, vp,
+                                                  vp, vp, i64, vp, vp, vp]
         _lib_handle = L
     return _lib_handle
 
@@ -453,3 +461,59 @@ def attn_ring_fill(k_src, v_src, lengths, k_cache, v_cache, sink_tokens: int, wi
     vc = _dev(v_cache, "v_cache", (B, H, S, d), torch.bfloat16, k_src.device)
     _check(lib().attn_ring_fill(ATTN_BF16, B, H, d, sink_tokens, window_tokens, lp, ks, vs,
                                 src_len, kc, vc, _stream()), "attn_ring_fill")
+
+
+def blocksparse_cache_slots(pattern: Pattern, strided_blocks: int) -> int:
+    """Slots per (b, h) of a BlockSparse compacted cache."""
+    return pattern.block * (pattern.sink_blocks + pattern.local_blocks + strided_blocks)
+
+
+def blocksparse_strided_capacity(pattern: Pattern, max_tokens: int) -> int:
+    """Strided-area blocks that positions below ``max_tokens`` can need (the
+    largest count over the heads' stride phases)."""
+    nb = (max_tokens + pattern.block - 1) // pattern.block
+    first = max(0, nb - pattern.local_blocks)       # first window block of the last position
+    span = max(0, first - pattern.sink_blocks)
+    return (span + pattern.stride - 1) // pattern.stride
+
+
+def attn_blocksparse_decode(q, k_new, v_new, k_cache, v_cache, pos, pattern: Pattern,
+                            strided_blocks: int, scale=None, o=None, lse=None, workspace=None):
+    """Decode one token per sequence of a BlockSparse layer against its
+    compacted cache [B,H,64*(sink+local+strided_blocks),d]."""
+    torch = _torch()
+    B, H, d, o, lse, ptrs = _decode_io(q, k_new, v_new, o, lse)
+    S = blocksparse_cache_slots(pattern, strided_blocks)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kc = _dev(k_cache, "k_cache", (B, H, S, d), q.dtype, q.device)
+    vc = _dev(v_cache, "v_cache", (B, H, S, d), q.dtype, q.device)
+    pp = _dev(pos, "pos", (B,), torch.int64, q.device)
+    need = attn_workspace_bytes(ATTN_OP_BLOCKSPARSE_DECODE, _dtype_code(q), B, H, S, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    wp = _dev(workspace, "workspace", device=q.device)
+    op = _dev(o, "o", q.shape, q.dtype, q.device)
+    lp = _dev(lse, "lse", (B, H), torch.float32, q.device)
+    pat = pattern.c_struct()
+    _check(lib().attn_blocksparse_decode(_dtype_code(q), B, H, d, scale, ctypes.byref(pat),
+                                         strided_blocks, pp, *ptrs, kc, vc, op, lp, wp,
+                                         workspace.numel() * workspace.element_size(), _stream()),
+           "attn_blocksparse_decode")
+    return o, lse
+
+
+def attn_blocksparse_cache_fill(k_src, v_src, lengths, k_cache, v_cache, pattern: Pattern,
+                                strided_blocks: int):
+    """Fills a BlockSparse compacted cache from prefill K/V."""
+    torch = _torch()
+    B, H, src_len, d = k_src.shape
+    S = blocksparse_cache_slots(pattern, strided_blocks)
+    ks = _dev(k_src, "k_src", dtype=torch.bfloat16)
+    vs = _dev(v_src, "v_src", k_src.shape, torch.bfloat16, k_src.device)
+    lp = _dev(lengths, "lengths", (B,), torch.int64, k_src.device)
+    kc = _dev(k_cache, "k_cache", (B, H, S, d), torch.bfloat16, k_src.device)
+    vc = _dev(v_cache, "v_cache", (B, H, S, d), torch.bfloat16, k_src.device)
+    pat = pattern.c_struct()
+    _check(lib().attn_blocksparse_cache_fill(ATTN_BF16, B, H, d, ctypes.byref(pat), strided_blocks,
+                                             lp, ks, vs, src_len, kc, vc, _stream()),
+           "attn_blocksparse_cache_fill")

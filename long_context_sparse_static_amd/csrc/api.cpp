@@ -64,7 +64,8 @@ size_t attn_workspace_bytes(int32_t op, attn_dtype_t dtype, int32_t B, int32_t H
     case ATTN_OP_FWD: return 0;
     case ATTN_OP_BWD: return 2 * (size_t)B * H * L_or_cap * sizeof(float);  // D, LSE2
     case ATTN_OP_SPARSE_DECODE:
-    case ATTN_OP_FULL_DECODE: return decode_ws_bytes(B, H, L_or_cap, d);
+    case ATTN_OP_FULL_DECODE:
+    case ATTN_OP_BLOCKSPARSE_DECODE: return decode_ws_bytes(B, H, L_or_cap, d);
   }
   return 0;
 }
@@ -171,7 +172,21 @@ static attn_status_t decode_common(attn_dtype_t dtype, int32_t B, int32_t H, int
   a.max_pos = max_pos;
   attn::decode_split_plan(B, H, n_keys, &a.n_split, &a.split_len);
   a.scale = scale;
+  a.bs_sink = a.bs_local = a.bs_stride = a.bs_cap = 0;
   return hip_status(attn::launch_decode_bf16(a, (hipStream_t)stream));
+}
+
+// BlockSparse compacted-cache geometry: blocks of 64 tokens, sink + local +
+// strided capacity; all checked before anything is enqueued.
+static bool bs_pattern_ok(const attn_pattern_t *p, int32_t strided_blocks) {
+  if (!p || p->kind != ATTN_BLOCKSPARSE || p->block != attn::kBlock) return false;
+  if (p->sink_blocks < 0 || p->local_blocks < 1 || p->stride < 1 || strided_blocks < 0) return false;
+  const int64_t blocks = (int64_t)p->sink_blocks + p->local_blocks + strided_blocks;
+  return blocks * attn::kBlock <= INT32_MAX;
+}
+
+static int64_t bs_slots(const attn_pattern_t *p, int32_t strided_blocks) {
+  return ((int64_t)p->sink_blocks + p->local_blocks + strided_blocks) * attn::kBlock;
 }
 
 attn_status_t attn_sparse_decode(attn_dtype_t dtype, int32_t B, int32_t H, int32_t d, float scale,
@@ -197,6 +212,76 @@ attn_status_t attn_full_decode(attn_dtype_t dtype, int32_t B, int32_t H, int32_t
   if (max_pos + 1 > (int64_t)INT32_MAX * 256) return ATTN_ERR_INVALID_ARG;
   return decode_common(dtype, B, H, d, scale, capacity, -1, 0, max_pos, dev_pos, q, k_new, v_new,
                        k_cache, v_cache, o, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_blocksparse_decode(attn_dtype_t dtype, int32_t B, int32_t H, int32_t d,
+                                      float scale, const attn_pattern_t *pattern,
+                                      int32_t strided_blocks, const int64_t *dev_pos,
+                                      const void *q, const void *k_new, const void *v_new,
+                                      void *k_cache, void *v_cache, void *o, float *lse,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+  if (!bs_pattern_ok(pattern, strided_blocks)) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || !(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (!dev_pos || !q || !k_new || !v_new || !k_cache || !v_cache || !o || !lse)
+    return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * H > 65535) return ATTN_ERR_INVALID_ARG;  // grid.y limit
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const int64_t slots = bs_slots(pattern, strided_blocks);
+  const size_t need = decode_ws_bytes(B, H, slots, d);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  attn::DecodeArgs a;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.o = o;
+  a.lse = lse;
+  a.pos = dev_pos;
+  a.part = (float *)workspace;
+  a.B = B;
+  a.H = H;
+  a.d = d;
+  a.cap = slots;
+  a.sink = 0;
+  a.window = 0;
+  a.max_pos = 0;
+  attn::decode_split_plan(B, H, slots, &a.n_split, &a.split_len);
+  a.scale = scale;
+  a.bs_sink = pattern->sink_blocks;
+  a.bs_local = pattern->local_blocks;
+  a.bs_stride = pattern->stride;
+  a.bs_cap = strided_blocks;
+  return hip_status(attn::launch_decode_bf16(a, (hipStream_t)stream));
+}
+
+attn_status_t attn_blocksparse_cache_fill(attn_dtype_t dtype, int32_t B, int32_t H, int32_t d,
+                                          const attn_pattern_t *pattern, int32_t strided_blocks,
+                                          const int64_t *dev_len, const void *k_src,
+                                          const void *v_src, int64_t src_len, void *k_cache,
+                                          void *v_cache, void *stream) {
+  if (!bs_pattern_ok(pattern, strided_blocks)) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || src_len < 0) return ATTN_ERR_INVALID_ARG;
+  if (!dev_len || !k_src || !v_src || !k_cache || !v_cache) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * H > 65535) return ATTN_ERR_INVALID_ARG;  // grid.y limit
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  attn::BsFillArgs a;
+  a.k_src = k_src;
+  a.v_src = v_src;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.len = dev_len;
+  a.src_len = src_len;
+  a.B = B;
+  a.H = H;
+  a.d = d;
+  a.sink = pattern->sink_blocks;
+  a.local = pattern->local_blocks;
+  a.stride = pattern->stride;
+  a.cap = strided_blocks;
+  return hip_status(attn::launch_bs_fill_bf16(a, (hipStream_t)stream));
 }
 
 attn_status_t attn_ring_fill(attn_dtype_t dtype, int32_t B, int32_t H, int32_t d,

@@ -30,10 +30,57 @@ __device__ __forceinline__ int64_t ring_slot(int64_t p, int sink, int window) {
   return p < sink ? p : sink + (p - sink) % window;
 }
 
+// BlockSparse compacted cache of one (b, h), block size 64 (the BlockSparse
+// pattern of LongGen's sparse layers: mlsanity index page "A Little Goes a
+// Long Way...", "Abstract (arXiv)"; the token at position t reads exactly
+// the keys its row of the prefill mask allows):
+//   slots [0, 64 s)              sink blocks 0 .. s-1
+//   slots [64 s, 64 (s + w))     ring of the w most recent blocks (block j
+//                                at ring block j mod w)
+//   slots [64 (s + w), ...)      strided blocks j >= s, (j + h) % stride == 0,
+//                                that have left the window, ascending
+// A strided block moves from the ring to the strided area when the block w
+// places later starts (bs_move_kernel, before the split kernel).
+__host__ __device__ __forceinline__ int64_t bs_strided_before(int64_t x, int64_t s, int64_t st,
+                                                               int64_t h) {
+  // number of j in [s, x) with (j + h) % st == 0
+  const int64_t r0 = ((-h) % st + st) % st;
+  const int64_t j0 = s <= r0 ? r0 : r0 + ((s - r0 + st - 1) / st) * st;
+  return j0 >= x ? 0 : (x - 1 - j0) / st + 1;
+}
+
+// Block held by ring block pb when the newest block is i (i >= 0).
+__device__ __forceinline__ int64_t bs_ring_block(int64_t i, int64_t pb, int64_t w) {
+  return i - (((i - pb) % w) + w) % w;
+}
+
+// Whether slot `slot` of a BlockSparse cache holds a key the token at
+// position t reads (t = 64 i + r, a = first window block, cnt strided blocks).
+__device__ __forceinline__ bool bs_slot_valid(const DecodeArgs &a, int64_t slot, int64_t t) {
+  const int64_t s = a.bs_sink, w = a.bs_local;
+  if (slot < 64 * s) return slot <= t;
+  if (slot < 64 * (s + w)) {
+    const int64_t q = slot - 64 * s, i = t >> 6;
+    const int64_t j = bs_ring_block(i, q >> 6, w);
+    return j >= s && j >= 0 && (j < i || (q & 63) <= (t & 63));
+  }
+  return true;  // strided blocks below the valid count
+}
+
 // Valid slot count and the new token's slot for position t; false if t is
 // outside what the layer accepts.
-__device__ __forceinline__ bool decode_geometry(const DecodeArgs &a, int64_t t, int64_t *n_valid,
-                                                int64_t *slot_new) {
+__device__ __forceinline__ bool decode_geometry(const DecodeArgs &a, int64_t t, int h,
+                                                int64_t *n_valid, int64_t *slot_new) {
+  if (a.bs_stride > 0) {
+    if (t < 0) return false;
+    const int64_t s = a.bs_sink, w = a.bs_local, i = t >> 6;
+    const int64_t first = i - w + 1 > 0 ? i - w + 1 : 0;
+    const int64_t cnt = bs_strided_before(first, s, a.bs_stride, h);
+    if (cnt > a.bs_cap) return false;
+    *n_valid = 64 * (s + w + cnt);
+    *slot_new = i < s ? t : 64 * s + 64 * (i % w) + (t & 63);
+    return true;
+  }
   if (a.sink >= 0) {
     if (t < 0) return false;
     const int64_t cap = (int64_t)a.sink + a.window;
@@ -62,7 +109,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
 
   const int64_t t = a.pos[b];
   int64_t n_valid = 0, slot_new = -1;
-  const bool ok = decode_geometry(a, t, &n_valid, &slot_new);
+  const bool ok = decode_geometry(a, t, bh % a.H, &n_valid, &slot_new);
+  const bool bs = a.bs_stride > 0;
   const int64_t s0 = (int64_t)split * a.split_len;
   const int64_t s1 = ok ? (s0 + a.split_len < n_valid ? s0 + a.split_len : n_valid) : 0;
 
@@ -119,7 +167,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
 #pragma unroll
       for (int off = 1; off < LPK; off <<= 1) acc += __shfl_xor(acc, off);
       const int64_t key = kb + u * KPW + g;
-      sc[u] = key < s1 ? acc : -INFINITY;
+      sc[u] = key < s1 && (!bs || bs_slot_valid(a, key, t)) ? acc : -INFINITY;
       mx = fmaxf(mx, sc[u]);
     }
     if (mx == -INFINITY) continue;
@@ -188,7 +236,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const int dd = threadIdx.x;
   const float *part = a.part + (size_t)bh * a.n_split * (D + 2);
   int64_t n_valid = 0, slot_new = 0;
-  const bool ok = decode_geometry(a, a.pos[b], &n_valid, &slot_new);
+  const bool ok = decode_geometry(a, a.pos[b], bh % a.H, &n_valid, &slot_new);
   const int used = ok ? (int)((n_valid + a.split_len - 1) / a.split_len) : 0;
   float mm = -INFINITY;
   for (int s = 0; s < used; ++s) mm = fmaxf(mm, part[(size_t)s * (D + 2) + D]);
@@ -231,6 +279,71 @@ __global__ __launch_bounds__(256) void ring_fill_kernel(RingFillArgs a) {
   *(u32x4 *)((bf16 *)a.v_cache + dst) = *(const u32x4 *)((const bf16 *)a.v_src + src);
 }
 
+// Moves a strided block out of the ring when the block w places later
+// starts at position t (first token of its block), before the ring block is
+// overwritten.  One workgroup per (b, h).
+template <int D>
+__global__ __launch_bounds__(256) void bs_move_kernel(DecodeArgs a) {
+  constexpr int CPR = D / 8;
+  const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  const int64_t t = a.pos[b];
+  const int64_t s = a.bs_sink, w = a.bs_local, st = a.bs_stride;
+  if (t < 0 || (t & 63) != 0) return;
+  const int64_t j = (t >> 6) - w;
+  if (j < s || (j + h) % st != 0) return;
+  const int64_t m = bs_strided_before(j, s, st, h);
+  if (m >= a.bs_cap) return;
+  const size_t src = (size_t)bh * a.cap + 64 * (s + j % w);
+  const size_t dst = (size_t)bh * a.cap + 64 * (s + w + m);
+  for (int ci = threadIdx.x; ci < 64 * CPR; ci += blockDim.x) {
+    const size_t r = ci / CPR, c = ci % CPR;
+    *(u32x4 *)((bf16 *)a.k_cache + (dst + r) * D + c * 8) =
+        *(const u32x4 *)((const bf16 *)a.k_cache + (src + r) * D + c * 8);
+    *(u32x4 *)((bf16 *)a.v_cache + (dst + r) * D + c * 8) =
+        *(const u32x4 *)((const bf16 *)a.v_cache + (src + r) * D + c * 8);
+  }
+}
+
+// Fills a BlockSparse compacted cache from prefill K/V [B,H,src_len,D]: slot
+// by slot, the token decode would hold there after appending tokens
+// 0 .. len-1.  Slots that hold nothing yet are left untouched.
+template <int D>
+__global__ __launch_bounds__(256) void bs_fill_kernel(BsFillArgs a) {
+  constexpr int CPR = D / 8;
+  const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int64_t s = a.sink, w = a.local, st = a.stride;
+  const int64_t slots = 64 * (s + w + a.cap);
+  const int64_t ci = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (ci >= slots * CPR) return;
+  const int64_t slot = ci / CPR;
+  const int c = (int)(ci % CPR);
+  int64_t n = a.len[b];
+  if (n > a.src_len) n = a.src_len;
+  if (n <= 0) return;
+  const int64_t last = (n - 1) >> 6;
+  int64_t p;
+  if (slot < 64 * s) {
+    p = slot;
+  } else if (slot < 64 * (s + w)) {
+    const int64_t q = slot - 64 * s;
+    const int64_t j = last - ((((last - (q >> 6)) % w) + w) % w);
+    if (j < s || j < 0) return;
+    p = 64 * j + (q & 63);
+  } else {
+    const int64_t m = (slot - 64 * (s + w)) >> 6;
+    const int64_t r0 = ((-(int64_t)h) % st + st) % st;
+    const int64_t j0 = s <= r0 ? r0 : r0 + ((s - r0 + st - 1) / st) * st;
+    const int64_t j = j0 + m * st;
+    if (j > last - w) return;  // still in the ring
+    p = 64 * j + (slot & 63);
+  }
+  if (p >= n) return;
+  const size_t src = ((size_t)bh * a.src_len + p) * D + c * 8;
+  const size_t dst = ((size_t)bh * slots + slot) * D + c * 8;
+  *(u32x4 *)((bf16 *)a.k_cache + dst) = *(const u32x4 *)((const bf16 *)a.k_src + src);
+  *(u32x4 *)((bf16 *)a.v_cache + dst) = *(const u32x4 *)((const bf16 *)a.v_src + src);
+}
+
 }  // namespace
 
 void decode_split_plan(int32_t B, int32_t H, int64_t n_keys, int32_t *n_split, int32_t *split_len) {
@@ -249,6 +362,12 @@ void decode_split_plan(int32_t B, int32_t H, int64_t n_keys, int32_t *n_split, i
 
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {
   dim3 grid(a.n_split, a.B * a.H);
+  if (a.bs_stride > 0) {
+    if (a.d == 128)
+      hipLaunchKernelGGL(bs_move_kernel<128>, dim3(a.B * a.H), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(bs_move_kernel<64>, dim3(a.B * a.H), dim3(256), 0, s, a);
+  }
   if (a.d == 128) {
     hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(kDecThreads), 0, s, a);
     hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(a.B * a.H), dim3(128), 0, s, a);
@@ -267,6 +386,17 @@ hipError_t launch_ring_fill_bf16(const RingFillArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(ring_fill_kernel<128>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(ring_fill_kernel<64>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bs_fill_bf16(const BsFillArgs &a, hipStream_t s) {
+  const int64_t slots = 64 * ((int64_t)a.sink + a.local + a.cap);
+  const int64_t chunks = slots * (a.d / 8);
+  dim3 grid((unsigned)((chunks + 255) / 256), a.B * a.H);
+  if (a.d == 128)
+    hipLaunchKernelGGL(bs_fill_kernel<128>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(bs_fill_kernel<64>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -57,6 +57,10 @@ struct DecodeArgs {
   int64_t max_pos;     // full layers: host bound on positions
   int32_t n_split, split_len;
   float scale;
+  // BlockSparse layers (bs_stride > 0): compacted cache of bs_sink sink
+  // blocks, a ring of bs_local blocks and bs_cap strided blocks; sink and
+  // window are unused then.
+  int32_t bs_sink, bs_local, bs_stride, bs_cap;
 };
 
 struct RingFillArgs {
@@ -72,6 +76,18 @@ hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_ring_fill_bf16(const RingFillArgs &a, hipStream_t s);
+
+// Fill of a BlockSparse compacted cache from prefill K/V: the state decode
+// would have reached after appending tokens 0 .. len-1.
+struct BsFillArgs {
+  const void *k_src, *v_src;
+  void *k_cache, *v_cache;
+  const int64_t *len;
+  int64_t src_len;
+  int32_t B, H, d;
+  int32_t sink, local, stride, cap;  // blocks
+};
+hipError_t launch_bs_fill_bf16(const BsFillArgs &a, hipStream_t s);
 
 // LDS bytes one forward workgroup needs (static tiles + union bitmap).
 size_t fwd_bf16_lds_bytes(int d, int n_kblocks);

@@ -5,7 +5,7 @@ does.  It shares no code with the HIP library.  See ``attention.py``."""
 
 from .attention import (  # noqa: F401
     ATTNSINK, BLOCKSPARSE, FULL, attention_backward, attention_forward,
-    block_lists, decode_one, decode_positions, dense_token_mask,
+    block_lists, blocksparse_decode_positions, decode_one, decode_positions, dense_token_mask,
     head_pattern, kv_cache_bytes, pattern_lists_for_head, sparse_backward, sparse_forward,
     transpose_lists,
 )

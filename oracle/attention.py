@@ -278,6 +278,18 @@ def decode_positions(t, sink_tokens=None, window_tokens=None):
     return np.array(sorted(keep), dtype=np.int64)
 
 
+def blocksparse_decode_positions(t, pattern, head):
+    """Token positions the token at absolute position t reads in a layer with
+    a block pattern (BlockSparse, or any pattern dict): the key blocks its
+    query block lists, keys later than t masked -- exactly its row of the
+    prefill mask.  Used for BlockSparse decode against a compacted cache."""
+    block = head_pattern(pattern, head)["block"]
+    i = t // block
+    row = pattern_lists_for_head(pattern, i + 1, head)[i]
+    keep = [p for j in row for p in range(j * block, (j + 1) * block) if p <= t]
+    return np.array(keep, dtype=np.int64)
+
+
 def decode_one(q, k_hist, v_hist, positions, scale):
     """o, lse of one query over the listed token rows of its history."""
     q = np.asarray(q, dtype=np.float64)

@@ -21,8 +21,8 @@ import torch
 import torch.nn.functional as F
 
 from oracle import (ATTNSINK, BLOCKSPARSE, FULL, attention_backward,
-                    attention_forward, block_lists, decode_one,
-                    decode_positions, dense_token_mask, kv_cache_bytes,
+                    attention_forward, block_lists, blocksparse_decode_positions,
+                    decode_one, decode_positions, dense_token_mask, kv_cache_bytes,
                     sparse_backward, sparse_forward, transpose_lists)
 
 
@@ -343,6 +343,42 @@ def test_decode_zero_query_counts():
         assert lse == pytest.approx(math.log(min(t + 1, 22)), abs=1e-12)
         keys = sorted(set(range(min(6, t + 1))) | set(range(max(0, t - 15), t + 1)))
         np.testing.assert_allclose(o, hist_v[keys].mean(axis=0), atol=1e-12)
+
+
+def test_blocksparse_decode_positions_worked_example():
+    """Token 5000 of head 3 with sink 1, local 16, stride 8 (64-token blocks):
+    its block 78 reads block 0, blocks 63..78 and the strided blocks
+    5, 13, ..., 61 (69 and 77 are already local); keys after 5000 masked."""
+    pat = dict(kind=BLOCKSPARSE, block=64, sink_blocks=1, local_blocks=16, stride=8)
+    want = list(range(64))
+    for j in (5, 13, 21, 29, 37, 45, 53, 61):
+        want += list(range(64 * j, 64 * j + 64))
+    want += list(range(63 * 64, 5001))
+    assert list(blocksparse_decode_positions(5000, pat, 3)) == want
+    # sink + window only (stride beyond every block): the ring rule of attnsink
+    pat1 = dict(kind=BLOCKSPARSE, block=64, sink_blocks=1, local_blocks=4, stride=10 ** 6)
+    for t in (0, 63, 64, 255, 256, 300, 1000):
+        got = blocksparse_decode_positions(t, pat1, 1)
+        keep = sorted(set(range(min(64, t + 1))) | set(range(64 * max(0, t // 64 - 3), t + 1)))
+        assert list(got) == keep
+
+
+def test_blocksparse_decode_equals_prefill_row():
+    """Decoding token t against its positions gives row t of the prefill
+    forward (whose mask is built by a separate routine, itself pinned to
+    library attention above), for every head phase and rows at and around
+    block edges."""
+    B, H, L, d = 1, 3, 96, 4
+    pat = dict(kind=BLOCKSPARSE, block=8, sink_blocks=1, local_blocks=2, stride=3, causal=True)
+    q, k, v = rand(B, H, L, d), rand(B, H, L, d), rand(B, H, L, d)
+    rows = [0, 7, 8, 23, 24, 25, 47, 64, 95]
+    o, lse = sparse_forward(q, k, v, pat, scale=0.5, rows=rows)
+    for h in range(H):
+        for t in rows:
+            od, ld = decode_one(q[0, h, t], k[0, h], v[0, h],
+                                blocksparse_decode_positions(t, pat, h), 0.5)
+            np.testing.assert_allclose(od, o[0, h, t], atol=1e-12)
+            assert ld == pytest.approx(lse[0, h, t], abs=1e-12)
 
 
 # --------------------------------------------------------------------------
