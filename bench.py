@@ -18,8 +18,10 @@ the full-layer and whole-hybrid prefill rates, the roofline of the dominant
 kernel and the CPU oracle baseline are reported alongside.
 
 Other workloads (--workload): attnsink8k, blocksparse32k, blocksparse128k,
-attnsink128k, train64k (forward + backward), and copy1g (a plain 1 GiB device
-copy, the calibration kernel for the HBM byte counters).
+attnsink128k, train64k (AttnSink forward + backward), blocksparse32k_train and
+blocksparse128k_train (BlockSparse forward + backward), bsdecode128k
+(BlockSparse decode against its compacted cache), and copy1g (a plain 1 GiB
+device copy, the calibration kernel for the HBM byte counters).
 """
 
 from __future__ import annotations
@@ -317,6 +319,66 @@ class Copy1G:
                                 parallelism="single GPU"))
 
 
+class BsDecode128k:
+    """Decode of 16 sequences at t = 131072 in a BlockSparse layer (sink 1,
+    local 16, stride 8 blocks) against its compacted cache, cycling over
+    distinct layer caches so that no read hits the 256 MB MALL."""
+    name = "bsdecode128k"
+
+    def __init__(self, n_layers=4):
+        dev = torch.device("cuda")
+        self.pat = lcs.blocksparse_pattern(1, 16, 8)
+        self.t = 131072
+        B = DEC_BATCH
+        self.cap_blocks = lcs.blocksparse_strided_capacity(self.pat, self.t + 1)
+        S = lcs.blocksparse_cache_slots(self.pat, self.cap_blocks)
+        self.S = S
+        self.pos = torch.full((B,), self.t, dtype=torch.int64, device=dev)
+        self.q = fill_randn((B, H, 1, D), seed_for(6, 0, "q_dec"))
+        self.k_new = fill_randn((B, H, 1, D), seed_for(6, 0, "k_new"))
+        self.v_new = fill_randn((B, H, 1, D), seed_for(6, 0, "v_new"))
+        self.caches = [(fill_randn((B, H, S, D), seed_for(6, layer, "cache")),
+                        fill_randn((B, H, S, D), seed_for(6, layer, "cache_v")))
+                       for layer in range(n_layers)]
+        self.o = torch.empty((B, H, 1, D), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(lcs.attn_workspace_bytes(lcs.ATTN_OP_BLOCKSPARSE_DECODE, lcs.ATTN_BF16,
+                                                       B, H, S, D), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        # keys each (b, h) attends: sink block, the 16 window blocks up to t
+        # (the newest holding t % 64 + 1 tokens) and the strided blocks of
+        # head h that left the window
+        i = self.t // BLK
+        s, w, st = self.pat.sink_blocks, self.pat.local_blocks, self.pat.stride
+        first = i - w + 1
+        keys = 0
+        for h in range(H):
+            strided = sum(1 for j in range(s, first) if (j + h) % st == 0)
+            keys += BLK * (s + w - 1 + strided) + self.t % BLK + 1
+        self.keys_per_seq = keys                     # summed over heads
+
+    def step(self, timer):
+        for kc, vc in self.caches:
+            with timer.span("decode_bs"):
+                lcs.attn_blocksparse_decode(self.q, self.k_new, self.v_new, kc, vc, self.pos, self.pat,
+                                            self.cap_blocks, o=self.o, lse=self.lse, workspace=self.ws)
+
+    def report(self, times, steps):
+        t = sum(times["decode_bs"]) / len(times["decode_bs"])        # ms per layer
+        nbytes = DEC_BATCH * self.keys_per_seq * 2 * D * 2
+        gbps = nbytes / (t * 1e-3) / 1e9
+        return dict(value=DEC_BATCH / (t * 1e-3), unit="tok/s (one layer)",
+                    extra=dict(layer_ms=t, layer_gbps=gbps, attended_bytes=nbytes,
+                               cache_slots=self.S, strided_capacity_blocks=self.cap_blocks),
+                    roofline=dict(bound="hbm", kernel="bs_move_kernel + decode_split_kernel + "
+                                  "decode_combine_kernel", achieved=gbps, peak=PEAK_HBM_GBPS,
+                                  unit="GB/s", frac=gbps / PEAK_HBM_GBPS, traffic=None),
+                    config=dict(workload="bsdecode128k: BlockSparse (sink 1, local 16, stride 8 "
+                                "blocks) decode of 16 seqs at t=131072, H=32 d=128 bf16, compacted "
+                                f"cache {self.S} slots", global_batch=DEC_BATCH, seq_len=self.t,
+                                parallelism="single GPU", layer_caches=len(self.caches)))
+
+
 def make_workload(name):
     if name == "hybrid128k":
         return Hybrid128k()
@@ -330,6 +392,12 @@ def make_workload(name):
         return Prefill(name, lcs.attnsink_pattern(1, 64), 131072, 5)
     if name == "train64k":
         return Prefill(name, lcs.attnsink_pattern(1, 64), 65536, 4, backward=True)
+    if name == "blocksparse32k_train":
+        return Prefill(name, lcs.blocksparse_pattern(1, 16, 8), 32768, 3, backward=True)
+    if name == "blocksparse128k_train":
+        return Prefill(name, lcs.blocksparse_pattern(1, 16, 8), 131072, 3, backward=True)
+    if name == "bsdecode128k":
+        return BsDecode128k()
     if name == "copy1g":
         return Copy1G()
     raise SystemExit(f"unknown workload {name}")
@@ -471,7 +539,7 @@ def main():
     line = {
         "metric": "effective TFLOP/s (computed blocks) sparse prefill @128K; decode tok/s",
         "value": rep["value"],
-        "unit": "TFLOP/s",
+        "unit": rep.get("unit", "TFLOP/s"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

@@ -135,6 +135,12 @@ attn_status_t attn_sparse_bwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t 
   a.d = d;
   a.scale = scale;
   a.causal = pattern->causal ? 1 : 0;
+  // Work grouping only (any grouping gives the same result): a per-head
+  // BlockSparse index groups each head's strided key blocks together.
+  a.kgroup = pattern->kind == ATTN_BLOCKSPARSE && dev_index->n_heads == H && pattern->stride >= 2 &&
+                     pattern->stride <= dev_index->n_kblocks
+                 ? pattern->stride
+                 : 1;
   return hip_status(attn::launch_bwd_bf16(a, (hipStream_t)stream));
 }
 

@@ -85,6 +85,56 @@ __device__ __forceinline__ bf16x8 pack_half(const f32x16 &t, int half) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// Key blocks of the dK/dV tiles of one head.  g == 1: tile t holds blocks
+// TB t .. TB t + TB - 1.  g > 1 (BlockSparse with stride g): the head's
+// strided class, the blocks j = r0 (mod g) with r0 = -h mod g, comes first,
+// TB class members per tile -- their CSC columns run from about j to the last
+// query block, so the members of one tile list nearly the same query blocks
+// and no wave idles through another member's long column; the remaining
+// blocks follow, TB consecutive ones per tile.  Every head gets the same
+// number of tiles (the class has ceil(nkb / g) members at most); a slot past
+// a head's blocks holds -1.
+template <int TB>
+struct KeyTiles {
+  int g, r0, n_cls, cls_tiles, nkb;
+
+  __host__ __device__ static int cls_tiles_max(int nkb, int g) {
+    return g > 1 ? ((nkb + g - 1) / g + TB - 1) / TB : 0;
+  }
+  __host__ __device__ static int per_head(int nkb, int g) {
+    if (g <= 1) return (nkb + TB - 1) / TB;
+    return cls_tiles_max(nkb, g) + (nkb - nkb / g + TB - 1) / TB;
+  }
+  // tiles of a head started before any other tile of any head (longest first)
+  __host__ __device__ static int priority(int nkb, int g) {
+    const int n = per_head(nkb, g);
+    const int p = g > 1 ? cls_tiles_max(nkb, g) + 1 : 1;
+    return p < n ? p : n;
+  }
+
+  __device__ __forceinline__ void init(int nkb_, int g_, int h) {
+    nkb = nkb_;
+    g = g_;
+    r0 = g > 1 ? (g - h % g) % g : 0;
+    n_cls = g > 1 && r0 < nkb ? (nkb - 1 - r0) / g + 1 : 0;
+    cls_tiles = cls_tiles_max(nkb, g);
+  }
+  __device__ __forceinline__ int block(int tile, int r) const {
+    if (g <= 1) {
+      const int j = tile * TB + r;
+      return j < nkb ? j : -1;
+    }
+    if (tile < cls_tiles) {
+      const int idx = tile * TB + r;
+      return idx < n_cls ? r0 + idx * g : -1;
+    }
+    const int idx = (tile - cls_tiles) * TB + r;
+    const int p = idx / (g - 1), o = idx % (g - 1);
+    const int j = p * g + o + (o >= r0 ? 1 : 0);
+    return j < nkb ? j : -1;
+  }
+};
+
 // One position of a union walk.
 struct BwdPos {
   bool valid;
@@ -260,29 +310,37 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
   extern __shared__ uint32_t dyn_lds[];
 
   const int nkb = a.ix.n_kblocks, nqb = a.ix.n_qblocks;
-  const int n_tiles = (nkb + kBwdTB - 1) / kBwdTB;
+  using KTiles = KeyTiles<kBwdTB>;
+  const int n_tiles = KTiles::per_head(nkb, a.kgroup);
+  const int n_first = KTiles::priority(nkb, a.kgroup);
   const int BH = a.B * a.H;
-  // Long CSC columns (the sink block, early blocks of full attention) are the
-  // first tiles of each head: start every head's tile 0 before anything else
-  // on its XCD, then walk the heads' remaining tiles in order.
+  // The longest CSC columns (the sink block, early blocks of full attention,
+  // the strided class of BlockSparse) are in the first n_first tiles of each
+  // head: start those, round-robin over the XCD's heads, before anything
+  // else on the XCD, then walk the heads' remaining tiles in order.
   int bh, tile;
-  if (BH % kNumXcd == 0 && n_tiles > 1) {
+  if (BH % kNumXcd == 0 && n_tiles > n_first) {
     const int hpx = BH / kNumXcd;
     const int xcd = blockIdx.x % kNumXcd;
     int s = blockIdx.x / kNumXcd;
-    if (s < hpx) {
-      bh = xcd * hpx + s;
-      tile = 0;
+    if (s < hpx * n_first) {
+      bh = xcd * hpx + s % hpx;
+      tile = s / hpx;
     } else {
-      s -= hpx;
-      bh = xcd * hpx + s / (n_tiles - 1);
-      tile = 1 + s % (n_tiles - 1);
+      s -= hpx * n_first;
+      bh = xcd * hpx + s / (n_tiles - n_first);
+      tile = n_first + s % (n_tiles - n_first);
     }
   } else {
     bh = blockIdx.x / n_tiles;
     tile = blockIdx.x % n_tiles;
   }
   const int hidx = a.ix.n_heads == 1 ? 0 : bh % a.H;
+  KTiles kt;
+  kt.init(nkb, a.kgroup, bh % a.H);
+  int krows[kBwdTB];
+#pragma unroll
+  for (int r = 0; r < kBwdTB; ++r) krows[r] = kt.block(tile, r);
   const size_t base = (size_t)bh * a.L * D;
   const bf16 *qg = (const bf16 *)a.q + base;
   const bf16 *dog = (const bf16 *)a.dout + base;
@@ -293,8 +351,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, hh = lane >> 5;
   const int my_r = wave >> 1;
-  const int kb = tile * kBwdTB + my_r;
-  const bool k_valid = kb < nkb;
+  const int kb = krows[my_r];
+  const bool k_valid = kb >= 0;
   const int k_tok = kb * kBlock + (wave & 1) * 32 + n;
   const size_t krow = base + (size_t)k_tok * D;
 
@@ -331,10 +389,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
 
   RowsBitmap<kBwdTB> pb;
   pb.init(dyn_lds, nqb);
-  pb.build(a.ix.col_ptr + (size_t)hidx * (nkb + 1), tile * kBwdTB, nkb, a.ix.nnz, a.ix.row_idx, nqb,
-           kBwdThreads);
+  pb.build_rows(a.ix.col_ptr + (size_t)hidx * (nkb + 1), krows, a.ix.nnz, a.ix.row_idx, nqb,
+                kBwdThreads);
   RowsIter<kBwdTB> it;
-  it.start(nqb, (tile * kBwdTB + 63) & ~63);
+  it.start(nqb, (krows[0] + 63) & ~63);
   auto advance = [&]() __attribute__((always_inline)) -> BwdPos {
     BwdPos p;
     p.valid = it.next(pb);
@@ -478,7 +536,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const int rpb = 256 / (D / 8);
   const int grid_delta = (int)((rows + rpb - 1) / rpb);
   const int q_tiles = (a.ix.n_qblocks + kBwdTB - 1) / kBwdTB;
-  const int k_tiles = (a.ix.n_kblocks + kBwdTB - 1) / kBwdTB;
+  const int k_tiles = KeyTiles<kBwdTB>::per_head(a.ix.n_kblocks, a.kgroup);
   const int BH = a.B * a.H;
   const size_t dyn_k = RowsBitmap<kBwdTB>::lds_bytes(a.ix.n_qblocks);
   const size_t dyn_q = RowsBitmap<kBwdTB>::lds_bytes(a.ix.n_kblocks);

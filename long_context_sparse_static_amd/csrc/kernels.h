@@ -42,6 +42,7 @@ struct BwdArgs {
   int32_t B, H, L, d;
   float scale;
   int32_t causal;
+  int32_t kgroup;      // dK/dV key-block grouping: 1, or the BlockSparse stride
 };
 
 struct DecodeArgs {

@@ -290,14 +290,15 @@ struct RowsBitmap {
   }
 
   // Caller: every thread of the workgroup, nt threads.  Ends with a barrier.
-  __device__ void build(const int32_t *ptr, int first, int n_rows, int nnz, const int32_t *ids,
-                        int n_ids, int nt) {
+  // Bitmap row r holds list rows[r] (none if rows[r] < 0).
+  __device__ void build_rows(const int32_t *ptr, const int (&rows)[R], int nnz, const int32_t *ids,
+                             int n_ids, int nt) {
     for (int i = threadIdx.x; i < R * nw + nsw; i += nt) bm[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int row = first + r;
-      if (row < n_rows) {
+      const int row = rows[r];
+      if (row >= 0) {
         const int p = clamp_i(ptr[row], 0, nnz);
         const int e = clamp_i(ptr[row + 1], p, nnz);
         for (int x = p + threadIdx.x; x < e; x += nt) {
@@ -314,6 +315,15 @@ struct RowsBitmap {
       if (any) atomicOr(&sm[w >> 5], 1u << (w & 31));
     }
     __syncthreads();
+  }
+
+  // Lists first .. first + R - 1 (those below n_rows).
+  __device__ void build(const int32_t *ptr, int first, int n_rows, int nnz, const int32_t *ids,
+                        int n_ids, int nt) {
+    int rows[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rows[r] = first + r < n_rows ? first + r : -1;
+    build_rows(ptr, rows, nnz, ids, n_ids, nt);
   }
 };
 

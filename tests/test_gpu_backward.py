@@ -33,6 +33,8 @@ SMALL = [
     (lcs.blocksparse_pattern(1, 3, 4), 128, 1, 8, 19),
     (lcs.full_pattern(), 128, 1, 2, 7),
     (lcs.attnsink_pattern(2, 2), 128, 1, 1, 1),
+    (lcs.blocksparse_pattern(2, 2, 3), 64, 1, 3, 13),     # stride 3: every head phase, ragged classes
+    (lcs.blocksparse_pattern(1, 2, 40), 128, 1, 2, 10),   # stride beyond every block
 ]
 
 
@@ -94,3 +96,32 @@ def test_bf16_backward_mixed_heads_full_oracle():
                                        [oracle_pattern(p) for p in pats])
     for name, g, w in (("dq", dq, wq), ("dk", dk, wk), ("dv", dv, wv)):
         print("mixed", name, assert_bf16_close(as_f64(g), w, name))
+
+
+def test_backward_blocksparse_32k_sampled_blocks():
+    """The 32K-token BlockSparse layer (sink 1, local 16, stride 8; 32 heads,
+    d 128) forward + backward: every dQ, dK, dV element is written and finite,
+    and the oracle checks sampled query blocks and key blocks of two head
+    phases on their exact sub-problems -- the sink block, strided-class
+    blocks whose columns span nearly every later query block, and blocks
+    read only locally."""
+    need_gpu()
+    pat = lcs.blocksparse_pattern(1, 16, 8)
+    L, H = 32768, 32
+    q, k, v, do = _inputs((1, H, L, 128), 3, big=True)
+    ix = lcs.build_device_index(pat, H, L, q.device, with_csc=True)
+    o, lse = lcs.attn_sparse_fwd(q, k, v, ix, pat)
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    lcs.attn_sparse_bwd(q, k, v, o, lse, do, ix, pat, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    nb = L // 64
+    # head 0: strided class j = 0 mod 8; head 13: j = 3 mod 8
+    for h, kblocks in ((0, [0, 8, 9, 16, 255, nb - 1]), (13, [3, 4, 11, 300, nb - 2])):
+        qblocks = [0, 17, 130, nb - 1]
+        want = sample_backward(q, k, v, do, pat, h, 0, qblocks, kblocks)
+        for (name, blk), w in want.items():
+            g = {"dq": dq, "dk": dk, "dv": dv}[name][0, h, 64 * blk:64 * (blk + 1)]
+            mx, mean = assert_bf16_close(as_f64(g), w, f"{name} head {h} block {blk}")
+            print(name, h, blk, mx, mean)
