@@ -4,8 +4,8 @@ block-sparse masks.  Only ``tests/``, ``__graft_entry__.smoke()`` and
 does.  It shares no code with the HIP library.  See ``attention.py``."""
 
 from .attention import (  # noqa: F401
-    ATTNSINK, BLOCKSPARSE, FULL, attention_backward, attention_forward,
+    ATTNSINK, BLOCKSPARSE, FULL, SLIDING, attention_backward, attention_forward,
     block_lists, blocksparse_decode_positions, decode_one, decode_positions, dense_token_mask,
-    head_pattern, kv_cache_bytes, pattern_lists_for_head, sparse_backward, sparse_forward,
-    transpose_lists,
+    head_pattern, kv_cache_bytes, pattern_lists_for_head, pattern_token_mask,
+    sliding_token_mask, sparse_backward, sparse_forward, transpose_lists,
 )

@@ -32,7 +32,10 @@ Readings taken where the pages are silent (each is listed in the design notes):
   * the softmax scale is 1/sqrt(d); LSE is the natural log of the sum of
     exp(scaled scores) over allowed keys; an empty row gives O = 0, LSE = -inf;
   * decode is token-granular: the new token t sees tokens 0..sink-1 and
-    t-window+1..t (itself included).
+    t-window+1..t (itself included);
+  * the token-granular sliding window (kind "sliding", with or without sink
+    blocks) applies that same token rule in prefill, so prefill row t and the
+    decode of token t read the same keys.
 
 Parity pins (tests/test_oracle_pins.py): every function here is pinned by a
 check that does not re-type its formula -- closed-form counts, textbook /
@@ -51,6 +54,7 @@ import numpy as np
 FULL = "full"
 ATTNSINK = "attnsink"
 BLOCKSPARSE = "blocksparse"
+SLIDING = "sliding"        # token-granular window (+ optional sink blocks)
 
 
 # ----------------------------------------------------------------------------
@@ -58,7 +62,7 @@ BLOCKSPARSE = "blocksparse"
 #               summary page, Approach: static, block-wise access]
 # ----------------------------------------------------------------------------
 def block_lists(kind, n_qblocks, *, sink_blocks=1, local_blocks=1, stride=0,
-                head=0, n_kblocks=None):
+                head=0, n_kblocks=None, window_tokens=0, block=64):
     """Ascending KV-block list of every query block, by brute-force scan.
 
     For query block ``i`` every key block ``j`` in ``0..n_kblocks-1`` is tested
@@ -66,6 +70,10 @@ def block_lists(kind, n_qblocks, *, sink_blocks=1, local_blocks=1, stride=0,
       * full:        j <= i
       * attnsink:    j < sink_blocks (and j <= i), or i-local_blocks < j <= i
       * blocksparse: the attnsink rule, or j < i with (j + head) % stride == 0
+      * sliding:     j <= i, and j < sink_blocks or the last key of block j is
+                     within window_tokens of the first query of block i (the
+                     blocks holding any key the token rule of
+                     ``sliding_token_mask`` allows for some query of block i)
     Returns a list of Python int lists.
     """
     if n_kblocks is None:
@@ -76,6 +84,9 @@ def block_lists(kind, n_qblocks, *, sink_blocks=1, local_blocks=1, stride=0,
         for j in range(n_kblocks):
             if kind == FULL:
                 keep = j <= i
+            elif kind == SLIDING:
+                keep = j <= i and (j < sink_blocks or
+                                   block * i - (block * j + block - 1) < window_tokens)
             elif kind in (ATTNSINK, BLOCKSPARSE):
                 is_sink = j < sink_blocks and j <= i
                 is_local = (i - local_blocks) < j <= i
@@ -97,6 +108,19 @@ def transpose_lists(lists, n_kblocks):
         for j in row:
             cols[j].append(i)
     return cols
+
+
+def sliding_token_mask(n_q_tokens, n_k_tokens, sink_tokens, window_tokens, rows=None):
+    """Boolean [n_rows, n_k_tokens] of the token-granular sliding window: query
+    position q reads key position k when k <= q and either k is one of the
+    first ``sink_tokens`` tokens or q - k < ``window_tokens`` (the window
+    holds the query itself and the window_tokens - 1 tokens before it).
+    With sink_tokens = 0 this is plain sliding-window attention."""
+    if rows is None:
+        rows = np.arange(n_q_tokens)
+    rows = np.asarray(rows)[:, None]
+    k = np.arange(n_k_tokens)[None, :]
+    return (k <= rows) & ((k < sink_tokens) | (rows - k < window_tokens))
 
 
 def dense_token_mask(lists, block, n_q_tokens, n_k_tokens, causal, rows=None):
@@ -206,7 +230,20 @@ def pattern_lists_for_head(pattern, n_qblocks, head):
     return block_lists(pattern["kind"], n_qblocks,
                        sink_blocks=pattern.get("sink_blocks", 0),
                        local_blocks=pattern.get("local_blocks", 0),
-                       stride=pattern.get("stride", 0), head=head)
+                       stride=pattern.get("stride", 0), head=head,
+                       window_tokens=pattern.get("window_tokens", 0),
+                       block=pattern.get("block", 64))
+
+
+def pattern_token_mask(pattern, head, L, rows=None):
+    """Dense [n_rows, L] mask of head ``head``: the token rule for a sliding
+    pattern, else the block lists expanded to tokens (causal inside blocks)."""
+    p = head_pattern(pattern, head)
+    if p["kind"] == SLIDING:
+        return sliding_token_mask(L, L, p["block"] * p.get("sink_blocks", 0),
+                                  p["window_tokens"], rows=rows)
+    lists = pattern_lists_for_head(pattern, L // p["block"], head)
+    return dense_token_mask(lists, p["block"], L, L, p.get("causal", True), rows=rows)
 
 
 def sparse_forward(q, k, v, pattern, scale=None, heads=None, rows=None):
@@ -224,16 +261,13 @@ def sparse_forward(q, k, v, pattern, scale=None, heads=None, rows=None):
     lse = np.full((B, H, L), np.nan)
     heads = range(H) if heads is None else heads
     for h in heads:
-        block = head_pattern(pattern, h)["block"]
-        lists = pattern_lists_for_head(pattern, L // block, h)
-        causal = head_pattern(pattern, h).get("causal", True)
         if rows is None:
-            mask = dense_token_mask(lists, block, L, L, causal)
+            mask = pattern_token_mask(pattern, h, L)
             for b in range(B):
                 o[b, h], lse[b, h] = attention_forward(q[b, h], k[b, h], v[b, h], mask, scale)
         else:
             rows = np.asarray(rows)
-            mask = dense_token_mask(lists, block, L, L, causal, rows=rows)
+            mask = pattern_token_mask(pattern, h, L, rows=rows)
             for b in range(B):
                 ob, lb = attention_forward(q[b, h][rows], k[b, h], v[b, h], mask, scale)
                 o[b, h][rows] = ob
@@ -251,9 +285,7 @@ def sparse_backward(q, k, v, do, pattern, scale=None, heads=None):
     lse = np.full((B, H, L), np.nan)
     heads = range(H) if heads is None else heads
     for h in heads:
-        block = head_pattern(pattern, h)["block"]
-        lists = pattern_lists_for_head(pattern, L // block, h)
-        mask = dense_token_mask(lists, block, L, L, head_pattern(pattern, h).get("causal", True))
+        mask = pattern_token_mask(pattern, h, L)
         for b in range(B):
             dq[b, h], dk[b, h], dv[b, h], o[b, h], lse[b, h] = attention_backward(
                 q[b, h], k[b, h], v[b, h], do[b, h], mask, scale)

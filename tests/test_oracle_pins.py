@@ -20,10 +20,11 @@ import pytest
 import torch
 import torch.nn.functional as F
 
-from oracle import (ATTNSINK, BLOCKSPARSE, FULL, attention_backward,
+from oracle import (ATTNSINK, BLOCKSPARSE, FULL, SLIDING, attention_backward,
                     attention_forward, block_lists, blocksparse_decode_positions,
                     decode_one, decode_positions, dense_token_mask, kv_cache_bytes,
-                    sparse_backward, sparse_forward, transpose_lists)
+                    pattern_token_mask, sliding_token_mask, sparse_backward,
+                    sparse_forward, transpose_lists)
 
 
 # --------------------------------------------------------------------------
@@ -183,6 +184,77 @@ def test_general_pattern_matches_library_with_mask():
     mask = dense_token_mask(lists, block, L, L, True)
     o, _ = attention_forward(q, k, v, mask, 0.25)
     np.testing.assert_allclose(o, sdpa(q, k, v, attn_mask=mask, scale=0.25), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# token-granular sliding window
+# --------------------------------------------------------------------------
+def test_sliding_mask_examples():
+    """Hand-checked rows: window 3, sink 2 tokens, 8 tokens."""
+    m = sliding_token_mask(8, 8, 2, 3)
+    assert [list(np.nonzero(m[q])[0]) for q in (0, 1, 2, 4, 7)] == [
+        [0], [0, 1], [0, 1, 2], [0, 1, 2, 3, 4], [0, 1, 5, 6, 7]]
+    m0 = sliding_token_mask(8, 8, 0, 3)
+    assert list(np.nonzero(m0[7])[0]) == [5, 6, 7] and list(np.nonzero(m0[1])[0]) == [0, 1]
+
+
+@pytest.mark.parametrize("L,block,s,W", [(96, 8, 0, 5), (96, 8, 1, 8), (100, 10, 2, 17),
+                                         (128, 16, 0, 1), (64, 8, 3, 200)])
+def test_sliding_block_lists_are_the_blocks_the_token_rule_touches(L, block, s, W):
+    """Block lists of the sliding kind == the block pairs holding any allowed
+    token pair, found by scanning the token mask."""
+    nb = L // block
+    m = sliding_token_mask(L, L, block * s, W)
+    want = [[j for j in range(nb) if m[i * block:(i + 1) * block, j * block:(j + 1) * block].any()]
+            for i in range(nb)]
+    assert block_lists(SLIDING, nb, sink_blocks=s, window_tokens=W, block=block) == want
+
+
+def test_sliding_window_reduces_to_library_attention():
+    """No sink and a window covering the sequence: causal attention.  Window
+    of 1: every token reads only itself (O = V).  A general band against SDPA
+    with the band built from torch's triangular masks."""
+    L, d = 48, 6
+    q, k, v = rand(1, 1, L, d), rand(1, 1, L, d), rand(1, 1, L, d)
+    pat = lambda s, W: dict(kind=SLIDING, block=8, sink_blocks=s, window_tokens=W)
+    o, _ = sparse_forward(q, k, v, pat(0, L), scale=0.4)
+    np.testing.assert_allclose(o[0, 0], sdpa(q[0, 0], k[0, 0], v[0, 0], is_causal=True, scale=0.4),
+                               atol=1e-12)
+    o, lse = sparse_forward(q, k, v, pat(0, 1), scale=0.4)
+    np.testing.assert_allclose(o[0, 0], v[0, 0], atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], 0.4 * np.einsum("id,id->i", q[0, 0], k[0, 0]), atol=1e-12)
+    ones = torch.ones(L, L, dtype=torch.bool)
+    band = (ones.tril(0) & ~ones.tril(-7)).numpy()          # q - 6 <= k <= q
+    band[:, :8] |= ones.tril(0).numpy()[:, :8]               # plus sink block 0
+    o, _ = sparse_forward(q, k, v, pat(1, 7), scale=0.4)
+    np.testing.assert_allclose(o[0, 0], sdpa(q[0, 0], k[0, 0], v[0, 0], attn_mask=band, scale=0.4),
+                               atol=1e-12)
+
+
+def test_sliding_zero_query_counts():
+    """Q = 0: LSE = ln(number of keys read) = ln(min(q + 1, W + sink keys
+    outside the window))."""
+    L, d, block, s, W = 120, 4, 8, 1, 13
+    q, k, v = np.zeros((1, 1, L, d)), rand(1, 1, L, d), rand(1, 1, L, d)
+    _, lse = sparse_forward(q, k, v, dict(kind=SLIDING, block=block, sink_blocks=s, window_tokens=W),
+                            scale=1.0)
+    for t in range(L):
+        n = min(t + 1, W) + max(0, min(block * s, t + 1 - W))
+        assert lse[0, 0, t] == pytest.approx(math.log(n), abs=1e-12)
+
+
+def test_sliding_prefill_row_equals_decode():
+    """With the token-granular window, prefill row t reads exactly the keys
+    decode of token t reads (sink tokens and the last W positions)."""
+    B, H, L, d = 1, 1, 160, 4
+    q, k, v = rand(B, H, L, d), rand(B, H, L, d), rand(B, H, L, d)
+    pat = dict(kind=SLIDING, block=16, sink_blocks=1, window_tokens=37)
+    rows = [0, 15, 16, 36, 37, 52, 53, 100, 159]
+    o, lse = sparse_forward(q, k, v, pat, scale=0.3, rows=rows)
+    for t in rows:
+        od, ld = decode_one(q[0, 0, t], k[0, 0], v[0, 0], decode_positions(t, 16, 37), 0.3)
+        np.testing.assert_allclose(od, o[0, 0, t], atol=1e-12)
+        assert ld == pytest.approx(lse[0, 0, t], abs=1e-12)
 
 
 @pytest.mark.parametrize("kind,s,w,stride,h", [(ATTNSINK, 1, 4, 0, 0), (ATTNSINK, 2, 3, 0, 0),
