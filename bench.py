@@ -19,7 +19,9 @@ kernel and the CPU oracle baseline are reported alongside.
 
 Other workloads (--workload): attnsink8k, blocksparse32k, blocksparse128k,
 attnsink128k, train64k (AttnSink forward + backward), blocksparse32k_train and
-blocksparse128k_train (BlockSparse forward + backward), bsdecode128k
+blocksparse128k_train (BlockSparse forward + backward), sliding128k and
+sliding64k_train (token-granular window of 4096 tokens + 1 sink block),
+bsdecode128k
 (BlockSparse decode against its compacted cache), and copy1g (a plain 1 GiB
 device copy, the calibration kernel for the HBM byte counters).
 """
@@ -396,6 +398,10 @@ def make_workload(name):
         return Prefill(name, lcs.blocksparse_pattern(1, 16, 8), 32768, 3, backward=True)
     if name == "blocksparse128k_train":
         return Prefill(name, lcs.blocksparse_pattern(1, 16, 8), 131072, 3, backward=True)
+    if name == "sliding128k":
+        return Prefill(name, lcs.sliding_pattern(1, 4096), 131072, 7)
+    if name == "sliding64k_train":
+        return Prefill(name, lcs.sliding_pattern(1, 4096), 65536, 4, backward=True)
     if name == "bsdecode128k":
         return BsDecode128k()
     if name == "copy1g":

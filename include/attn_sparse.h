@@ -56,8 +56,17 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
 
 /* Pattern kinds.  Full: every key block up to the diagonal.  AttnSink: sink
  * blocks plus a window of the most recent blocks.  BlockSparse: AttnSink plus
- * strided earlier blocks whose phase depends on the head. */
-typedef enum { ATTN_FULL = 0, ATTN_ATTNSINK = 1, ATTN_BLOCKSPARSE = 2 } attn_kind_t;
+ * strided earlier blocks whose phase depends on the head.  Sliding: a
+ * token-granular window of the most recent window_tokens tokens (window
+ * attention over recent tokens, LongGen's sparse-pattern family: mlsanity
+ * index page "A Little Goes a Long Way...", "Abstract (arXiv)"), plus
+ * optional sink blocks; sink_blocks = 0 is plain sliding-window attention. */
+typedef enum {
+  ATTN_FULL = 0,
+  ATTN_ATTNSINK = 1,
+  ATTN_BLOCKSPARSE = 2,
+  ATTN_SLIDING = 3
+} attn_kind_t;
 
 /* Operation ids for attn_workspace_bytes. */
 typedef enum {
@@ -69,20 +78,28 @@ typedef enum {
 } attn_op_t;
 
 /* Static pattern description (host struct, passed by pointer).
- * Query block i (tokens 64i..64i+63) reads key block j when
+ * AttnSink / BlockSparse: query block i (tokens 64i..64i+63) reads key
+ * block j when
  *   j <  sink_blocks and j <= i                              (sink)
  *   i - local_blocks < j <= i                                (window; it
  *                                                             holds the diagonal)
  *   kind == BLOCKSPARSE, j < i and (j + h) % stride == 0     (strided; h = head)
  * Full ignores the other fields and reads every j <= i.  With causal != 0,
- * keys later than the query token are masked inside any block. */
+ * keys later than the query token are masked inside any block.
+ * Sliding (causal must be 1): query token q reads key token k when k <= q
+ * and (k < 64 sink_blocks or q - k < window_tokens) -- the same keys decode
+ * of token q reads from a sink + window ring (attn_sparse_decode with
+ * sink_tokens = 64 sink_blocks, window_tokens = window_tokens).  Its block
+ * lists hold every block with such a key; the kernels mask keys outside
+ * the window inside its edge blocks. */
 typedef struct {
-  int32_t kind;         /* attn_kind_t                                       */
-  int32_t block;        /* tokens per block; must be 64                      */
-  int32_t sink_blocks;  /* >= 0                                              */
-  int32_t local_blocks; /* >= 1 for AttnSink / BlockSparse                   */
-  int32_t stride;       /* BlockSparse: >= 1; otherwise ignored              */
-  int32_t causal;       /* 1: mask key position > query position             */
+  int32_t kind;          /* attn_kind_t                                      */
+  int32_t block;         /* tokens per block; must be 64                     */
+  int32_t sink_blocks;   /* >= 0                                             */
+  int32_t local_blocks;  /* >= 1 for AttnSink / BlockSparse; else ignored    */
+  int32_t stride;        /* BlockSparse: >= 1; otherwise ignored             */
+  int32_t causal;        /* 1: mask key position > query position            */
+  int32_t window_tokens; /* Sliding: >= 1; otherwise ignored                 */
 } attn_pattern_t;
 
 /* Block index in CSR form (and its transpose, CSC, for the backward pass).
@@ -128,9 +145,10 @@ attn_status_t attn_index_build(const attn_pattern_t *pattern, int32_t n_heads,
  * DuoAttention on the Hugging Face paper-search page "long-context decoding
  * latency"): head h's rows follow patterns[h] with stride phase h.
  * patterns: n_heads host structs that share `block` and `causal` (a launch
- * applies both to every head); otherwise ATTN_ERR_INVALID_ARG.  Buffers and
- * the NULL-CSC rule as for attn_index_build.  Pass any of the patterns to the
- * device ops: they read only its block and causal fields. */
+ * applies both to every head) and are not ATTN_SLIDING (whose token window
+ * a launch would apply to every head); otherwise ATTN_ERR_INVALID_ARG.
+ * Buffers and the NULL-CSC rule as for attn_index_build.  Pass any of the
+ * patterns to the device ops: they read only its block and causal fields. */
 attn_status_t attn_index_nnz_mixed(const attn_pattern_t *patterns, int32_t n_heads,
                                    int64_t L, int64_t *nnz_out);
 attn_status_t attn_index_build_mixed(const attn_pattern_t *patterns, int32_t n_heads,
@@ -164,6 +182,10 @@ size_t attn_workspace_bytes(int32_t op, attn_dtype_t dtype, int32_t B,
  *   dtype: ATTN_BF16 (q/k/v/o bf16, fp32 accumulation) or ATTN_F32 (all
  *          fp32).  d in {64, 128}.  pattern->block == 64, L % 64 == 0.
  *   dev_index: device CSR for L/64 query and key blocks (CSC unused).
+ *   pattern: its causal flag applies to every head; for kind ATTN_SLIDING
+ *   its token window (sink_blocks, window_tokens) also masks keys inside
+ *   the listed blocks of every head.  Sliding with causal == 0 is
+ *   ATTN_ERR_INVALID_ARG.
  *   q, k, v: [B,H,L,d] in; o: [B,H,L,d] out; lse: [B,H,L] fp32 out.
  *   Rows with no allowed key give O = 0, LSE = -inf.  No workspace. */
 attn_status_t attn_sparse_fwd(attn_dtype_t dtype, int32_t B, int32_t H,
@@ -181,6 +203,7 @@ attn_status_t attn_sparse_fwd(attn_dtype_t dtype, int32_t B, int32_t H,
  * dK = scale dS^T Q.
  *   dtype: ATTN_BF16 only; d in {64, 128}.
  *   dev_index: CSR and CSC (col_ptr/row_idx must be set).
+ *   pattern: as for attn_sparse_fwd (causal flag; Sliding token window).
  *   q, k, v, o, dout: [B,H,L,d] bf16 in; lse: [B,H,L] fp32 in (from the
  *   forward); dq, dk, dv: [B,H,L,d] bf16 out.
  *   workspace: attn_workspace_bytes(ATTN_OP_BWD, ...) = 2*B*H*L*4 bytes

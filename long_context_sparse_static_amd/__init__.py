@@ -39,6 +39,7 @@ ATTN_BF16 = 1
 ATTN_FULL = 0
 ATTN_ATTNSINK = 1
 ATTN_BLOCKSPARSE = 2
+ATTN_SLIDING = 3
 
 ATTN_OP_FWD = 0
 ATTN_OP_BWD = 1
@@ -67,7 +68,8 @@ class AttnError(RuntimeError):
 class attn_pattern_t(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("sink_blocks", ctypes.c_int32), ("local_blocks", ctypes.c_int32),
-                ("stride", ctypes.c_int32), ("causal", ctypes.c_int32)]
+                ("stride", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("window_tokens", ctypes.c_int32)]
 
 
 class attn_index_t(ctypes.Structure):
@@ -155,10 +157,11 @@ class Pattern:
     stride: int = 0
     causal: bool = True
     block: int = BLOCK
+    window_tokens: int = 0
 
     def c_struct(self) -> attn_pattern_t:
         return attn_pattern_t(self.kind, self.block, self.sink_blocks, self.local_blocks,
-                              self.stride, 1 if self.causal else 0)
+                              self.stride, 1 if self.causal else 0, self.window_tokens)
 
     @property
     def head_dependent(self) -> bool:
@@ -176,6 +179,13 @@ def attnsink_pattern(sink_blocks: int, local_blocks: int, causal: bool = True) -
 def blocksparse_pattern(sink_blocks: int, local_blocks: int, stride: int,
                         causal: bool = True) -> Pattern:
     return Pattern(ATTN_BLOCKSPARSE, sink_blocks, local_blocks, stride, causal)
+
+
+def sliding_pattern(sink_blocks: int, window_tokens: int) -> Pattern:
+    """Token-granular window of ``window_tokens`` tokens (the query and the
+    window_tokens - 1 before it) plus ``sink_blocks`` sink blocks; 0 sink
+    blocks is plain sliding-window attention."""
+    return Pattern(ATTN_SLIDING, sink_blocks, 0, 0, True, window_tokens=window_tokens)
 
 
 def attn_index_nnz(pattern: Pattern, n_heads: int, L: int) -> int:

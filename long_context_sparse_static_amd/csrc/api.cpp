@@ -37,6 +37,8 @@ bool prefill_dims_ok(int32_t B, int32_t H, int64_t L, int32_t d, float scale,
                      const attn_pattern_t *p) {
   if (B < 1 || H < 1 || L < attn::kBlock || L % attn::kBlock != 0) return false;
   if (!p || p->block != attn::kBlock) return false;
+  if (p->kind == ATTN_SLIDING && (p->window_tokens < 1 || p->sink_blocks < 0 || !p->causal))
+    return false;
   if (!(scale > 0.f) || !isfinite(scale)) return false;
   // int32 token / tile arithmetic inside the kernels
   if ((int64_t)B * H * L > INT32_MAX) return false;
@@ -45,6 +47,13 @@ bool prefill_dims_ok(int32_t B, int32_t H, int64_t L, int32_t d, float scale,
 }
 
 attn_status_t hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+// Token window of a Sliding pattern (window 0: none).
+void window_of(const attn_pattern_t *p, int32_t *window, int32_t *sink_blk) {
+  const bool sl = p->kind == ATTN_SLIDING;
+  *window = sl ? p->window_tokens : 0;
+  *sink_blk = sl ? p->sink_blocks : 0;
+}
 
 size_t decode_ws_bytes(int32_t B, int32_t H, int64_t n_keys, int32_t d) {
   int32_t ns = 0, len = 0;
@@ -97,6 +106,7 @@ attn_status_t attn_sparse_fwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t 
   a.d = d;
   a.scale = scale;
   a.causal = pattern->causal ? 1 : 0;
+  window_of(pattern, &a.window, &a.sink_blk);
   hipStream_t s = (hipStream_t)stream;
   return hip_status(dtype == ATTN_BF16 ? attn::launch_fwd_bf16(a, s) : attn::launch_fwd_f32(a, s));
 }
@@ -135,6 +145,7 @@ attn_status_t attn_sparse_bwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t 
   a.d = d;
   a.scale = scale;
   a.causal = pattern->causal ? 1 : 0;
+  window_of(pattern, &a.window, &a.sink_blk);
   // Work grouping only (any grouping gives the same result): a per-head
   // BlockSparse index groups each head's strided key blocks together.
   a.kgroup = pattern->kind == ATTN_BLOCKSPARSE && dev_index->n_heads == H && pattern->stride >= 2 &&

@@ -10,7 +10,9 @@
 // Each row is generated directly in ascending order as
 //   sink blocks [0, min(sink, i+1))
 //   strided blocks in [sink, a) with (j + h) % stride == 0   (BlockSparse)
-//   window blocks [max(a, sink), i]          with a = max(0, i - local + 1)
+//   window blocks [max(a, sink), i]          with a = max(0, i - local + 1),
+//                                            Sliding: a = the block of token
+//                                            64 i - window + 1 (clamped at 0)
 // which is a disjoint, sorted partition of the set the header defines.
 
 #include <stdint.h>
@@ -27,6 +29,7 @@ bool pattern_ok(const attn_pattern_t *p, int64_t L) {
   if (!p || p->block <= 0 || L <= 0 || L % p->block != 0) return false;
   if (L / p->block > INT32_MAX - 1) return false;
   if (p->kind == ATTN_FULL) return true;
+  if (p->kind == ATTN_SLIDING) return p->sink_blocks >= 0 && p->window_tokens >= 1 && p->causal;
   if (p->kind != ATTN_ATTNSINK && p->kind != ATTN_BLOCKSPARSE) return false;
   if (p->sink_blocks < 0 || p->local_blocks < 1) return false;
   if (p->kind == ATTN_BLOCKSPARSE && p->stride < 1) return false;
@@ -42,7 +45,14 @@ int64_t emit_row(const attn_pattern_t *p, int64_t i, int32_t h, Sink &&sink) {
     return n;
   }
   const int64_t s = p->sink_blocks;
-  const int64_t a = std::max<int64_t>(0, i - p->local_blocks + 1);
+  int64_t a;
+  if (p->kind == ATTN_SLIDING) {
+    // first key allowed for the block's first query: 64 i - window + 1
+    const int64_t k0 = i * p->block - p->window_tokens + 1;
+    a = k0 <= 0 ? 0 : k0 / p->block;
+  } else {
+    a = std::max<int64_t>(0, i - p->local_blocks + 1);
+  }
   const int64_t sink_end = std::min<int64_t>(s, i + 1);
   for (int64_t j = 0; j < sink_end; ++j) sink(j), ++n;
   if (p->kind == ATTN_BLOCKSPARSE) {
@@ -127,7 +137,7 @@ void build_lists(PatternOf &&pattern_of, int32_t n_heads, int64_t nb, int32_t *r
 bool mixed_ok(const attn_pattern_t *patterns, int32_t n_heads, int64_t L) {
   if (!patterns || n_heads < 1) return false;
   for (int32_t h = 0; h < n_heads; ++h) {
-    if (!pattern_ok(&patterns[h], L)) return false;
+    if (!pattern_ok(&patterns[h], L) || patterns[h].kind == ATTN_SLIDING) return false;
     if (patterns[h].block != patterns[0].block) return false;
     if ((patterns[h].causal != 0) != (patterns[0].causal != 0)) return false;
   }

@@ -148,7 +148,7 @@ struct BwdPos {
 //   S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - D), dQ^T += K^T dS^T
 // K is read as rows and transposed (kBothRead), V as rows.
 // ----------------------------------------------------------------------------
-template <int D>
+template <int D, bool WIN>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   using KT = SwzTile<D, kBothRead>;
   using VT = SwzTile<D, kRowRead>;
@@ -175,7 +175,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int my_r = wave >> 1;
   const int qb = tile * kBwdTB + my_r;
   const bool q_valid = qb < nqb;
-  const int q_tok = qb * kBlock + (wave & 1) * 32 + n;
+  const int q_wave = qb * kBlock + (wave & 1) * 32;  // first query of this wave
+  const int q_tok = q_wave + n;
   const size_t qrow = base + (size_t)q_tok * D;
 
   bf16x8 bq[KS], bdo[KS];
@@ -231,12 +232,16 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     const bool diag = a.causal && j >= qb;
     // key offset in the block = 32 t + 8 (r / 4) + 4 hh + r % 4
     const int lim = q_tok - j * kBlock - 4 * hh;
+    // token window: keys k <= q - window of blocks past the sink blocks
+    const bool wedge = WIN && j >= a.sink_blk && j * kBlock <= q_wave + 31 - a.window;
+    const int lo = lim - a.window;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(__builtin_fmaf(s[t][r], c, -lse2));
         if (diag && 32 * t + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
+        if (wedge && 32 * t + 8 * (r >> 2) + (r & 3) <= lo) p = 0.f;
         s[t][r] = p * (dp[t][r] - dlt);  // dS^T
       }
 #pragma unroll
@@ -295,7 +300,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 //   dV^T += dO^T P,  dK^T += Q^T dS
 // Q and dO are read as rows and transposed (kBothRead).
 // ----------------------------------------------------------------------------
-template <int D>
+template <int D, bool WIN>
 __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BwdArgs a) {
   using QT = SwzTile<D, kBothRead>;
   constexpr int KS = D / 16, MT = D / 32;
@@ -353,7 +358,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
   const int my_r = wave >> 1;
   const int kb = krows[my_r];
   const bool k_valid = kb >= 0;
-  const int k_tok = kb * kBlock + (wave & 1) * 32 + n;
+  const int k_wave = kb * kBlock + (wave & 1) * 32;  // first key of this wave
+  const int k_tok = k_wave + n;
   const size_t krow = base + (size_t)k_tok * D;
 
   bf16x8 bk[KS], bv[KS];
@@ -416,6 +422,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
     constexpr int NM = 8 * KS;       // MFMAs per query block
     constexpr int PF = 4;            // operand prefetch distance
     const bool diag = a.causal && kb >= i;
+    // token window: queries q >= k + window, for keys past the sink blocks
+    const bool wedge = WIN && kb >= a.sink_blk && i * kBlock + 63 >= k_wave + a.window;
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
     bf16x8 bp[2][2], bds[2][2];
     float l2[16], dl[16];
@@ -461,6 +469,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
       const int lim = k_tok - i * kBlock - 32 * m - 4 * hh;
       float p = fast_exp2(__builtin_fmaf(s[m][r], c, -l2[r]));
       if (diag && 8 * (r >> 2) + (r & 3) < lim) p = 0.f;
+      if (wedge && 8 * (r >> 2) + (r & 3) >= lim + a.window) p = 0.f;
       s[m][r] = p;
       dp[m][r] = p * (dp[m][r] - dl[r]);
       if (r == 7 || r == 15) {
@@ -530,7 +539,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
-template <int D>
+template <int D, bool WIN>
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const size_t rows = (size_t)a.B * a.H * a.L;
   const int rpb = 256 / (D / 8);
@@ -540,15 +549,15 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const int BH = a.B * a.H;
   const size_t dyn_k = RowsBitmap<kBwdTB>::lds_bytes(a.ix.n_qblocks);
   const size_t dyn_q = RowsBitmap<kBwdTB>::lds_bytes(a.ix.n_kblocks);
-  hipError_t e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel<D>,
+  hipError_t e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel<D, WIN>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_k);
   if (e == hipSuccess)
-    e = hipFuncSetAttribute((const void *)bwd_dq_kernel<D>,
+    e = hipFuncSetAttribute((const void *)bwd_dq_kernel<D, WIN>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_q);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3(grid_delta), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(BH * k_tiles), dim3(kBwdThreads), dyn_k, s, a);
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(BH * q_tiles), dim3(kBwdThreads), dyn_q, s, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, WIN>), dim3(BH * k_tiles), dim3(kBwdThreads), dyn_k, s, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, WIN>), dim3(BH * q_tiles), dim3(kBwdThreads), dyn_q, s, a);
   return hipGetLastError();
 }
 
@@ -561,7 +570,8 @@ size_t bwd_bf16_lds_bytes(int d, int n_blocks) {
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s) {
-  return a.d == 128 ? launch_bwd<128>(a, s) : launch_bwd<64>(a, s);
+  if (a.window > 0) return a.d == 128 ? launch_bwd<128, true>(a, s) : launch_bwd<64, true>(a, s);
+  return a.d == 128 ? launch_bwd<128, false>(a, s) : launch_bwd<64, false>(a, s);
 }
 
 }  // namespace attn

@@ -80,7 +80,7 @@ struct WalkPos {
   uint32_t mask;  // bit r: listed by query block r of the workgroup
 };
 
-template <int D>
+template <int D, bool WIN>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   using Lay = FwdLayout<D>;
   constexpr int KS = D / 16;   // k-steps of S^T = K Q^T
@@ -117,7 +117,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int my_r = 2 * grp + ((wave >> 1) & 1);
   const int qb = tile * kFwdQB + my_r;
   const bool q_valid = qb < nqb;
-  const int q_tok = qb * kBlock + (wave & 1) * 32 + n;
+  const int q_wave = qb * kBlock + (wave & 1) * 32;  // first query of this wave
+  const int q_tok = q_wave + n;
 
   // Q^T operand of S^T = K Q^T: lane holds query n, d = 16 ks + 8 hh .. +7.
   bf16x8 bq[KS];
@@ -221,6 +222,18 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (32 * t + 8 * (r >> 2) + (r & 3) > lim) sc[t][r] = -INFINITY;
+    }
+    if constexpr (WIN) {
+      // token window: keys k <= q - window of blocks past the sink blocks
+      // (only blocks holding such a key for one of this wave's queries)
+      if (j >= a.sink_blk && j * kBlock <= q_wave + 31 - a.window) {
+        const int lo = q_tok - a.window - j * kBlock - 4 * hh;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * t + 8 * (r >> 2) + (r & 3) <= lo) sc[t][r] = -INFINITY;
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -370,15 +383,15 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     a.lse[(size_t)bh * a.L + q_tok] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
 }
 
-template <int D>
+template <int D, bool WIN>
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
   const int n_tiles = (a.ix.n_qblocks + kFwdQB - 1) / kFwdQB;
   const int grid = a.B * a.H * n_tiles;
   const size_t dyn = RowsBitmap<kFwdQB>::lds_bytes(a.ix.n_kblocks);
-  hipError_t e = hipFuncSetAttribute((const void *)fwd_bf16_kernel<D>,
+  hipError_t e = hipFuncSetAttribute((const void *)fwd_bf16_kernel<D, WIN>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(grid), dim3(kFwdThreads), dyn, s, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, WIN>), dim3(grid), dim3(kFwdThreads), dyn, s, a);
   return hipGetLastError();
 }
 
@@ -390,7 +403,8 @@ size_t fwd_bf16_lds_bytes(int d, int n_kblocks) {
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s) {
-  return a.d == 128 ? launch_fwd<128>(a, s) : launch_fwd<64>(a, s);
+  if (a.window > 0) return a.d == 128 ? launch_fwd<128, true>(a, s) : launch_fwd<64, true>(a, s);
+  return a.d == 128 ? launch_fwd<128, false>(a, s) : launch_fwd<64, false>(a, s);
 }
 
 }  // namespace attn

@@ -65,6 +65,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
       acc += __shfl_xor(acc, 2);
       acc *= a.scale;
       if (a.causal && j * kBlock + kk > q_tok) acc = -INFINITY;
+      if (a.window > 0 && j >= a.sink_blk && j * kBlock + kk <= q_tok - a.window) acc = -INFINITY;
       s[kk] = acc;
       mx = fmaxf(mx, acc);
     }

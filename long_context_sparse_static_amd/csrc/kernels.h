@@ -30,6 +30,9 @@ struct FwdArgs {
   int32_t B, H, L, d;
   float scale;
   int32_t causal;
+  // Token window (Sliding patterns; window 0: none): key k of a block
+  // j >= sink_blk is masked for query q when k <= q - window.
+  int32_t window, sink_blk;
 };
 
 struct BwdArgs {
@@ -42,6 +45,7 @@ struct BwdArgs {
   int32_t B, H, L, d;
   float scale;
   int32_t causal;
+  int32_t window, sink_blk;  // token window, as in FwdArgs
   int32_t kgroup;      // dK/dV key-block grouping: 1, or the BlockSparse stride
 };
 

@@ -9,20 +9,22 @@ import numpy as np
 import torch
 
 import long_context_sparse_static_amd as lcs
-from oracle import (attention_backward, attention_forward, dense_token_mask,
-                    pattern_lists_for_head, transpose_lists)
+from oracle import (attention_backward, attention_forward, pattern_lists_for_head,
+                    pattern_token_mask, transpose_lists)
 from synth_inputs import as_f64
 
 # bf16 path: max-abs 2e-2 and mean-abs 2e-3; fp32 path: max-abs 1e-5.
 BF16_MAX, BF16_MEAN = 2e-2, 2e-3
 F32_MAX = 1e-5
 
-ORACLE_KIND = {lcs.ATTN_FULL: "full", lcs.ATTN_ATTNSINK: "attnsink", lcs.ATTN_BLOCKSPARSE: "blocksparse"}
+ORACLE_KIND = {lcs.ATTN_FULL: "full", lcs.ATTN_ATTNSINK: "attnsink", lcs.ATTN_BLOCKSPARSE: "blocksparse",
+               lcs.ATTN_SLIDING: "sliding"}
 
 
 def oracle_pattern(p: "lcs.Pattern") -> dict:
     return dict(kind=ORACLE_KIND[p.kind], block=p.block, sink_blocks=p.sink_blocks,
-                local_blocks=p.local_blocks, stride=p.stride, causal=p.causal)
+                local_blocks=p.local_blocks, stride=p.stride, causal=p.causal,
+                window_tokens=p.window_tokens)
 
 
 def errors(got, want):
@@ -63,7 +65,7 @@ def sample_rows_forward(q, k, v, pattern, head, b, rows, scale=None):
     rows = np.asarray(sorted(rows))
     kblocks = sorted({j for r in rows for j in lists[r // pattern.block]})
     keys = np.concatenate([np.arange(j * pattern.block, (j + 1) * pattern.block) for j in kblocks])
-    mask = dense_token_mask(lists, pattern.block, L, L, pattern.causal, rows=rows)[:, keys]
+    mask = pattern_token_mask(oracle_pattern(pattern), head, L, rows=rows)[:, keys]
     qh = as_f64(q[b, head, torch.as_tensor(rows, device=q.device)])
     kh = as_f64(k[b, head, torch.as_tensor(keys, device=k.device)])
     vh = as_f64(v[b, head, torch.as_tensor(keys, device=v.device)])
@@ -89,7 +91,7 @@ def sample_backward(q, k, v, do, pattern, head, b, qblocks, kblocks, scale=None)
     def sub(i):
         if i not in cache:
             rows, keys = tok([i]), tok(lists[i])
-            mask = dense_token_mask(lists, B_, L, L, pattern.causal, rows=rows)[:, keys]
+            mask = pattern_token_mask(oracle_pattern(pattern), head, L, rows=rows)[:, keys]
             cache[i] = attention_backward(qh[rows], kh[keys], vh[keys], doh[rows], mask, scale)[:3]
         return cache[i]
 

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import long_context_sparse_static_amd as lcs
-from oracle import ATTNSINK, BLOCKSPARSE, FULL, block_lists, transpose_lists
+from oracle import ATTNSINK, BLOCKSPARSE, FULL, SLIDING, block_lists, transpose_lists
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn_sparse.h")
@@ -53,6 +53,11 @@ PATTERNS = {
     "full_32k": (lcs.full_pattern(), FULL, dict(), 1, 32768),
     "odd_sink2": (lcs.attnsink_pattern(2, 3), ATTNSINK, dict(sink_blocks=2, local_blocks=3), 1, 64 * 37),
     "odd_bs": (lcs.blocksparse_pattern(3, 5, 7), BLOCKSPARSE, dict(sink_blocks=3, local_blocks=5, stride=7), 9, 64 * 50),
+    "sliding_4096_sink1": (lcs.sliding_pattern(1, 4096), SLIDING, dict(sink_blocks=1, window_tokens=4096), 1, 65536),
+    "sliding_1000": (lcs.sliding_pattern(0, 1000), SLIDING, dict(sink_blocks=0, window_tokens=1000), 1, 64 * 40),
+    "sliding_1": (lcs.sliding_pattern(0, 1), SLIDING, dict(sink_blocks=0, window_tokens=1), 1, 64 * 9),
+    "sliding_65_sink2": (lcs.sliding_pattern(2, 65), SLIDING, dict(sink_blocks=2, window_tokens=65), 1, 64 * 21),
+    "sliding_wide": (lcs.sliding_pattern(1, 10 ** 6), SLIDING, dict(sink_blocks=1, window_tokens=10 ** 6), 1, 64 * 13),
 }
 
 
@@ -111,6 +116,16 @@ def test_mixed_index_rejects_inconsistent_heads():
         lcs.attn_index_nnz_mixed([lcs.full_pattern(), lcs.Pattern(7)], L)  # unknown kind
     with pytest.raises(lcs.AttnError):
         lcs.attn_index_nnz_mixed([lcs.full_pattern()], 1000)              # L % 64
+    with pytest.raises(lcs.AttnError):                                    # one token window per launch
+        lcs.attn_index_nnz_mixed([lcs.full_pattern(), lcs.sliding_pattern(1, 100)], L)
+
+
+def test_sliding_pattern_rejections():
+    L = 64 * 8
+    for bad in (lcs.sliding_pattern(1, 0), lcs.sliding_pattern(-1, 64),
+                lcs.Pattern(lcs.ATTN_SLIDING, 1, 0, 0, False, window_tokens=64)):
+        with pytest.raises(lcs.AttnError):
+            lcs.attn_index_nnz(bad, 1, L)
 
 
 def test_index_nnz_closed_forms():
