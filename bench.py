@@ -22,7 +22,8 @@ attnsink128k, train64k (AttnSink forward + backward), blocksparse32k_train and
 blocksparse128k_train (BlockSparse forward + backward), sliding128k and
 sliding64k_train (token-granular window of 4096 tokens + 1 sink block),
 bsdecode128k
-(BlockSparse decode against its compacted cache), and copy1g (a plain 1 GiB
+(BlockSparse decode against its compacted cache), pageddecode128k (full-layer
+decode against 64-token pages named by a block table), and copy1g (a plain 1 GiB
 device copy, the calibration kernel for the HBM byte counters).
 """
 
@@ -381,6 +382,54 @@ class BsDecode128k:
                                 parallelism="single GPU", layer_caches=len(self.caches)))
 
 
+class PagedDecode128k:
+    """Full-layer decode of 16 sequences at t = 131072 against paged caches:
+    pools of 16 x 2049 64-token pages in shuffled order, cycled over two
+    distinct pools so that no read hits the 256 MB MALL."""
+    name = "pageddecode128k"
+
+    def __init__(self, n_pools=2):
+        dev = torch.device("cuda")
+        B = DEC_BATCH
+        self.t = 131072
+        self.max_pages = self.t // BLK + 1
+        n_pages = B * self.max_pages
+        g = torch.Generator().manual_seed(seed_for(8, 0, "cache"))
+        self.table = torch.randperm(n_pages, generator=g).to(torch.int32).reshape(B, self.max_pages).to(dev)
+        self.pos = torch.full((B,), self.t, dtype=torch.int64, device=dev)
+        self.q = fill_randn((B, H, 1, D), seed_for(8, 0, "q_dec"))
+        self.k_new = fill_randn((B, H, 1, D), seed_for(8, 0, "k_new"))
+        self.v_new = fill_randn((B, H, 1, D), seed_for(8, 0, "v_new"))
+        self.pools = [(fill_randn((n_pages, H, BLK, D), seed_for(8, 10 + i, "cache")),
+                       fill_randn((n_pages, H, BLK, D), seed_for(8, 10 + i, "cache_v")))
+                      for i in range(n_pools)]
+        self.o = torch.empty((B, H, 1, D), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(lcs.attn_workspace_bytes(lcs.ATTN_OP_FULL_DECODE, lcs.ATTN_BF16, B, H,
+                                                       self.t + 1, D), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, timer):
+        for kp, vp in self.pools:
+            with timer.span("decode_paged"):
+                lcs.attn_paged_decode(self.q, self.k_new, self.v_new, kp, vp, self.table, self.pos,
+                                      max_pos=self.t, o=self.o, lse=self.lse, workspace=self.ws)
+
+    def report(self, times, steps):
+        t = sum(times["decode_paged"]) / len(times["decode_paged"])
+        nbytes = DEC_BATCH * H * (self.t + 1) * 2 * D * 2
+        gbps = nbytes / (t * 1e-3) / 1e9
+        return dict(value=DEC_BATCH / (t * 1e-3), unit="tok/s (one layer)",
+                    extra=dict(layer_ms=t, layer_gbps=gbps, attended_bytes=nbytes),
+                    roofline=dict(bound="hbm", kernel="decode_split_kernel (paged) + decode_combine_kernel",
+                                  achieved=gbps, peak=PEAK_HBM_GBPS, unit="GB/s", frac=gbps / PEAK_HBM_GBPS,
+                                  traffic=None),
+                    config=dict(workload="pageddecode128k: full-layer decode of 16 seqs at t=131072, "
+                                "H=32 d=128 bf16, 64-token pages in shuffled order",
+                                global_batch=DEC_BATCH, seq_len=self.t, parallelism="single GPU",
+                                pools=len(self.pools)))
+
+
 def make_workload(name):
     if name == "hybrid128k":
         return Hybrid128k()
@@ -404,6 +453,8 @@ def make_workload(name):
         return Prefill(name, lcs.sliding_pattern(1, 4096), 65536, 4, backward=True)
     if name == "bsdecode128k":
         return BsDecode128k()
+    if name == "pageddecode128k":
+        return PagedDecode128k()
     if name == "copy1g":
         return Copy1G()
     raise SystemExit(f"unknown workload {name}")

@@ -254,6 +254,49 @@ attn_status_t attn_full_decode(attn_dtype_t dtype, int32_t B, int32_t H,
                                void *o, float *lse, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* Decode one new token per sequence in a full-attention layer whose cache
+ * is paged: a pool of 64-token pages shared by the batch, each sequence
+ * naming its pages in a block table (the block-table KV cache of
+ * PagedAttention, listed among LongGen's foundations on the mlsanity index
+ * page, "Builds on"; LongGen is served with vLLM: atlas.scime.ai summary,
+ * "Approach").  No sequence needs a contiguous [capacity] slab.
+ *   k_pages, v_pages: [n_pages, H, 64, d] device pools; token p of
+ *   sequence b lives in page dev_block_table[b * max_pages + p / 64], row
+ *   p % 64 (all heads of a token share the page id).
+ *   dev_block_table: [B, max_pages] int32 device.  The caller allocates
+ *   pages; the entry for the new token's block must be set before the call.
+ *   dev_pos, k_new, v_new, q, o, lse: as for attn_full_decode (k_new / v_new
+ *   are written to the new token's page row, q attends to tokens 0..t).
+ *   max_pos: host upper bound on every t, < 64 * max_pages.
+ *   A position outside [0, max_pos] or a page id outside [0, n_pages) in
+ *   any block 0 .. t / 64 of a sequence gives that sequence o = 0, lse = NaN
+ *   (such pages are never read or written).
+ *   dtype: ATTN_BF16; d in {64, 128}.
+ *   workspace: attn_workspace_bytes(ATTN_OP_FULL_DECODE, ..., max_pos+1, d). */
+attn_status_t attn_paged_decode(attn_dtype_t dtype, int32_t B, int32_t H,
+                                int32_t d, float scale, int32_t n_pages,
+                                int32_t max_pages,
+                                const int32_t *dev_block_table,
+                                int64_t max_pos, const int64_t *dev_pos,
+                                const void *q, const void *k_new,
+                                const void *v_new, void *k_pages,
+                                void *v_pages, void *o, float *lse,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/* Copies prefill K/V into a page pool: tokens 0 .. min(len[b], src_len,
+ * 64 max_pages) - 1 of sequence b go to the pages its block table names
+ * (entries outside [0, n_pages) are skipped).
+ *   k_src, v_src: [B,H,src_len,d] bf16 device; dev_len: [B] int64 device.
+ *   Pools and table as for attn_paged_decode.  dtype: ATTN_BF16. */
+attn_status_t attn_paged_cache_fill(attn_dtype_t dtype, int32_t B, int32_t H,
+                                    int32_t d, int32_t n_pages,
+                                    int32_t max_pages,
+                                    const int32_t *dev_block_table,
+                                    const int64_t *dev_len, const void *k_src,
+                                    const void *v_src, int64_t src_len,
+                                    void *k_pages, void *v_pages, void *stream);
+
 /* Decode one new token per sequence in a BlockSparse layer against its
  * compacted cache (the block-wise sparse layers of LongGen: mlsanity index
  * page, "Abstract (arXiv)"; their reduced KV cache: atlas.scime.ai summary,

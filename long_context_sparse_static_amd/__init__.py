@@ -55,7 +55,7 @@ EXPORTED = (
     "attn_index_build_mixed", "attn_index_validate",
     "attn_layer_map", "attn_workspace_bytes", "attn_sparse_fwd", "attn_sparse_bwd",
     "attn_sparse_decode", "attn_full_decode", "attn_ring_fill", "attn_blocksparse_decode",
-    "attn_blocksparse_cache_fill",
+    "attn_blocksparse_cache_fill", "attn_paged_decode", "attn_paged_cache_fill",
 )
 
 
@@ -132,6 +132,12 @@ def lib():
         L.attn_blocksparse_cache_fill.restype = i32
         L.attn_blocksparse_cache_fill.argtypes = [i32, i32, i32, i32, P(attn_pattern_t), i32, vp,
                                                   vp, vp, i64, vp, vp, vp]
+        L.attn_paged_decode.restype = i32
+        L.attn_paged_decode.argtypes = [i32, i32, i32, i32, f32, i32, i32, vp, i64, vp, vp, vp,
+                                        vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_paged_cache_fill.restype = i32
+        L.attn_paged_cache_fill.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, i64,
+                                            vp, vp, vp]
         _lib_handle = L
     return _lib_handle
 
@@ -457,6 +463,49 @@ def attn_full_decode(q, k_new, v_new, k_cache, v_cache, pos, max_pos: int, scale
                                   _stream()),
            "attn_full_decode")
     return o, lse
+
+
+def attn_paged_decode(q, k_new, v_new, k_pages, v_pages, block_table, pos, max_pos: int,
+                      scale=None, o=None, lse=None, workspace=None):
+    """Decode one token per sequence against a paged full cache: pools
+    [n_pages,H,64,d] and a block table [B,max_pages] int32."""
+    torch = _torch()
+    B, H, d, o, lse, ptrs = _decode_io(q, k_new, v_new, o, lse)
+    n_pages = k_pages.shape[0]
+    max_pages = block_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kp = _dev(k_pages, "k_pages", (n_pages, H, BLOCK, d), q.dtype, q.device)
+    vp = _dev(v_pages, "v_pages", (n_pages, H, BLOCK, d), q.dtype, q.device)
+    tp = _dev(block_table, "block_table", (B, max_pages), torch.int32, q.device)
+    pp = _dev(pos, "pos", (B,), torch.int64, q.device)
+    need = attn_workspace_bytes(ATTN_OP_FULL_DECODE, _dtype_code(q), B, H, max_pos + 1, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    wp = _dev(workspace, "workspace", device=q.device)
+    op = _dev(o, "o", q.shape, q.dtype, q.device)
+    lp = _dev(lse, "lse", (B, H), torch.float32, q.device)
+    _check(lib().attn_paged_decode(_dtype_code(q), B, H, d, scale, n_pages, max_pages, tp, max_pos,
+                                   pp, *ptrs, kp, vp, op, lp, wp,
+                                   workspace.numel() * workspace.element_size(), _stream()),
+           "attn_paged_decode")
+    return o, lse
+
+
+def attn_paged_cache_fill(k_src, v_src, lengths, k_pages, v_pages, block_table):
+    """Copies each sequence's prefill K/V [B,H,src_len,d] into its pages."""
+    torch = _torch()
+    B, H, src_len, d = k_src.shape
+    n_pages = k_pages.shape[0]
+    max_pages = block_table.shape[1]
+    ks = _dev(k_src, "k_src", dtype=torch.bfloat16)
+    vs = _dev(v_src, "v_src", k_src.shape, torch.bfloat16, k_src.device)
+    lp = _dev(lengths, "lengths", (B,), torch.int64, k_src.device)
+    kp = _dev(k_pages, "k_pages", (n_pages, H, BLOCK, d), torch.bfloat16, k_src.device)
+    vp = _dev(v_pages, "v_pages", (n_pages, H, BLOCK, d), torch.bfloat16, k_src.device)
+    tp = _dev(block_table, "block_table", (B, max_pages), torch.int32, k_src.device)
+    _check(lib().attn_paged_cache_fill(ATTN_BF16, B, H, d, n_pages, max_pages, tp, lp, ks, vs,
+                                       src_len, kp, vp, _stream()),
+           "attn_paged_cache_fill")
 
 
 def attn_ring_fill(k_src, v_src, lengths, k_cache, v_cache, sink_tokens: int, window_tokens: int):

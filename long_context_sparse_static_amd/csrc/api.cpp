@@ -56,9 +56,7 @@ void window_of(const attn_pattern_t *p, int32_t *window, int32_t *sink_blk) {
 }
 
 size_t decode_ws_bytes(int32_t B, int32_t H, int64_t n_keys, int32_t d) {
-  int32_t ns = 0, len = 0;
-  attn::decode_split_plan(B, H, n_keys, &ns, &len);
-  return (size_t)B * H * ns * (d + 2) * sizeof(float);
+  return (size_t)B * H * attn::decode_split_bound(B, H, n_keys) * (d + 2) * sizeof(float);
 }
 
 }  // namespace
@@ -160,11 +158,13 @@ static attn_status_t decode_common(attn_dtype_t dtype, int32_t B, int32_t H, int
                                    int64_t max_pos, const int64_t *dev_pos, const void *q,
                                    const void *k_new, const void *v_new, void *k_cache,
                                    void *v_cache, void *o, float *lse, void *workspace,
-                                   size_t workspace_bytes, void *stream) {
+                                   size_t workspace_bytes, void *stream,
+                                   const int32_t *table = nullptr, int32_t max_pages = 0,
+                                   int32_t n_pages = 0) {
   if (B < 1 || H < 1 || !(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_INVALID_ARG;
   if (!dev_pos || !q || !k_new || !v_new || !k_cache || !v_cache || !o || !lse)
     return ATTN_ERR_INVALID_ARG;
-  if ((int64_t)B * H > INT32_MAX / 4) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * H > 65535) return ATTN_ERR_INVALID_ARG;  // grid.y limit
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   const int64_t n_keys = sink >= 0 ? cap : max_pos + 1;
@@ -190,6 +190,9 @@ static attn_status_t decode_common(attn_dtype_t dtype, int32_t B, int32_t H, int
   attn::decode_split_plan(B, H, n_keys, &a.n_split, &a.split_len);
   a.scale = scale;
   a.bs_sink = a.bs_local = a.bs_stride = a.bs_cap = 0;
+  a.table = table;
+  a.max_pages = max_pages;
+  a.n_pages = n_pages;
   return hip_status(attn::launch_decode_bf16(a, (hipStream_t)stream));
 }
 
@@ -231,6 +234,48 @@ attn_status_t attn_full_decode(attn_dtype_t dtype, int32_t B, int32_t H, int32_t
                        k_cache, v_cache, o, lse, workspace, workspace_bytes, stream);
 }
 
+attn_status_t attn_paged_decode(attn_dtype_t dtype, int32_t B, int32_t H, int32_t d, float scale,
+                                int32_t n_pages, int32_t max_pages,
+                                const int32_t *dev_block_table, int64_t max_pos,
+                                const int64_t *dev_pos, const void *q, const void *k_new,
+                                const void *v_new, void *k_pages, void *v_pages, void *o,
+                                float *lse, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  if (n_pages < 1 || max_pages < 1 || !dev_block_table) return ATTN_ERR_INVALID_ARG;
+  if (max_pos < 0 || max_pos >= (int64_t)max_pages * attn::kBlock) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * max_pages > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  return decode_common(dtype, B, H, d, scale, (int64_t)max_pages * attn::kBlock, -1, 0, max_pos,
+                       dev_pos, q, k_new, v_new, k_pages, v_pages, o, lse, workspace,
+                       workspace_bytes, stream, dev_block_table, max_pages, n_pages);
+}
+
+attn_status_t attn_paged_cache_fill(attn_dtype_t dtype, int32_t B, int32_t H, int32_t d,
+                                    int32_t n_pages, int32_t max_pages,
+                                    const int32_t *dev_block_table, const int64_t *dev_len,
+                                    const void *k_src, const void *v_src, int64_t src_len,
+                                    void *k_pages, void *v_pages, void *stream) {
+  if (B < 1 || H < 1 || n_pages < 1 || max_pages < 1 || src_len < 0) return ATTN_ERR_INVALID_ARG;
+  if (!dev_block_table || !dev_len || !k_src || !v_src || !k_pages || !v_pages)
+    return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * H > 65535 || (int64_t)B * max_pages > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  attn::PagedFillArgs a;
+  a.k_src = k_src;
+  a.v_src = v_src;
+  a.k_pages = k_pages;
+  a.v_pages = v_pages;
+  a.table = dev_block_table;
+  a.len = dev_len;
+  a.src_len = src_len;
+  a.B = B;
+  a.H = H;
+  a.d = d;
+  a.max_pages = max_pages;
+  a.n_pages = n_pages;
+  return hip_status(attn::launch_paged_fill_bf16(a, (hipStream_t)stream));
+}
+
 attn_status_t attn_blocksparse_decode(attn_dtype_t dtype, int32_t B, int32_t H, int32_t d,
                                       float scale, const attn_pattern_t *pattern,
                                       int32_t strided_blocks, const int64_t *dev_pos,
@@ -270,6 +315,8 @@ attn_status_t attn_blocksparse_decode(attn_dtype_t dtype, int32_t B, int32_t H, 
   a.bs_local = pattern->local_blocks;
   a.bs_stride = pattern->stride;
   a.bs_cap = strided_blocks;
+  a.table = nullptr;
+  a.max_pages = a.n_pages = 0;
   return hip_status(attn::launch_decode_bf16(a, (hipStream_t)stream));
 }
 

@@ -15,8 +15,15 @@
 //                        so no ordering between them is needed).
 //   decode_combine_kernel grid (B*H): merges the partials, writes o and lse.
 //   ring_fill_kernel     copies prefill K/V into the sink + window ring.
+//   paged_fill_kernel    copies prefill K/V into the pages of a block table.
 //
 // Ring slot of token p: p if p < sink, else sink + (p - sink) % window.
+// Paged full layers (a block-table cache in the manner of PagedAttention,
+// listed among LongGen's foundations on the mlsanity index page, "Builds
+// on"; LongGen is served with vLLM: atlas.scime.ai summary, "Approach"): pools
+// [n_pages, H, 64, d], token p of sequence b in page table[b][p / 64] at
+// row p % 64; a page id outside [0, n_pages) reads nothing and makes the
+// result NaN.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -81,6 +88,12 @@ __device__ __forceinline__ bool decode_geometry(const DecodeArgs &a, int64_t t, 
     *slot_new = i < s ? t : 64 * s + 64 * (i % w) + (t & 63);
     return true;
   }
+  if (a.table) {
+    if (t < 0 || t > a.max_pos) return false;
+    *n_valid = t + 1;
+    *slot_new = t;
+    return true;
+  }
   if (a.sink >= 0) {
     if (t < 0) return false;
     const int64_t cap = (int64_t)a.sink + a.window;
@@ -114,7 +127,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
   const int64_t s0 = (int64_t)split * a.split_len;
   const int64_t s1 = ok ? (s0 + a.split_len < n_valid ? s0 + a.split_len : n_valid) : 0;
 
-  const size_t row0 = (size_t)bh * a.cap;
+  const bool paged = a.table != nullptr;
+  const int h = bh % a.H;
+  const int32_t *tab = paged ? a.table + (size_t)b * a.max_pages : nullptr;
+  // element offset of (page, h) and whether the page id is in range
+  auto page_base = [&](int64_t blk, bool &valid) -> size_t {
+    const int pg = tab[blk];
+    valid = pg >= 0 && pg < a.n_pages;
+    return ((size_t)(valid ? pg : 0) * a.H + h) * kBlock * D;
+  };
+  const size_t row0 = paged ? 0 : (size_t)bh * a.cap;
   const bf16 *kc = (const bf16 *)a.k_cache + row0 * D;
   const bf16 *vc = (const bf16 *)a.v_cache + row0 * D;
   const bf16 *kn = (const bf16 *)a.k_new + (size_t)bh * D;
@@ -122,10 +144,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
 
   // Append the new token (one workgroup per (b, h) owns its slot).
   if (ok && slot_new >= s0 && slot_new < s1 && threadIdx.x < LPK) {
-    *(u32x4 *)((bf16 *)a.k_cache + (row0 + slot_new) * D + threadIdx.x * 8) =
-        *(const u32x4 *)(kn + threadIdx.x * 8);
-    *(u32x4 *)((bf16 *)a.v_cache + (row0 + slot_new) * D + threadIdx.x * 8) =
-        *(const u32x4 *)(vn + threadIdx.x * 8);
+    bool valid = true;
+    const size_t dst = paged ? page_base(slot_new >> 6, valid) + (size_t)(slot_new & 63) * D
+                             : (row0 + slot_new) * D;
+    if (valid) {
+      *(u32x4 *)((bf16 *)a.k_cache + dst + threadIdx.x * 8) = *(const u32x4 *)(kn + threadIdx.x * 8);
+      *(u32x4 *)((bf16 *)a.v_cache + dst + threadIdx.x * 8) = *(const u32x4 *)(vn + threadIdx.x * 8);
+    }
   }
 
   const float cs = a.scale * kLog2e;
@@ -143,14 +168,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
   for (int i = 0; i < 8; ++i) o[i] = 0.f;
 
   constexpr int STEP = NWAVE * KPW * kDecUnroll;
+  static_assert(KPW * kDecUnroll <= kBlock && kBlock % (KPW * kDecUnroll) == 0,
+                "the keys of one wave iteration lie in one 64-token page");
   for (int64_t kb = s0 + (int64_t)wave * KPW * kDecUnroll; kb < s1; kb += STEP) {
     u32x4 kw[kDecUnroll], vw[kDecUnroll];
+    // paged: this iteration's keys (KPW * kDecUnroll aligned ones) share a
+    // page, looked up once per wave
+    bool pvalid = true;
+    const size_t pbase = paged ? page_base(__builtin_amdgcn_readfirstlane((int)(kb >> 6)), pvalid) : 0;
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
       const int64_t key = kb + u * KPW + g;
       const int64_t safe = key < s1 ? key : s0;
-      const bf16 *kp = safe == slot_new ? kn : kc + safe * D;
-      const bf16 *vp = safe == slot_new ? vn : vc + safe * D;
+      const size_t off = paged ? pbase + (size_t)(safe & 63) * D : (size_t)safe * D;
+      const bool use_new = safe == slot_new || !pvalid;
+      const bf16 *kp = use_new ? kn : kc + off;
+      const bf16 *vp = use_new ? vn : vc + off;
       kw[u] = __builtin_nontemporal_load((const u32x4 *)(kp + c * 8));
       vw[u] = __builtin_nontemporal_load((const u32x4 *)(vp + c * 8));
     }
@@ -167,7 +200,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
 #pragma unroll
       for (int off = 1; off < LPK; off <<= 1) acc += __shfl_xor(acc, off);
       const int64_t key = kb + u * KPW + g;
-      sc[u] = key < s1 && (!bs || bs_slot_valid(a, key, t)) ? acc : -INFINITY;
+      sc[u] = key < s1 && pvalid && (!bs || bs_slot_valid(a, key, t)) ? acc : -INFINITY;
       mx = fmaxf(mx, sc[u]);
     }
     if (mx == -INFINITY) continue;
@@ -236,7 +269,14 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const int dd = threadIdx.x;
   const float *part = a.part + (size_t)bh * a.n_split * (D + 2);
   int64_t n_valid = 0, slot_new = 0;
-  const bool ok = decode_geometry(a, a.pos[b], bh % a.H, &n_valid, &slot_new);
+  bool ok = decode_geometry(a, a.pos[b], bh % a.H, &n_valid, &slot_new);
+  if (a.table && ok) {
+    // every page the position reads must be in range, else the result is NaN
+    const int32_t *tab = a.table + (size_t)b * a.max_pages;
+    bool bad = false;
+    for (int64_t j = dd; j <= a.pos[b] >> 6; j += D) bad |= tab[j] < 0 || tab[j] >= a.n_pages;
+    ok = !__syncthreads_or(bad);
+  }
   const int used = ok ? (int)((n_valid + a.split_len - 1) / a.split_len) : 0;
   float mm = -INFINITY;
   for (int s = 0; s < used; ++s) mm = fmaxf(mm, part[(size_t)s * (D + 2) + D]);
@@ -344,6 +384,28 @@ __global__ __launch_bounds__(256) void bs_fill_kernel(BsFillArgs a) {
   *(u32x4 *)((bf16 *)a.v_cache + dst) = *(const u32x4 *)((const bf16 *)a.v_src + src);
 }
 
+// Copies tokens 0 .. min(len, src_len) - 1 of prefill K/V [B,H,src_len,D]
+// into the pages the block table names (pages with an id outside
+// [0, n_pages) are skipped).
+template <int D>
+__global__ __launch_bounds__(256) void paged_fill_kernel(PagedFillArgs a) {
+  constexpr int CPR = D / 8;
+  const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int64_t ci = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t n = a.len[b];
+  if (n > a.src_len) n = a.src_len;
+  if (n > (int64_t)a.max_pages * kBlock) n = (int64_t)a.max_pages * kBlock;
+  if (ci >= n * CPR) return;
+  const int64_t p = ci / CPR;
+  const int c = (int)(ci % CPR);
+  const int pg = a.table[(size_t)b * a.max_pages + (p >> 6)];
+  if (pg < 0 || pg >= a.n_pages) return;
+  const size_t src = ((size_t)bh * a.src_len + p) * D + c * 8;
+  const size_t dst = (((size_t)pg * a.H + h) * kBlock + (p & 63)) * D + c * 8;
+  *(u32x4 *)((bf16 *)a.k_pages + dst) = *(const u32x4 *)((const bf16 *)a.k_src + src);
+  *(u32x4 *)((bf16 *)a.v_pages + dst) = *(const u32x4 *)((const bf16 *)a.v_src + src);
+}
+
 }  // namespace
 
 void decode_split_plan(int32_t B, int32_t H, int64_t n_keys, int32_t *n_split, int32_t *split_len) {
@@ -358,6 +420,18 @@ void decode_split_plan(int32_t B, int32_t H, int64_t n_keys, int32_t *n_split, i
   if (ns < 1) ns = 1;
   *n_split = (int32_t)ns;
   *split_len = (int32_t)len;
+}
+
+int32_t decode_split_bound(int32_t B, int32_t H, int64_t n_keys) {
+  // decode_split_plan gives ceil(n / len) splits with len >= 512 and
+  // len >= ceil(n / want): at most min(want, ceil(n / 512)), which never
+  // decreases as n grows (so a workspace sized for a capacity fits every
+  // position below it).
+  const int64_t bh = (int64_t)B * H;
+  const int64_t want = (2048 + bh - 1) / bh;
+  int64_t ns = (n_keys + 511) / 512;
+  if (ns > want) ns = want;
+  return (int32_t)(ns < 1 ? 1 : ns);
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {
@@ -397,6 +471,18 @@ hipError_t launch_bs_fill_bf16(const BsFillArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(bs_fill_kernel<128>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(bs_fill_kernel<64>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_fill_bf16(const PagedFillArgs &a, hipStream_t s) {
+  int64_t n = a.src_len < (int64_t)a.max_pages * kBlock ? a.src_len : (int64_t)a.max_pages * kBlock;
+  const int64_t chunks = n * (a.d / 8);
+  if (chunks == 0) return hipSuccess;
+  dim3 grid((unsigned)((chunks + 255) / 256), a.B * a.H);
+  if (a.d == 128)
+    hipLaunchKernelGGL(paged_fill_kernel<128>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(paged_fill_kernel<64>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -66,6 +66,11 @@ struct DecodeArgs {
   // blocks, a ring of bs_local blocks and bs_cap strided blocks; sink and
   // window are unused then.
   int32_t bs_sink, bs_local, bs_stride, bs_cap;
+  // Paged full layers (table != nullptr): k_cache / v_cache are page pools
+  // [n_pages, H, 64, d]; logical block j of sequence b lives in page
+  // table[b * max_pages + j].  cap is unused then.
+  const int32_t *table;
+  int32_t max_pages, n_pages;
 };
 
 struct RingFillArgs {
@@ -94,6 +99,18 @@ struct BsFillArgs {
 };
 hipError_t launch_bs_fill_bf16(const BsFillArgs &a, hipStream_t s);
 
+// Fill of a page pool from prefill K/V [B,H,src_len,d]: tokens 0 .. len-1
+// of sequence b into the pages its block table names.
+struct PagedFillArgs {
+  const void *k_src, *v_src;
+  void *k_pages, *v_pages;
+  const int32_t *table;
+  const int64_t *len;
+  int64_t src_len;
+  int32_t B, H, d, max_pages, n_pages;
+};
+hipError_t launch_paged_fill_bf16(const PagedFillArgs &a, hipStream_t s);
+
 // LDS bytes one forward workgroup needs (static tiles + union bitmap).
 size_t fwd_bf16_lds_bytes(int d, int n_kblocks);
 size_t bwd_bf16_lds_bytes(int d, int n_blocks);  // the larger (dK/dV) backward kernel
@@ -102,5 +119,7 @@ constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024;
 // Split-KV sizing shared by the workspace query and the decode launcher.
 void decode_split_plan(int32_t B, int32_t H, int64_t n_keys, int32_t *n_split,
                        int32_t *split_len);
+// Upper bound of decode_split_plan's n_split over all key counts <= n_keys.
+int32_t decode_split_bound(int32_t B, int32_t H, int64_t n_keys);
 
 }  // namespace attn
