@@ -121,6 +121,21 @@ typedef struct {
   const int32_t *row_idx; /* [nnz] or NULL                                  */
 } attn_index_t;
 
+/* Element strides of a tensor indexed [b, h, l, e] whose d elements e of a
+ * token row are contiguous: element (b, h, l, e) sits at
+ *   b * batch + h * head + l * token + e   (in elements, not bytes).
+ * Contiguous [B,H,L,d] is {H*L*d, L*d, d}; [B,L,H,d] is {L*H*d, d, H*d}; the
+ * Q of a fused [B,L,3,H,d] projection is {3*L*H*d, d, 3*H*d} at offset 0
+ * (K at H*d, V at 2*H*d).  Strides must be >= 0 and whole 16-byte vectors
+ * (multiples of 8 bf16 / 4 fp32 elements), token <= INT32_MAX / 64, and the
+ * base pointer 16-byte aligned.  Outputs must not overlap each other or the
+ * inputs. */
+typedef struct {
+  int64_t batch;
+  int64_t head;
+  int64_t token;
+} attn_strides_t;
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *attn_status_str(attn_status_t status);
 
@@ -196,6 +211,22 @@ attn_status_t attn_sparse_fwd(attn_dtype_t dtype, int32_t B, int32_t H,
                               float *lse, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/* attn_sparse_fwd over tensors with explicit strides (attn_strides_t): for
+ * instance [B,L,H,d] activations, or Q/K/V read in place from a fused QKV
+ * projection.  LSE stays contiguous [B,H,L] fp32.  Same dtypes, patterns,
+ * index and errors as attn_sparse_fwd; invalid strides or misaligned
+ * pointers give ATTN_ERR_INVALID_ARG. */
+attn_status_t attn_sparse_fwd_strided(attn_dtype_t dtype, int32_t B, int32_t H,
+                                      int64_t L, int32_t d, float scale,
+                                      const attn_pattern_t *pattern,
+                                      const attn_index_t *dev_index,
+                                      const void *q, const attn_strides_t *q_strides,
+                                      const void *k, const attn_strides_t *k_strides,
+                                      const void *v, const attn_strides_t *v_strides,
+                                      void *o, const attn_strides_t *o_strides,
+                                      float *lse, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
 /* Backward of the prefill forward, for context-extension training (the
  * LongGen sparse layers are trained during length extension: mlsanity index
  * page, "Abstract (arXiv)").  With P the masked softmax and loss gradients
@@ -216,6 +247,23 @@ attn_status_t attn_sparse_bwd(attn_dtype_t dtype, int32_t B, int32_t H,
                               const float *lse, const void *dout, void *dq,
                               void *dk, void *dv, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/* attn_sparse_bwd over tensors with explicit strides (attn_strides_t), one
+ * stride set per tensor; LSE stays contiguous [B,H,L] fp32 and the
+ * workspace is as for attn_sparse_bwd.  Errors as attn_sparse_bwd, plus
+ * ATTN_ERR_INVALID_ARG for invalid strides or misaligned pointers. */
+attn_status_t attn_sparse_bwd_strided(
+    attn_dtype_t dtype, int32_t B, int32_t H, int64_t L, int32_t d, float scale,
+    const attn_pattern_t *pattern, const attn_index_t *dev_index,
+    const void *q, const attn_strides_t *q_strides,
+    const void *k, const attn_strides_t *k_strides,
+    const void *v, const attn_strides_t *v_strides,
+    const void *o, const attn_strides_t *o_strides, const float *lse,
+    const void *dout, const attn_strides_t *dout_strides,
+    void *dq, const attn_strides_t *dq_strides,
+    void *dk, const attn_strides_t *dk_strides,
+    void *dv, const attn_strides_t *dv_strides,
+    void *workspace, size_t workspace_bytes, void *stream);
 
 /* Decode one new token per sequence in a sparse (sink + window) layer,
  * against its reduced ring-buffer cache.

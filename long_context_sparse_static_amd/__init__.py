@@ -56,6 +56,7 @@ EXPORTED = (
     "attn_layer_map", "attn_workspace_bytes", "attn_sparse_fwd", "attn_sparse_bwd",
     "attn_sparse_decode", "attn_full_decode", "attn_ring_fill", "attn_blocksparse_decode",
     "attn_blocksparse_cache_fill", "attn_paged_decode", "attn_paged_cache_fill",
+    "attn_sparse_fwd_strided", "attn_sparse_bwd_strided",
 )
 
 
@@ -70,6 +71,10 @@ class attn_pattern_t(ctypes.Structure):
                 ("sink_blocks", ctypes.c_int32), ("local_blocks", ctypes.c_int32),
                 ("stride", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("window_tokens", ctypes.c_int32)]
+
+
+class attn_strides_t(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("token", ctypes.c_int64)]
 
 
 class attn_index_t(ctypes.Structure):
@@ -132,6 +137,15 @@ def lib():
         L.attn_blocksparse_cache_fill.restype = i32
         L.attn_blocksparse_cache_fill.argtypes = [i32, i32, i32, i32, P(attn_pattern_t), i32, vp,
                                                   vp, vp, i64, vp, vp, vp]
+        S = P(attn_strides_t)
+        L.attn_sparse_fwd_strided.restype = i32
+        L.attn_sparse_fwd_strided.argtypes = [i32, i32, i32, i64, i32, f32, P(attn_pattern_t),
+                                              P(attn_index_t), vp, S, vp, S, vp, S, vp, S, vp, vp,
+                                              sz, vp]
+        L.attn_sparse_bwd_strided.restype = i32
+        L.attn_sparse_bwd_strided.argtypes = [i32, i32, i32, i64, i32, f32, P(attn_pattern_t),
+                                              P(attn_index_t), vp, S, vp, S, vp, S, vp, S, vp, vp,
+                                              S, vp, S, vp, S, vp, S, vp, sz, vp]
         L.attn_paged_decode.restype = i32
         L.attn_paged_decode.argtypes = [i32, i32, i32, i32, f32, i32, i32, vp, i64, vp, vp, vp,
                                         vp, vp, vp, vp, vp, vp, sz, vp]
@@ -404,6 +418,72 @@ def attn_sparse_bwd(q, k, v, o, lse, dout, index: DeviceIndex, pattern: Pattern,
                                  ctypes.byref(ix), *ptrs, lp, dp, *outs, wp,
                                  workspace.numel() * workspace.element_size(), _stream()),
            "attn_sparse_bwd")
+    return dq, dk, dv
+
+
+def _view(t, name, shape, dtype, device):
+    """Pointer and element strides of a [B,H,L,d]-indexed device tensor view
+    whose last dimension is contiguous (any strides otherwise)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype or t.device != device:
+        raise ValueError(f"{name} must be {dtype} on {device}")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name}: the head dimension must be contiguous")
+    return t.data_ptr(), attn_strides_t(t.stride(0), t.stride(1), t.stride(2))
+
+
+def attn_sparse_fwd_strided(q, k, v, index: DeviceIndex, pattern: Pattern, scale=None, o=None,
+                            lse=None):
+    """Prefill forward on [B,H,L,d]-indexed views with any strides (for
+    example ``x.transpose(1, 2)`` of [B,L,H,d] activations, or slices of a
+    fused QKV projection).  ``o`` defaults to ``empty_like(q)``."""
+    torch = _torch()
+    B, H, L, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    views = [_view(x, n, q.shape, q.dtype, q.device) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"))]
+    lp = _dev(lse, "lse", (B, H, L), torch.float32, q.device)
+    args = [a for ptr, st in views for a in (ptr, ctypes.byref(st))]
+    p = pattern.c_struct()
+    ix = index.c_struct()
+    _check(lib().attn_sparse_fwd_strided(_dtype_code(q), B, H, L, d, scale, ctypes.byref(p),
+                                         ctypes.byref(ix), *args, lp, None, 0, _stream()),
+           "attn_sparse_fwd_strided")
+    return o, lse
+
+
+def attn_sparse_bwd_strided(q, k, v, o, lse, dout, index: DeviceIndex, pattern: Pattern,
+                            scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """Backward on [B,H,L,d]-indexed views with any strides; the gradients
+    default to ``empty_like`` of q, k and v."""
+    torch = _torch()
+    B, H, L, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_workspace_bytes(ATTN_OP_BWD, _dtype_code(q), B, H, L, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    v4 = [_view(x, n, q.shape, q.dtype, q.device) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"))]
+    lp = _dev(lse, "lse", (B, H, L), torch.float32, q.device)
+    vd = _view(dout, "dout", q.shape, q.dtype, q.device)
+    vg = [_view(x, n, q.shape, q.dtype, q.device) for x, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    wp = _dev(workspace, "workspace", device=q.device)
+    flat = lambda vs: [a for ptr, st in vs for a in (ptr, ctypes.byref(st))]
+    p = pattern.c_struct()
+    ix = index.c_struct()
+    _check(lib().attn_sparse_bwd_strided(_dtype_code(q), B, H, L, d, scale, ctypes.byref(p),
+                                         ctypes.byref(ix), *flat(v4), lp, *flat([vd]), *flat(vg), wp,
+                                         workspace.numel() * workspace.element_size(), _stream()),
+           "attn_sparse_bwd_strided")
     return dq, dk, dv
 
 

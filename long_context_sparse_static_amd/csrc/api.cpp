@@ -77,15 +77,47 @@ size_t attn_workspace_bytes(int32_t op, attn_dtype_t dtype, int32_t B, int32_t H
   return 0;
 }
 
-attn_status_t attn_sparse_fwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t L, int32_t d,
-                              float scale, const attn_pattern_t *pattern,
-                              const attn_index_t *dev_index, const void *q, const void *k,
-                              const void *v, void *o, float *lse, void *workspace,
-                              size_t workspace_bytes, void *stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+}  // extern "C"
+
+namespace {
+
+// Contiguous [B,H,L,d] strides.
+attn_strides_t dense_strides(int32_t H, int64_t L, int32_t d) {
+  attn_strides_t s;
+  s.token = d;
+  s.head = L * d;
+  s.batch = (int64_t)H * L * d;
+  return s;
+}
+
+// Strides the kernels can address: non-negative, whole 16-byte vectors
+// (vec elements), 64 token rows within int32 offsets, 16-byte aligned base.
+bool strides_ok(const attn_strides_t *s, const void *p, int vec) {
+  if (!s || !p || ((uintptr_t)p & 15) != 0) return false;
+  if (s->batch < 0 || s->head < 0 || s->token < 0) return false;
+  if (s->batch % vec || s->head % vec || s->token % vec) return false;
+  return s->token <= INT32_MAX / attn::kBlock;
+}
+
+attn::Strides to_kernel(const attn_strides_t *s) {
+  attn::Strides k;
+  k.b = s->batch;
+  k.h = s->head;
+  k.l = (int32_t)s->token;
+  return k;
+}
+
+attn_status_t fwd_impl(attn_dtype_t dtype, int32_t B, int32_t H, int64_t L, int32_t d,
+                       float scale, const attn_pattern_t *pattern, const attn_index_t *dev_index,
+                       const void *q, const attn_strides_t *qs, const void *k,
+                       const attn_strides_t *ks, const void *v, const attn_strides_t *vs,
+                       void *o, const attn_strides_t *os, float *lse, void *stream) {
   if (!prefill_dims_ok(B, H, L, d, scale, pattern)) return ATTN_ERR_INVALID_ARG;
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
+  const int vec = dtype == ATTN_F32 ? 4 : 8;
+  if (!strides_ok(qs, q, vec) || !strides_ok(ks, k, vec) || !strides_ok(vs, v, vec) ||
+      !strides_ok(os, o, vec))
+    return ATTN_ERR_INVALID_ARG;
   if (!index_shape_ok(dev_index, H, L, false)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
@@ -97,6 +129,10 @@ attn_status_t attn_sparse_fwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t 
   a.v = v;
   a.o = o;
   a.lse = lse;
+  a.qs = to_kernel(qs);
+  a.ks = to_kernel(ks);
+  a.vs = to_kernel(vs);
+  a.os = to_kernel(os);
   a.ix = view_of(dev_index);
   a.B = B;
   a.H = H;
@@ -109,14 +145,21 @@ attn_status_t attn_sparse_fwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t 
   return hip_status(dtype == ATTN_BF16 ? attn::launch_fwd_bf16(a, s) : attn::launch_fwd_f32(a, s));
 }
 
-attn_status_t attn_sparse_bwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t L, int32_t d,
-                              float scale, const attn_pattern_t *pattern,
-                              const attn_index_t *dev_index, const void *q, const void *k,
-                              const void *v, const void *o, const float *lse, const void *dout,
-                              void *dq, void *dk, void *dv, void *workspace,
-                              size_t workspace_bytes, void *stream) {
+attn_status_t bwd_impl(attn_dtype_t dtype, int32_t B, int32_t H, int64_t L, int32_t d, float scale,
+                       const attn_pattern_t *pattern, const attn_index_t *dev_index,
+                       const void *q, const attn_strides_t *qs, const void *k,
+                       const attn_strides_t *ks, const void *v, const attn_strides_t *vs,
+                       const void *o, const attn_strides_t *os, const float *lse,
+                       const void *dout, const attn_strides_t *dos, void *dq,
+                       const attn_strides_t *dqs, void *dk, const attn_strides_t *dks, void *dv,
+                       const attn_strides_t *dvs, void *workspace, size_t workspace_bytes,
+                       void *stream) {
   if (!prefill_dims_ok(B, H, L, d, scale, pattern)) return ATTN_ERR_INVALID_ARG;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
+  if (!strides_ok(qs, q, 8) || !strides_ok(ks, k, 8) || !strides_ok(vs, v, 8) ||
+      !strides_ok(os, o, 8) || !strides_ok(dos, dout, 8) || !strides_ok(dqs, dq, 8) ||
+      !strides_ok(dks, dk, 8) || !strides_ok(dvs, dv, 8))
+    return ATTN_ERR_INVALID_ARG;
   if (!index_shape_ok(dev_index, H, L, true)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
@@ -134,6 +177,14 @@ attn_status_t attn_sparse_bwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t 
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
+  a.qs = to_kernel(qs);
+  a.ks = to_kernel(ks);
+  a.vs = to_kernel(vs);
+  a.os = to_kernel(os);
+  a.dos = to_kernel(dos);
+  a.dqs = to_kernel(dqs);
+  a.dks = to_kernel(dks);
+  a.dvs = to_kernel(dvs);
   a.delta = (float *)workspace;
   a.lse2 = (float *)workspace + (size_t)B * H * L;
   a.ix = view_of(dev_index);
@@ -151,6 +202,61 @@ attn_status_t attn_sparse_bwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t 
                  ? pattern->stride
                  : 1;
   return hip_status(attn::launch_bwd_bf16(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_sparse_fwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t L, int32_t d,
+                              float scale, const attn_pattern_t *pattern,
+                              const attn_index_t *dev_index, const void *q, const void *k,
+                              const void *v, void *o, float *lse, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  const attn_strides_t s = dense_strides(H, L, d);
+  return fwd_impl(dtype, B, H, L, d, scale, pattern, dev_index, q, &s, k, &s, v, &s, o, &s, lse,
+                  stream);
+}
+
+attn_status_t attn_sparse_fwd_strided(attn_dtype_t dtype, int32_t B, int32_t H, int64_t L,
+                                      int32_t d, float scale, const attn_pattern_t *pattern,
+                                      const attn_index_t *dev_index, const void *q,
+                                      const attn_strides_t *q_strides, const void *k,
+                                      const attn_strides_t *k_strides, const void *v,
+                                      const attn_strides_t *v_strides, void *o,
+                                      const attn_strides_t *o_strides, float *lse,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return fwd_impl(dtype, B, H, L, d, scale, pattern, dev_index, q, q_strides, k, k_strides, v,
+                  v_strides, o, o_strides, lse, stream);
+}
+
+attn_status_t attn_sparse_bwd(attn_dtype_t dtype, int32_t B, int32_t H, int64_t L, int32_t d,
+                              float scale, const attn_pattern_t *pattern,
+                              const attn_index_t *dev_index, const void *q, const void *k,
+                              const void *v, const void *o, const float *lse, const void *dout,
+                              void *dq, void *dk, void *dv, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  const attn_strides_t s = dense_strides(H, L, d);
+  return bwd_impl(dtype, B, H, L, d, scale, pattern, dev_index, q, &s, k, &s, v, &s, o, &s, lse,
+                  dout, &s, dq, &s, dk, &s, dv, &s, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_sparse_bwd_strided(
+    attn_dtype_t dtype, int32_t B, int32_t H, int64_t L, int32_t d, float scale,
+    const attn_pattern_t *pattern, const attn_index_t *dev_index, const void *q,
+    const attn_strides_t *q_strides, const void *k, const attn_strides_t *k_strides,
+    const void *v, const attn_strides_t *v_strides, const void *o,
+    const attn_strides_t *o_strides, const float *lse, const void *dout,
+    const attn_strides_t *dout_strides, void *dq, const attn_strides_t *dq_strides, void *dk,
+    const attn_strides_t *dk_strides, void *dv, const attn_strides_t *dv_strides,
+    void *workspace, size_t workspace_bytes, void *stream) {
+  return bwd_impl(dtype, B, H, L, d, scale, pattern, dev_index, q, q_strides, k, k_strides, v,
+                  v_strides, o, o_strides, lse, dout, dout_strides, dq, dq_strides, dk, dk_strides,
+                  dv, dv_strides, workspace, workspace_bytes, stream);
 }
 
 static attn_status_t decode_common(attn_dtype_t dtype, int32_t B, int32_t H, int32_t d,

@@ -48,8 +48,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   const int c = threadIdx.x % LPR;
   float acc = 0.f;
   if (row < total) {
-    const u32x4 o = *(const u32x4 *)((const bf16 *)a.o + row * D + c * 8);
-    const u32x4 g = *(const u32x4 *)((const bf16 *)a.dout + row * D + c * 8);
+    const int bh = (int)(row / a.L), l = (int)(row % a.L);
+    const int bb = bh / a.H, head = bh % a.H;
+    const bf16 *op = (const bf16 *)a.o + a.os.at(bb, head) + (size_t)l * a.os.l;
+    const bf16 *gp = (const bf16 *)a.dout + a.dos.at(bb, head) + (size_t)l * a.dos.l;
+    const u32x4 o = *(const u32x4 *)(op + c * 8);
+    const u32x4 g = *(const u32x4 *)(gp + c * 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       acc += bf16_lo(o[i]) * bf16_lo(g[i]) + bf16_hi(o[i]) * bf16_hi(g[i]);
@@ -148,7 +152,7 @@ struct BwdPos {
 //   S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - D), dQ^T += K^T dS^T
 // K is read as rows and transposed (kBothRead), V as rows.
 // ----------------------------------------------------------------------------
-template <int D, bool WIN>
+template <int D, bool WIN, bool DENSE>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   using KT = SwzTile<D, kBothRead>;
   using VT = SwzTile<D, kRowRead>;
@@ -165,9 +169,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int bh = lin / n_tiles;
   const int tile = n_tiles - 1 - lin % n_tiles;   // heaviest tiles first
   const int hidx = a.ix.n_heads == 1 ? 0 : bh % a.H;
-  const size_t base = (size_t)bh * a.L * D;
-  const bf16 *kg = (const bf16 *)a.k + base;
-  const bf16 *vg = (const bf16 *)a.v + base;
+  // token-row strides: compile-time for contiguous [B,H,L,d] tensors
+  const int bb = bh / a.H, head = bh % a.H;
+  const size_t dense_base = (size_t)bh * a.L * D;
+  const int lq = DENSE ? D : a.qs.l, lk = DENSE ? D : a.ks.l, lv = DENSE ? D : a.vs.l;
+  const int ldo = DENSE ? D : a.dos.l, ldq = DENSE ? D : a.dqs.l;
+  const bf16 *kg = (const bf16 *)a.k + (DENSE ? dense_base : a.ks.at(bb, head));
+  const bf16 *vg = (const bf16 *)a.v + (DENSE ? dense_base : a.vs.at(bb, head));
 
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -177,13 +185,14 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const bool q_valid = qb < nqb;
   const int q_wave = qb * kBlock + (wave & 1) * 32;  // first query of this wave
   const int q_tok = q_wave + n;
-  const size_t qrow = base + (size_t)q_tok * D;
+  const bf16 *qp = (const bf16 *)a.q + (DENSE ? dense_base : a.qs.at(bb, head)) + (size_t)q_tok * lq;
+  const bf16 *dop = (const bf16 *)a.dout + (DENSE ? dense_base : a.dos.at(bb, head)) + (size_t)q_tok * ldo;
 
   bf16x8 bq[KS], bdo[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    bq[ks] = q_valid ? *(const bf16x8 *)((const bf16 *)a.q + qrow + ks * 16 + hh * 8) : bf16x8{};
-    bdo[ks] = q_valid ? *(const bf16x8 *)((const bf16 *)a.dout + qrow + ks * 16 + hh * 8) : bf16x8{};
+    bq[ks] = q_valid ? *(const bf16x8 *)(qp + ks * 16 + hh * 8) : bf16x8{};
+    bdo[ks] = q_valid ? *(const bf16x8 *)(dop + ks * 16 + hh * 8) : bf16x8{};
   }
   const float c = a.scale * kLog2e;
   float lse2 = INFINITY, dlt = 0.f;
@@ -197,9 +206,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   VT vr;
   vr.init_reads(lane);
   typename KT::template Loader<kBwdWaves> kl;
-  kl.init(wave, lane);
+  kl.init(wave, lane, lk);
   typename VT::template Loader<kBwdWaves> vl;
-  vl.init(wave, lane);
+  vl.init(wave, lane, lv);
 
   RowsBitmap<kBwdTB> pb;
   pb.init(dyn_lds, a.ix.n_kblocks);
@@ -255,8 +264,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   BwdPos cur = advance(), nxt{false, 0, 0u};
   if (cur.valid) {
     nxt = advance();
-    kl.load(kg + (size_t)cur.j * kBlock * D, k0);
-    vl.load(vg + (size_t)cur.j * kBlock * D, v0);
+    kl.load(kg + (size_t)cur.j * kBlock * lk, k0);
+    vl.load(vg + (size_t)cur.j * kBlock * lv, v0);
   }
   // Block of walk step t lives in slot t & 1; the next block's tiles load into
   // the other slot while this one is computed.
@@ -266,8 +275,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (nxt.valid) {
-      kl.load(kg + (size_t)nxt.j * kBlock * D, P ? k0 : k1);
-      vl.load(vg + (size_t)nxt.j * kBlock * D, P ? v0 : v1);
+      kl.load(kg + (size_t)nxt.j * kBlock * lk, P ? k0 : k1);
+      vl.load(vg + (size_t)nxt.j * kBlock * lv, P ? v0 : v1);
     }
     if (listed(cur)) block_work(P ? k1 : k0, P ? v1 : v0, cur.j);
     cur = nxt;
@@ -280,7 +289,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 
   if (!q_valid) return;
-  bf16 *out = (bf16 *)a.dq + qrow;
+  bf16 *out = (bf16 *)a.dq + (DENSE ? dense_base : a.dqs.at(bb, head)) + (size_t)q_tok * ldq;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -300,7 +309,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 //   dV^T += dO^T P,  dK^T += Q^T dS
 // Q and dO are read as rows and transposed (kBothRead).
 // ----------------------------------------------------------------------------
-template <int D, bool WIN>
+template <int D, bool WIN, bool DENSE>
 __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BwdArgs a) {
   using QT = SwzTile<D, kBothRead>;
   constexpr int KS = D / 16, MT = D / 32;
@@ -346,9 +355,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
   int krows[kBwdTB];
 #pragma unroll
   for (int r = 0; r < kBwdTB; ++r) krows[r] = kt.block(tile, r);
-  const size_t base = (size_t)bh * a.L * D;
-  const bf16 *qg = (const bf16 *)a.q + base;
-  const bf16 *dog = (const bf16 *)a.dout + base;
+  // token-row strides: compile-time for contiguous [B,H,L,d] tensors
+  const int bb = bh / a.H, head = bh % a.H;
+  const size_t dense_base = (size_t)bh * a.L * D;
+  const int lq = DENSE ? D : a.qs.l, ldo_l = DENSE ? D : a.dos.l;
+  const bf16 *qg = (const bf16 *)a.q + (DENSE ? dense_base : a.qs.at(bb, head));
+  const bf16 *dog = (const bf16 *)a.dout + (DENSE ? dense_base : a.dos.at(bb, head));
   const float *lseg = a.lse2 + (size_t)bh * a.L;
   const float *dltg = a.delta + (size_t)bh * a.L;
 
@@ -360,13 +372,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
   const bool k_valid = kb >= 0;
   const int k_wave = kb * kBlock + (wave & 1) * 32;  // first key of this wave
   const int k_tok = k_wave + n;
-  const size_t krow = base + (size_t)k_tok * D;
+  const bf16 *kp = (const bf16 *)a.k + (DENSE ? dense_base : a.ks.at(bb, head)) +
+                   (size_t)k_tok * (DENSE ? D : a.ks.l);
+  const bf16 *vp = (const bf16 *)a.v + (DENSE ? dense_base : a.vs.at(bb, head)) +
+                   (size_t)k_tok * (DENSE ? D : a.vs.l);
 
   bf16x8 bk[KS], bv[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    bk[ks] = k_valid ? *(const bf16x8 *)((const bf16 *)a.k + krow + ks * 16 + hh * 8) : bf16x8{};
-    bv[ks] = k_valid ? *(const bf16x8 *)((const bf16 *)a.v + krow + ks * 16 + hh * 8) : bf16x8{};
+    bk[ks] = k_valid ? *(const bf16x8 *)(kp + ks * 16 + hh * 8) : bf16x8{};
+    bv[ks] = k_valid ? *(const bf16x8 *)(vp + ks * 16 + hh * 8) : bf16x8{};
   }
   const float c = a.scale * kLog2e;
   f32x16 dk[MT], dv[MT];
@@ -375,8 +390,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
 
   QT rd;
   rd.init_reads(lane);
-  typename QT::template Loader<kBwdWaves> ld;
-  ld.init(wave, lane);
+  typename QT::template Loader<kBwdWaves> ldq, ldo;   // Q and dO tiles (own row strides)
+  ldq.init(wave, lane, lq);
+  ldo.init(wave, lane, ldo_l);
   // the two 64-float per-token vectors of a query block: wave 0 loads LSE2,
   // wave 1 the D values (4 bytes per lane)
   auto load_vec = [&](int i, float *lv, float *ev) __attribute__((always_inline)) {
@@ -388,8 +404,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
                                        (__attribute__((address_space(3))) void *)ev, 4, 0, 0);
   };
   auto load_block = [&](int i, char *qt, char *ot, float *lv, float *ev) __attribute__((always_inline)) {
-    ld.load(qg + (size_t)i * kBlock * D, qt);
-    ld.load(dog + (size_t)i * kBlock * D, ot);
+    ldq.load(qg + (size_t)i * kBlock * lq, qt);
+    ldo.load(dog + (size_t)i * kBlock * ldo_l, ot);
     load_vec(i, lv, ev);
   };
 
@@ -523,8 +539,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
   }
 
   if (!k_valid) return;
-  bf16 *dko = (bf16 *)a.dk + krow;
-  bf16 *dvo = (bf16 *)a.dv + krow;
+  bf16 *dko = (bf16 *)a.dk + (DENSE ? dense_base : a.dks.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.dks.l);
+  bf16 *dvo = (bf16 *)a.dv + (DENSE ? dense_base : a.dvs.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.dvs.l);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -539,7 +555,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
-template <int D, bool WIN>
+template <int D, bool WIN, bool DENSE>
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const size_t rows = (size_t)a.B * a.H * a.L;
   const int rpb = 256 / (D / 8);
@@ -549,15 +565,15 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const int BH = a.B * a.H;
   const size_t dyn_k = RowsBitmap<kBwdTB>::lds_bytes(a.ix.n_qblocks);
   const size_t dyn_q = RowsBitmap<kBwdTB>::lds_bytes(a.ix.n_kblocks);
-  hipError_t e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel<D, WIN>,
+  hipError_t e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel<D, WIN, DENSE>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_k);
   if (e == hipSuccess)
-    e = hipFuncSetAttribute((const void *)bwd_dq_kernel<D, WIN>,
+    e = hipFuncSetAttribute((const void *)bwd_dq_kernel<D, WIN, DENSE>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_q);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3(grid_delta), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, WIN>), dim3(BH * k_tiles), dim3(kBwdThreads), dyn_k, s, a);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, WIN>), dim3(BH * q_tiles), dim3(kBwdThreads), dyn_q, s, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, WIN, DENSE>), dim3(BH * k_tiles), dim3(kBwdThreads), dyn_k, s, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, WIN, DENSE>), dim3(BH * q_tiles), dim3(kBwdThreads), dyn_q, s, a);
   return hipGetLastError();
 }
 
@@ -570,8 +586,16 @@ size_t bwd_bf16_lds_bytes(int d, int n_blocks) {
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s) {
-  if (a.window > 0) return a.d == 128 ? launch_bwd<128, true>(a, s) : launch_bwd<64, true>(a, s);
-  return a.d == 128 ? launch_bwd<128, false>(a, s) : launch_bwd<64, false>(a, s);
+  const bool dense = dense_layout(a.qs, a.H, a.L, a.d) && dense_layout(a.ks, a.H, a.L, a.d) &&
+                     dense_layout(a.vs, a.H, a.L, a.d) && dense_layout(a.os, a.H, a.L, a.d) &&
+                     dense_layout(a.dos, a.H, a.L, a.d) && dense_layout(a.dqs, a.H, a.L, a.d) &&
+                     dense_layout(a.dks, a.H, a.L, a.d) && dense_layout(a.dvs, a.H, a.L, a.d);
+  if (a.window > 0) {
+    if (dense) return a.d == 128 ? launch_bwd<128, true, true>(a, s) : launch_bwd<64, true, true>(a, s);
+    return a.d == 128 ? launch_bwd<128, true, false>(a, s) : launch_bwd<64, true, false>(a, s);
+  }
+  if (dense) return a.d == 128 ? launch_bwd<128, false, true>(a, s) : launch_bwd<64, false, true>(a, s);
+  return a.d == 128 ? launch_bwd<128, false, false>(a, s) : launch_bwd<64, false, false>(a, s);
 }
 
 }  // namespace attn

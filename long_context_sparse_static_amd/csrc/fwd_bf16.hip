@@ -80,7 +80,7 @@ struct WalkPos {
   uint32_t mask;  // bit r: listed by query block r of the workgroup
 };
 
-template <int D, bool WIN>
+template <int D, bool WIN, bool DENSE>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   using Lay = FwdLayout<D>;
   constexpr int KS = D / 16;   // k-steps of S^T = K Q^T
@@ -105,10 +105,16 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int tile = n_tiles - 1 - lin % n_tiles;  // heaviest (latest) tiles first
   const int hidx = a.ix.n_heads == 1 ? 0 : bh % a.H;
 
-  const size_t base = (size_t)bh * a.L * D;
-  const bf16 *qg = (const bf16 *)a.q + base;
-  const bf16 *kg = (const bf16 *)a.k + base;
-  const bf16 *vg = (const bf16 *)a.v + base;
+  // Token-row strides: compile-time for contiguous [B,H,L,d] tensors (so tile
+  // addresses stay shifts and no stride is held in registers), else the
+  // caller's strides.
+  const int bb = bh / a.H, head = bh % a.H;
+  const size_t dense_base = (size_t)bh * a.L * D;
+  const int lq = DENSE ? D : a.qs.l, lk = DENSE ? D : a.ks.l, lv = DENSE ? D : a.vs.l;
+  const int lo_ = DENSE ? D : a.os.l;
+  const bf16 *qg = (const bf16 *)a.q + (DENSE ? dense_base : a.qs.at(bb, head));
+  const bf16 *kg = (const bf16 *)a.k + (DENSE ? dense_base : a.ks.at(bb, head));
+  const bf16 *vg = (const bf16 *)a.v + (DENSE ? dense_base : a.vs.at(bb, head));
 
   const int wave = uniform(threadIdx.x >> 6);
   const int grp = wave >> 2;                 // 0: group A, 1: group B (one step behind)
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   bf16x8 bq[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    bq[ks] = q_valid ? *(const bf16x8 *)(qg + (size_t)q_tok * D + ks * 16 + hh * 8) : bf16x8{};
+    bq[ks] = q_valid ? *(const bf16x8 *)(qg + (size_t)q_tok * lq + ks * 16 + hh * 8) : bf16x8{};
 
   // Per-lane global element offsets of this wave's share of a tile load
   // (group B waves load; a wave's share is 16 token rows).
@@ -134,8 +140,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   for (int i = 0; i < Lay::LPW; ++i) {
     const int r = lw * (kBlock / kLoadWaves) + i * Lay::RPI + lane / Lay::CPR;
     const int pc = lane % Lay::CPR;
-    goff_k[i] = r * D + ((pc ^ Lay::kswz(r)) << 3);
-    goff_v[i] = r * D + ((pc ^ Lay::vswz(r)) << 3);
+    goff_k[i] = r * lk + ((pc ^ Lay::kswz(r)) << 3);
+    goff_v[i] = r * lv + ((pc ^ Lay::vswz(r)) << 3);
   }
   auto load_tile = [&](const bf16 *g, char *lds, const int (&goff)[Lay::LPW]) {
 #pragma unroll
@@ -293,7 +299,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   WalkPos prev{false, 0, 0u}, cur = advance(), nxt{false, 0, 0u};
   if (cur.valid) {
     nxt = advance();
-    if (grp == 1) load_tile(kg + (size_t)cur.j * kBlock * D, k0, goff_k);
+    if (grp == 1) load_tile(kg + (size_t)cur.j * kBlock * lk, k0, goff_k);
   }
   // Phases 2t and 2t+1 for t = 0 .. n (n = walk length): group A runs the
   // matrix-core step of walk block t in phase 2t and its vector step in
@@ -321,8 +327,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // the matrix-core waves never queue behind the address unit).
   auto issue_loads = [&](auto PAR) {
     constexpr int P = decltype(PAR)::value;
-    if (nxt.valid) load_tile(kg + (size_t)nxt.j * kBlock * D, P ? k0 : k1, goff_k);
-    if (cur.valid) load_tile(vg + (size_t)cur.j * kBlock * D, P ? v1 : v0, goff_v);
+    if (nxt.valid) load_tile(kg + (size_t)nxt.j * kBlock * lk, P ? k0 : k1, goff_k);
+    if (cur.valid) load_tile(vg + (size_t)cur.j * kBlock * lv, P ? v1 : v0, goff_v);
   };
   auto matrix_phase = [&](auto PAR) {
     constexpr int P = decltype(PAR)::value;
@@ -369,7 +375,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   if (!q_valid) return;
   const float l_tot = xor32_sum(l_part);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  bf16 *orow = (bf16 *)a.o + base + (size_t)q_tok * D;
+  bf16 *orow = (bf16 *)a.o + (DENSE ? dense_base : a.os.at(bb, head)) + (size_t)q_tok * lo_;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -383,16 +389,24 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     a.lse[(size_t)bh * a.L + q_tok] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
 }
 
-template <int D, bool WIN>
+template <int D, bool WIN, bool DENSE>
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
   const int n_tiles = (a.ix.n_qblocks + kFwdQB - 1) / kFwdQB;
   const int grid = a.B * a.H * n_tiles;
   const size_t dyn = RowsBitmap<kFwdQB>::lds_bytes(a.ix.n_kblocks);
-  hipError_t e = hipFuncSetAttribute((const void *)fwd_bf16_kernel<D, WIN>,
+  hipError_t e = hipFuncSetAttribute((const void *)fwd_bf16_kernel<D, WIN, DENSE>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, WIN>), dim3(grid), dim3(kFwdThreads), dyn, s, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, WIN, DENSE>), dim3(grid), dim3(kFwdThreads), dyn, s, a);
   return hipGetLastError();
+}
+
+template <int D, bool WIN>
+hipError_t launch_fwd_layout(const FwdArgs &a, hipStream_t s) {
+  return dense_layout(a.qs, a.H, a.L, D) && dense_layout(a.ks, a.H, a.L, D) &&
+                 dense_layout(a.vs, a.H, a.L, D) && dense_layout(a.os, a.H, a.L, D)
+             ? launch_fwd<D, WIN, true>(a, s)
+             : launch_fwd<D, WIN, false>(a, s);
 }
 
 }  // namespace
@@ -403,8 +417,9 @@ size_t fwd_bf16_lds_bytes(int d, int n_kblocks) {
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s) {
-  if (a.window > 0) return a.d == 128 ? launch_fwd<128, true>(a, s) : launch_fwd<64, true>(a, s);
-  return a.d == 128 ? launch_fwd<128, false>(a, s) : launch_fwd<64, false>(a, s);
+  if (a.window > 0)
+    return a.d == 128 ? launch_fwd_layout<128, true>(a, s) : launch_fwd_layout<64, true>(a, s);
+  return a.d == 128 ? launch_fwd_layout<128, false>(a, s) : launch_fwd_layout<64, false>(a, s);
 }
 
 }  // namespace attn

@@ -25,11 +25,11 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
   const int qb = nqb - 1 - lin % nqb;
   const int h = bh % a.H;
   const int hidx = a.ix.n_heads == 1 ? 0 : h;
-  const size_t base = (size_t)bh * a.L * D;
-  const float *qg = (const float *)a.q + base;
-  const float *kg = (const float *)a.k + base;
-  const float *vg = (const float *)a.v + base;
-  float *og = (float *)a.o + base;
+  const int bb = bh / a.H;
+  const float *qg = (const float *)a.q + a.qs.at(bb, h);
+  const float *kg = (const float *)a.k + a.ks.at(bb, h);
+  const float *vg = (const float *)a.v + a.vs.at(bb, h);
+  float *og = (float *)a.o + a.os.at(bb, h);
 
   const int t = threadIdx.x;
   const int qi = t >> 2, part = t & 3;
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
   float qv[DP], ov[DP];
 #pragma unroll
   for (int i = 0; i < DP; ++i) {
-    qv[i] = qg[(size_t)q_tok * D + part * DP + i];
+    qv[i] = qg[(size_t)q_tok * a.qs.l + part * DP + i];
     ov[i] = 0.f;
   }
   float m_run = -INFINITY, l_run = 0.f;
@@ -50,8 +50,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
     if (j < 0 || j >= a.ix.n_kblocks) continue;
     __syncthreads();
     for (int i = t; i < kBlock * D / 4; i += blockDim.x) {
-      ((f32x4 *)klds)[i] = ((const f32x4 *)(kg + (size_t)j * kBlock * D))[i];
-      ((f32x4 *)vlds)[i] = ((const f32x4 *)(vg + (size_t)j * kBlock * D))[i];
+      const size_t row = (size_t)j * kBlock + i / (D / 4), c4 = 4 * (i % (D / 4));
+      ((f32x4 *)klds)[i] = *(const f32x4 *)(kg + row * a.ks.l + c4);
+      ((f32x4 *)vlds)[i] = *(const f32x4 *)(vg + row * a.vs.l + c4);
     }
     __syncthreads();
     float s[kBlock];
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
   }
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
 #pragma unroll
-  for (int i = 0; i < DP; ++i) og[(size_t)q_tok * D + part * DP + i] = ov[i] * inv;
+  for (int i = 0; i < DP; ++i) og[(size_t)q_tok * a.os.l + part * DP + i] = ov[i] * inv;
   if (part == 0) a.lse[(size_t)bh * a.L + q_tok] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
 }
 

@@ -22,10 +22,28 @@ struct IndexView {
   int32_t nnz;
 };
 
+// Element strides of one tensor indexed [b, h, l, e] (the d elements e of a
+// token row are contiguous): element (b, h, l, e) sits at
+// b * s.b + h * s.h + l * s.l + e.  Contiguous [B,H,L,d]: {H L d, L d, d};
+// [B,L,H,d]: {L H d, d, H d}.
+struct Strides {
+  int64_t b, h;
+  int32_t l;
+  __host__ __device__ __forceinline__ size_t at(int bb, int hh) const {
+    return (size_t)bb * b + (size_t)hh * h;
+  }
+};
+
+// Whether s is the contiguous [B,H,L,d] layout.
+inline bool dense_layout(const Strides &s, int32_t H, int32_t L, int32_t d) {
+  return s.l == d && s.h == (int64_t)L * d && s.b == (int64_t)H * L * d;
+}
+
 struct FwdArgs {
   const void *q, *k, *v;
   void *o;
-  float *lse;
+  float *lse;            // [B,H,L] contiguous
+  Strides qs, ks, vs, os;
   IndexView ix;
   int32_t B, H, L, d;
   float scale;
@@ -39,6 +57,7 @@ struct BwdArgs {
   const void *q, *k, *v, *o, *dout;
   const float *lse;
   void *dq, *dk, *dv;
+  Strides qs, ks, vs, os, dos, dqs, dks, dvs;
   float *delta;        // workspace: D = rowsum(dO * O), [B,H,L] fp32
   float *lse2;         // workspace: LSE * log2(e) (+inf for empty rows), [B,H,L] fp32
   IndexView ix;

@@ -214,12 +214,13 @@ struct SwzTile {
     static_assert(LPW >= 1 && kBlock % (NL * RPI) == 0, "load shape");
     int goff[LPW];   // per-lane global element offsets
     int lds_row0;    // first LDS row of this wave's share
-    __device__ __forceinline__ void init(int lw, int lane) {
+    // row_stride: elements between consecutive token rows in global memory
+    __device__ __forceinline__ void init(int lw, int lane, int row_stride) {
       lds_row0 = lw * (kBlock / NL);
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int r = lds_row0 + i * RPI + lane / CPR;
-        goff[i] = r * D + (((lane % CPR) ^ swz(r)) << 3);
+        goff[i] = r * row_stride + (((lane % CPR) ^ swz(r)) << 3);
       }
     }
     __device__ __forceinline__ void load(const bf16 *g, char *lds) const {

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     assert sorted(lcs.EXPORTED) == names
     L = lcs.lib()
     for n in names:
@@ -262,3 +262,53 @@ def test_decode_validation_errors():
     rf = L_.attn_ring_fill
     assert rf(lcs.ATTN_BF16, 1, 1, 128, 64, 0, FAKE, FAKE, FAKE, 10, FAKE, FAKE, None) == lcs.ATTN_ERR_INVALID_ARG
     assert rf(lcs.ATTN_BF16, 1, 1, 100, 64, 64, FAKE, FAKE, FAKE, 10, FAKE, FAKE, None) == lcs.ATTN_ERR_UNSUPPORTED
+
+
+def test_strided_validation_errors():
+    """Strides that are not whole 16-byte vectors, negative strides, a token
+    stride beyond 64-row int32 offsets and a misaligned base are rejected
+    before any launch."""
+    L_ = lcs.lib()
+    p = lcs.attnsink_pattern(1, 2).c_struct()
+    ix = lcs.attn_index_t(1, 4, 4, 10, FAKE, FAKE, None, None)
+    good = lcs.attn_strides_t(2 * 256 * 128, 256 * 128, 128)
+
+    def fwd(qs=good, q=FAKE, dtype=lcs.ATTN_BF16):
+        return L_.attn_sparse_fwd_strided(dtype, 1, 2, 256, 128, 0.1, ctypes.byref(p), ctypes.byref(ix),
+                                          q, ctypes.byref(qs), FAKE, ctypes.byref(good), FAKE,
+                                          ctypes.byref(good), FAKE, ctypes.byref(good), FAKE, None, 0,
+                                          None)
+    assert fwd(qs=lcs.attn_strides_t(65536, 32768, 132)) == lcs.ATTN_ERR_INVALID_ARG   # 264 B rows
+    assert fwd(qs=lcs.attn_strides_t(65536, -32768, 128)) == lcs.ATTN_ERR_INVALID_ARG
+    assert fwd(qs=lcs.attn_strides_t(65536, 32768, 1 << 26)) == lcs.ATTN_ERR_INVALID_ARG
+    assert fwd(q=ctypes.c_void_p(0x1008)) == lcs.ATTN_ERR_INVALID_ARG                  # 8-byte aligned
+    assert fwd(qs=lcs.attn_strides_t(65536, 32768, 130), dtype=lcs.ATTN_F32) == lcs.ATTN_ERR_INVALID_ARG
+    csc = lcs.attn_index_t(1, 4, 4, 10, FAKE, FAKE, FAKE, FAKE)
+    bad = lcs.attn_strides_t(0, 0, 12)
+    g = ctypes.byref(good)
+    assert L_.attn_sparse_bwd_strided(lcs.ATTN_BF16, 1, 2, 256, 128, 0.1, ctypes.byref(p),
+                                      ctypes.byref(csc), FAKE, g, FAKE, g, FAKE, g, FAKE, g, FAKE,
+                                      FAKE, g, FAKE, g, FAKE, ctypes.byref(bad), FAKE, g, FAKE,
+                                      1 << 20, None) == lcs.ATTN_ERR_INVALID_ARG
+
+
+def test_sliding_forward_requires_causal():
+    p = lcs.Pattern(lcs.ATTN_SLIDING, 1, 0, 0, False, window_tokens=100).c_struct()
+    assert _fwd(pattern=p) == lcs.ATTN_ERR_INVALID_ARG
+    p = lcs.sliding_pattern(1, 0).c_struct()
+    assert _fwd(pattern=p) == lcs.ATTN_ERR_INVALID_ARG
+
+
+def test_paged_validation_errors():
+    L_ = lcs.lib()
+
+    def pd(n_pages=10, max_pages=4, table=FAKE, max_pos=255, wsb=1 << 30):
+        return L_.attn_paged_decode(lcs.ATTN_BF16, 2, 4, 128, 0.1, n_pages, max_pages, table, max_pos,
+                                    FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wsb, None)
+    assert pd(n_pages=0) == lcs.ATTN_ERR_INVALID_ARG
+    assert pd(table=None) == lcs.ATTN_ERR_INVALID_ARG
+    assert pd(max_pos=256) == lcs.ATTN_ERR_INVALID_ARG          # beyond 64 * max_pages - 1
+    assert pd(wsb=8) == lcs.ATTN_ERR_WORKSPACE
+    pf = L_.attn_paged_cache_fill
+    assert pf(lcs.ATTN_BF16, 2, 4, 128, 10, 0, FAKE, FAKE, FAKE, FAKE, 100, FAKE, FAKE, None) == lcs.ATTN_ERR_INVALID_ARG
+    assert pf(lcs.ATTN_BF16, 2, 4, 96, 10, 4, FAKE, FAKE, FAKE, FAKE, 100, FAKE, FAKE, None) == lcs.ATTN_ERR_UNSUPPORTED
