@@ -38,7 +38,9 @@
 //   * Online softmax in base 2 with scale*log2(e) folded into one FMA; the
 //     running max is only moved when a block raises it by more than 2^8, so
 //     the O rescale is skipped on most blocks (exact: the final O / l uses
-//     the same reference point for both sums).  The row sum l adds the same
+//     the same reference point for both sums).  No per-block max is taken on
+//     the common path: a block's P sum exceeding 2^8 flags the blocks that
+//     might raise it.  The row sum l adds the same
 //     bf16-rounded P that enters the P V product (two per dot2 instruction),
 //     so numerator and denominator see identical weights.
 #include <type_traits>
@@ -241,40 +243,53 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
             if (32 * t + 8 * (r >> 2) + (r & 3) <= lo) sc[t][r] = -INFINITY;
       }
     }
-    float mx = -INFINITY;
+    // P = exp2(s c - msub) of the block, packed into pk for the next P V;
+    // returns this lane's sum of the packed (bf16) P.  k-step ks of P V
+    // takes registers 8 (ks % 2) .. +7 of tile ks / 2.
+    auto exps = [&](float msub) -> float {
+      float lb = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4 w;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
-    mx = xor32_max(mx);
-    const float mc = mx * c;
-    const bool need = mc > m_run + 8.0f;
-    if (__any(need)) {
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * (ks & 1) + 2 * e;
+          const float p0 = fast_exp2(__builtin_fmaf(sc[ks >> 1][r], c, -msub));
+          const float p1 = fast_exp2(__builtin_fmaf(sc[ks >> 1][r + 1], c, -msub));
+          // The packed words are built here, not read back out of a bf16x8:
+          // extracting 32-bit words of a bit-cast bf16x8 for the dot2
+          // compiled to four reads of word 0 (hipcc, ROCm 7.2).
+          w[e] = pack_bf16x2(p0, p1);
+          lb = sum_bf16x2(w[e], lb);
+        }
+        pk[ks] = __builtin_bit_cast(bf16x8, w);
+      }
+      return lb;
+    };
+    // Lazy running max without a per-block max.  A block's P (against the
+    // current m_run) can exceed 2^8 only if its sum does, so a block whose P
+    // sum is not <= 2^8 (which also catches inf and NaN), or a row with no
+    // max yet, takes the exact path: block max, rescale when it rises by
+    // more than 8 (base 2), P again.
+    float lb = exps(m_run);
+    if (__any(m_run == -INFINITY || !(lb <= 256.0f))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
+      mx = xor32_max(mx);
+      const float mc = mx * c;
+      const bool need = mc > m_run + 8.0f;
       const float m_new = need ? mc : m_run;
       const float alpha = m_new == m_run ? 1.0f : fast_exp2(m_run - m_new);
       l_part *= alpha;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) oacc[mt] *= alpha;
       m_run = m_new;
+      lb = exps(m_run == -INFINITY ? 0.f : m_run);
     }
-    const float msub = m_run == -INFINITY ? 0.f : m_run;
-    // k-step ks of P V takes registers 8 (ks % 2) .. +7 of tile ks / 2.
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 8 * (ks & 1) + 2 * e;
-        const float p0 = fast_exp2(__builtin_fmaf(sc[ks >> 1][r], c, -msub));
-        const float p1 = fast_exp2(__builtin_fmaf(sc[ks >> 1][r + 1], c, -msub));
-        // The packed words are built here, not read back out of a bf16x8:
-        // extracting 32-bit words of a bit-cast bf16x8 for the dot2 compiled
-        // to four reads of word 0 (hipcc, ROCm 7.2).
-        w[e] = pack_bf16x2(p0, p1);
-        l_part = sum_bf16x2(w[e], l_part);
-      }
-      pk[ks] = __builtin_bit_cast(bf16x8, w);
-    }
+    l_part += lb;
   };
 
   // The first matrix-core step multiplies pk = 0 by slot v1 before any
