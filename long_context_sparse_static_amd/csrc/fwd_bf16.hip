@@ -373,6 +373,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     even_phase();
     issue_loads(PAR);
     vector_or_zero(prev);
+    // this wave's tile loads land before its matrix step reads LDS, so the
+    // compiler need not treat them as pending there
+    __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     matrix_phase(PAR);
     return true;
