@@ -127,7 +127,7 @@ typedef struct {
  * Contiguous [B,H,L,d] is {H*L*d, L*d, d}; [B,L,H,d] is {L*H*d, d, H*d}; the
  * Q of a fused [B,L,3,H,d] projection is {3*L*H*d, d, 3*H*d} at offset 0
  * (K at H*d, V at 2*H*d).  Strides must be >= 0 and whole 16-byte vectors
- * (multiples of 8 bf16 / 4 fp32 elements), token <= INT32_MAX / 64, and the
+ * (multiples of 8 bf16 / 4 fp32 elements), token <= INT32_MAX / 128, and the
  * base pointer 16-byte aligned.  Outputs must not overlap each other or the
  * inputs. */
 typedef struct {

@@ -91,12 +91,13 @@ attn_strides_t dense_strides(int32_t H, int64_t L, int32_t d) {
 }
 
 // Strides the kernels can address: non-negative, whole 16-byte vectors
-// (vec elements), 64 token rows within int32 offsets, 16-byte aligned base.
+// (vec elements), 64 token rows within int32 byte offsets, 16-byte aligned
+// base.
 bool strides_ok(const attn_strides_t *s, const void *p, int vec) {
   if (!s || !p || ((uintptr_t)p & 15) != 0) return false;
   if (s->batch < 0 || s->head < 0 || s->token < 0) return false;
   if (s->batch % vec || s->head % vec || s->token % vec) return false;
-  return s->token <= INT32_MAX / attn::kBlock;
+  return s->token <= INT32_MAX / (2 * attn::kBlock);  // 64 rows of bf16 in int32 bytes
 }
 
 attn::Strides to_kernel(const attn_strides_t *s) {

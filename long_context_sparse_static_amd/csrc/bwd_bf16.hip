@@ -17,7 +17,7 @@
 //
 // gfx950 mapping (both MFMA kernels): the streamed tiles (K and V for dQ; Q
 // and dO for dK/dV) go straight from global memory into XOR-swizzled LDS
-// rows (global_load_lds_dwordx4), double-buffered in slots that every load
+// rows (buffer_load_dwordx4 ... lds), double-buffered in slots that every load
 // and read names at compile time, so the compiler never waits for a tile
 // load in flight before reading the other slot.  A tile needed both as a row
 // operand and transposed is read transposed through ds_read_b64_tr_b16;
@@ -397,11 +397,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
   // wave 1 the D values (4 bytes per lane)
   auto load_vec = [&](int i, float *lv, float *ev) __attribute__((always_inline)) {
     if (wave == 0)
-      __builtin_amdgcn_global_load_lds((const void *)(lseg + (size_t)i * kBlock + lane),
-                                       (__attribute__((address_space(3))) void *)lv, 4, 0, 0);
+      load_lds<4>(buffer_rsrc(lseg + (size_t)i * kBlock), 4 * lane, lv);
     else if (wave == 1)
-      __builtin_amdgcn_global_load_lds((const void *)(dltg + (size_t)i * kBlock + lane),
-                                       (__attribute__((address_space(3))) void *)ev, 4, 0, 0);
+      load_lds<4>(buffer_rsrc(dltg + (size_t)i * kBlock), 4 * lane, ev);
   };
   auto load_block = [&](int i, char *qt, char *ot, float *lv, float *ev) __attribute__((always_inline)) {
     ldq.load(qg + (size_t)i * kBlock * lq, qt);

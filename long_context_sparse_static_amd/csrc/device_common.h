@@ -71,6 +71,27 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Direct global -> LDS loads through a raw buffer descriptor: lane i's BYTES
+// (4 or 16) from base + byte_off land at lds + i * BYTES (lds wave-uniform).
+// Unlike global_load_lds, the compiler counts this form on vmcnt alone, so
+// LDS reads issued while it is in flight keep exact lgkmcnt waits (with a
+// global_load_lds pending it waits for every outstanding LDS read instead).
+// Descriptor: stride 0 (raw bytes), no range limit, data format 32 (the
+// untyped-buffer setting of the gfx9 descriptor word 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, 0x00020000);
+}
+template <int BYTES>
+__device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t rs, int byte_off, void *lds) {
+  static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte lanes");
+  auto *l = (__attribute__((address_space(3))) void *)lds;
+  // the builtin wants its size as a literal
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, byte_off, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 4, byte_off, 0, 0, 0);
+}
+
 // A wave-uniform copy of a value every lane holds (kept in an SGPR).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

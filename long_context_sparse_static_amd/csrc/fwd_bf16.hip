@@ -26,7 +26,7 @@
 //     the workgroups on one XCD stream the same key blocks at the same time
 //     and L2 serves the repeats.
 //   * K and V tiles go straight from global memory into LDS
-//     (global_load_lds_dwordx4: no staging registers, no LDS store
+//     (buffer_load_dwordx4 ... lds: no staging registers, no LDS store
 //     instructions) into unpadded rows whose 16-byte chunks are XOR-swizzled
 //     so the operand reads below hit all 64 banks.  Two K and two V slots;
 //     the tiles of key block t+1 (K) and t (V) are issued two steps before
@@ -142,16 +142,14 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   for (int i = 0; i < Lay::LPW; ++i) {
     const int r = lw * (kBlock / kLoadWaves) + i * Lay::RPI + lane / Lay::CPR;
     const int pc = lane % Lay::CPR;
-    goff_k[i] = r * lk + ((pc ^ Lay::kswz(r)) << 3);
-    goff_v[i] = r * lv + ((pc ^ Lay::vswz(r)) << 3);
+    goff_k[i] = 2 * (r * lk + ((pc ^ Lay::kswz(r)) << 3));   // bytes
+    goff_v[i] = 2 * (r * lv + ((pc ^ Lay::vswz(r)) << 3));
   }
   auto load_tile = [&](const bf16 *g, char *lds, const int (&goff)[Lay::LPW]) {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g);
 #pragma unroll
     for (int i = 0; i < Lay::LPW; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const void *)(g + goff[i]),
-          (__attribute__((address_space(3))) void *)(lds + (lw * (kBlock / kLoadWaves) + i * Lay::RPI) * RB),
-          16, 0, 0);
+      load_lds<16>(rs, goff[i], lds + (lw * (kBlock / kLoadWaves) + i * Lay::RPI) * RB);
   };
 
   // Per-lane LDS read offsets.  K row operand for k-step ks: row n (+32 t),

@@ -181,7 +181,7 @@ __device__ __forceinline__ bf16x8 pack_acc_operand(const f32x16 &t, int half) {
 }
 
 // A 64 x D bf16 tile staged straight from global memory into LDS
-// (global_load_lds_dwordx4) as 64 unpadded rows of RB = 2 D bytes whose
+// (buffer_load_dwordx4 ... lds) as 64 unpadded rows of RB = 2 D bytes whose
 // 16-byte chunks are XOR-swizzled: chunk c of row r sits at chunk
 // c ^ swz(r).  The swizzle is chosen by how the tile is read:
 //   kRowRead  as the row operand of a 32x32x16 MFMA (lane = row, 16 bytes);
@@ -212,7 +212,7 @@ struct SwzTile {
   struct Loader {
     static constexpr int LPW = kBlock / NL / RPI;  // instructions per wave
     static_assert(LPW >= 1 && kBlock % (NL * RPI) == 0, "load shape");
-    int goff[LPW];   // per-lane global element offsets
+    int goff[LPW];   // per-lane global byte offsets from the tile's first row
     int lds_row0;    // first LDS row of this wave's share
     // row_stride: elements between consecutive token rows in global memory
     __device__ __forceinline__ void init(int lw, int lane, int row_stride) {
@@ -220,15 +220,13 @@ struct SwzTile {
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int r = lds_row0 + i * RPI + lane / CPR;
-        goff[i] = r * row_stride + (((lane % CPR) ^ swz(r)) << 3);
+        goff[i] = 2 * (r * row_stride + (((lane % CPR) ^ swz(r)) << 3));
       }
     }
     __device__ __forceinline__ void load(const bf16 *g, char *lds) const {
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g);
 #pragma unroll
-      for (int i = 0; i < LPW; ++i)
-        __builtin_amdgcn_global_load_lds(
-            (const void *)(g + goff[i]),
-            (__attribute__((address_space(3))) void *)(lds + (lds_row0 + i * RPI) * RB), 16, 0, 0);
+      for (int i = 0; i < LPW; ++i) load_lds<16>(rs, goff[i], lds + (lds_row0 + i * RPI) * RB);
     }
   };
 

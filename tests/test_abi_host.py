@@ -280,7 +280,7 @@ def test_strided_validation_errors():
                                           None)
     assert fwd(qs=lcs.attn_strides_t(65536, 32768, 132)) == lcs.ATTN_ERR_INVALID_ARG   # 264 B rows
     assert fwd(qs=lcs.attn_strides_t(65536, -32768, 128)) == lcs.ATTN_ERR_INVALID_ARG
-    assert fwd(qs=lcs.attn_strides_t(65536, 32768, 1 << 26)) == lcs.ATTN_ERR_INVALID_ARG
+    assert fwd(qs=lcs.attn_strides_t(65536, 32768, 1 << 25)) == lcs.ATTN_ERR_INVALID_ARG
     assert fwd(q=ctypes.c_void_p(0x1008)) == lcs.ATTN_ERR_INVALID_ARG                  # 8-byte aligned
     assert fwd(qs=lcs.attn_strides_t(65536, 32768, 130), dtype=lcs.ATTN_F32) == lcs.ATTN_ERR_INVALID_ARG
     csc = lcs.attn_index_t(1, 4, 4, 10, FAKE, FAKE, FAKE, FAKE)
