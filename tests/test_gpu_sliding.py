@@ -131,3 +131,23 @@ def test_sliding_prefill_last_row_equals_decode():
         assert_bf16_close(as_f64(od[0, h, 0]), wo, f"decode head {h}")
         assert abs(float(lse[0, h, t]) - wl) < 2e-3 and abs(float(ld[0, h]) - wl) < 2e-3
     assert float((o[0, :, t] - od[0, :, 0]).abs().max()) < 2e-2
+
+
+@pytest.mark.parametrize("s,W,d", [(1, 100, 128), (0, 37, 64), (2, 64, 128)])
+def test_sliding_zero_query_lse_counts(s, W, d):
+    """Q = 0: LSE = ln(number of keys read) exactly -- min(q + 1, W) window
+    keys plus the sink keys left of the window -- which pins the token
+    window's edges on the GPU."""
+    need_gpu()
+    H, nb = 4, 9
+    L = 64 * nb
+    pat = lcs.sliding_pattern(s, W)
+    q = torch.zeros((1, H, L, d), dtype=torch.bfloat16, device="cuda")
+    _, k, v = _inputs((1, H, L, d), 760)
+    _, o, lse = _fwd(q, k, v, pat)
+    t = np.arange(L)
+    counts = np.minimum(t + 1, W) + np.maximum(0, np.minimum(64 * s, t + 1 - W))
+    for h in range(H):
+        np.testing.assert_allclose(lse[0, h].cpu().numpy(), np.log(counts), rtol=0, atol=2e-6)
+    wo, _ = sparse_forward(np.zeros((1, H, L, d)), as_f64(k), as_f64(v), oracle_pattern(pat))
+    assert_bf16_close(as_f64(o), wo, "O")
