@@ -31,7 +31,8 @@ namespace attn {
 namespace {
 
 constexpr int kDecThreads = 256;
-constexpr int kDecUnroll = 8;  // keys in flight per lane group
+constexpr int kDecUnroll = 4;       // keys in flight per lane group
+constexpr int kDecTargetWgs = 4096;  // split-KV workgroups aimed for per launch
 
 __device__ __forceinline__ int64_t ring_slot(int64_t p, int sink, int window) {
   return p < sink ? p : sink + (p - sink) % window;
@@ -409,10 +410,12 @@ __global__ __launch_bounds__(256) void paged_fill_kernel(PagedFillArgs a) {
 }  // namespace
 
 void decode_split_plan(int32_t B, int32_t H, int64_t n_keys, int32_t *n_split, int32_t *split_len) {
-  // Aim for >= 8 workgroups per CU across 256 CUs, but keep each split at
-  // >= 512 keys so a workgroup streams >= 256 KB (d = 128).
+  // Aim for >= 16 workgroups per CU across 256 CUs, but keep each split at
+  // >= 512 keys so a workgroup streams >= 256 KB (d = 128).  (Measured at
+  // 16 x 32 heads x 131073 keys: 1536 to 16384 workgroups and 2 to 8 keys in
+  // flight per lane group all land within 2% of each other, 6.66-6.79 TB/s.)
   const int64_t bh = (int64_t)B * H;
-  int64_t want = (2048 + bh - 1) / bh;
+  int64_t want = (kDecTargetWgs + bh - 1) / bh;
   int64_t len = (n_keys + want - 1) / want;
   if (len < 512) len = 512;
   len = (len + 255) / 256 * 256;
@@ -428,7 +431,7 @@ int32_t decode_split_bound(int32_t B, int32_t H, int64_t n_keys) {
   // decreases as n grows (so a workspace sized for a capacity fits every
   // position below it).
   const int64_t bh = (int64_t)B * H;
-  const int64_t want = (2048 + bh - 1) / bh;
+  const int64_t want = (kDecTargetWgs + bh - 1) / bh;
   int64_t ns = (n_keys + 511) / 512;
   if (ns > want) ns = want;
   return (int32_t)(ns < 1 ? 1 : ns);
