@@ -36,11 +36,10 @@
 //     V reaches the matrix cores through the transposing LDS read
 //     (ds_read_b64_tr_b16) for O^T += V^T P^T; P goes fp32 -> bf16 (RNE).
 //   * Online softmax in base 2 with scale*log2(e) folded into one FMA; the
-//     running max is only moved when a block raises it by more than 2^8, so
-//     the O rescale is skipped on most blocks (exact: the final O / l uses
-//     the same reference point for both sums).  No per-block max is taken on
-//     the common path: a block's P sum exceeding 2^8 flags the blocks that
-//     might raise it.  The row sum l adds the same
+//     running max is only moved when a block's P sum (against it) exceeds
+//     2^8, so neither a per-block max nor the O rescale runs on most blocks
+//     (exact: the final O / l uses the same reference point for both sums,
+//     and no P exceeds 2^8).  The row sum l adds the same
 //     bf16-rounded P that enters the P V product (two per dot2 instruction),
 //     so numerator and denominator see identical weights.
 #include <type_traits>
@@ -267,8 +266,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     // Lazy running max without a per-block max.  A block's P (against the
     // current m_run) can exceed 2^8 only if its sum does, so a block whose P
     // sum is not <= 2^8 (which also catches inf and NaN), or a row with no
-    // max yet, takes the exact path: block max, rescale when it rises by
-    // more than 8 (base 2), P again.
+    // max yet, takes the exact path: block max, rescale to it if it is
+    // higher (so later blocks see P <= 1 again), P again.
     float lb = exps(m_run);
     if (__any(m_run == -INFINITY || !(lb <= 256.0f))) {
       float mx = -INFINITY;
@@ -278,7 +277,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
       mx = xor32_max(mx);
       const float mc = mx * c;
-      const bool need = mc > m_run + 8.0f;
+      const bool need = mc > m_run;
       const float m_new = need ? mc : m_run;
       const float alpha = m_new == m_run ? 1.0f : fast_exp2(m_run - m_new);
       l_part *= alpha;

@@ -220,3 +220,33 @@ def test_bf16_mixed_heads_32k_sampled():
         idx = torch.as_tensor(rows, device=q.device)
         assert_bf16_close(as_f64(o[0, h, idx]), wo, f"mixed O head {h}")
         assert_bf16_close(as_f64(lse[0, h, idx]), wlse, f"mixed LSE head {h}")
+
+
+@pytest.mark.parametrize("kind", ["rising", "spikes"])
+def test_running_max_paths(kind):
+    """Inputs that drive the forward's running-max paths hard: scores that
+    rise block after block along the key axis (the max moves again and
+    again), and a few keys whose scores are hundreds above the rest (P would
+    overflow against a stale max).  Both must match the oracle."""
+    need_gpu()
+    pat = lcs.full_pattern()
+    B, H, L, d = 1, 2, 64 * 12, 128
+    g = torch.Generator().manual_seed(4242)
+    q = torch.randn((B, H, L, d), generator=g)
+    k = torch.randn((B, H, L, d), generator=g) * 0.3
+    v = torch.randn((B, H, L, d), generator=g)
+    if kind == "rising":
+        # key j leans along a shared direction with weight growing in j
+        u = torch.randn(d, generator=g)
+        q += 2.0 * u
+        k += (torch.arange(L, dtype=torch.float32) / 64.0 * 0.35)[:, None] * u
+    else:
+        k[:, :, 5 * 64 + 7] = q[:, :, -1] * 10.0     # scores ~160 (base 2) above the rest
+        k[:, :, 9 * 64 + 40] = -q[:, :, -1] * 10.0
+        k[:, :, 11 * 64 + 3] = q[:, :, 700] * 12.0
+    q, k, v = (x.to(torch.bfloat16).cuda() for x in (q, k, v))
+    o, lse = _run(q, k, v, pat)
+    wo, wl = sparse_forward(as_f64(q), as_f64(k), as_f64(v), oracle_pattern(pat))
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    print(kind, "O", assert_bf16_close(as_f64(o), wo, "O"))
+    print(kind, "LSE", assert_bf16_close(as_f64(lse), wl, "LSE"))
