@@ -463,9 +463,21 @@ def make_workload(name):
 # ----------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample of the same workload)
 # ----------------------------------------------------------------------------
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
+
+
 def cpu_baseline(budget_s=15.0):
     """Times the oracle on sampled query rows of one 128K AttnSink layer and
-    scales to effective TFLOP/s over the computed blocks of those rows."""
+    scales to effective TFLOP/s over the computed blocks of those rows.  The
+    same rows of the GPU forward on the same inputs are compared with the
+    oracle's, and their errors reported beside the rate."""
     from oracle import sparse_forward
     try:
         from threadpoolctl import threadpool_info
@@ -475,24 +487,38 @@ def cpu_baseline(budget_s=15.0):
     L = 131072
     g = torch.Generator().manual_seed(seed_for(5, 0, "q"))
     # one head's Q/K/V, generated on the host (the sample needs the whole key range)
-    q = torch.randn((1, 1, L, D), generator=g).to(torch.bfloat16).double().numpy()
-    k = torch.randn((1, 1, L, D), generator=g).to(torch.bfloat16).double().numpy()
-    v = torch.randn((1, 1, L, D), generator=g).to(torch.bfloat16).double().numpy()
+    qt, kt, vt = (torch.randn((1, 1, L, D), generator=g).to(torch.bfloat16) for _ in range(3))
+    q, k, v = (x.double().numpy() for x in (qt, kt, vt))
     pat = dict(kind="attnsink", block=BLK, sink_blocks=SINK_BLOCKS, local_blocks=WINDOW_BLOCKS, causal=True)
+    # the GPU forward of the same head
+    gpat = lcs.attnsink_pattern(SINK_BLOCKS, WINDOW_BLOCKS)
+    gq, gk, gv = (x.cuda() for x in (qt, kt, vt))
+    ix = lcs.build_device_index(gpat, 1, L, gq.device, with_csc=False)
+    go, glse = lcs.attn_sparse_fwd(gq, gk, gv, ix, gpat)
+    go, glse = go[0, 0].double().cpu().numpy(), glse[0, 0].double().cpu().numpy()
     rng = np.random.default_rng(0)
     rows_done, pairs_done, t_used, batch = 0, 0.0, 0.0, 64
+    err_o = err_l = 0.0
+    err_sum, n_el = 0.0, 0
     while t_used < budget_s and rows_done < 4096:
         rows = np.sort(rng.choice(np.arange(WINDOW_BLOCKS * BLK, L), size=batch, replace=False))
         t0 = time.perf_counter()
-        sparse_forward(q, k, v, pat, rows=rows)
+        o, lse = sparse_forward(q, k, v, pat, rows=rows)
         t_used += time.perf_counter() - t0
+        d_o = np.abs(go[rows] - o[0, 0, rows])
+        err_o = max(err_o, float(d_o.max()))
+        err_l = max(err_l, float(np.abs(glse[rows] - lse[0, 0, rows]).max()))
+        err_sum += float(d_o.sum())
+        n_el += d_o.size
         rows_done += batch
         pairs_done += batch * (SINK_BLOCKS + WINDOW_BLOCKS) / BLK   # block pairs per query row
     flops = pairs_done * pair_flops()
     return dict(value=flops / t_used / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
                 sample=f"{rows_done} query rows (random, past the first window) of one head of one "
                        f"128K AttnSink layer, float64 dense-masked NumPy; {t_used:.1f} s",
-                affinity_cpus=len(os.sched_getaffinity(0)))
+                affinity_cpus=len(os.sched_getaffinity(0)), cpu_model=cpu_model(),
+                parity_vs_gpu=dict(rows=rows_done, o_max_abs=err_o, o_mean_abs=err_sum / max(n_el, 1),
+                                   lse_max_abs=err_l, tolerance="max 2e-2, mean 2e-3"))
 
 
 # ----------------------------------------------------------------------------

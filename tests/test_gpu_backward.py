@@ -1,5 +1,7 @@
 """GPU parity of the training backward (attn_sparse_bwd) against the oracle."""
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -125,3 +127,28 @@ def test_backward_blocksparse_32k_sampled_blocks():
             g = {"dq": dq, "dk": dk, "dv": dv}[name][0, h, 64 * blk:64 * (blk + 1)]
             mx, mean = assert_bf16_close(as_f64(g), w, f"{name} head {h} block {blk}")
             print(name, h, blk, mx, mean)
+
+
+@pytest.mark.parametrize("pat", [lcs.attnsink_pattern(1, 3), lcs.blocksparse_pattern(1, 2, 3)])
+def test_peaky_sink_forward_backward(pat):
+    """Attention concentrated on the sink block, as trained models show:
+    queries share a direction and the sink keys point along it, so most of
+    every row's softmax mass sits on the first 64 tokens.  Forward and all
+    three gradients against the oracle."""
+    need_gpu()
+    B, H, L, d = 1, 4, 64 * 12, 128
+    g = torch.Generator().manual_seed(777)
+    u = torch.randn(d, generator=g)
+    q = torch.randn((B, H, L, d), generator=g) * 0.5 + 0.8 * u
+    k = torch.randn((B, H, L, d), generator=g) * 0.5
+    k[:, :, :64] += 1.2 * u
+    v = torch.randn((B, H, L, d), generator=g)
+    do = torch.randn((B, H, L, d), generator=g)
+    q, k, v, do = (x.to(torch.bfloat16).cuda() for x in (q, k, v, do))
+    dq, dk, dv = _fwd_bwd(q, k, v, do, pat)
+    wq, wk, wv, wo, wl = sparse_backward(as_f64(q), as_f64(k), as_f64(v), as_f64(do), oracle_pattern(pat))
+    # the sink really dominates: the oracle's probability mass on block 0 for late rows
+    s = as_f64(q[0, 0, -64:]) @ as_f64(k[0, 0]).T / math.sqrt(d)
+    assert (np.exp(s[:, :64] - wl[0, 0, -64:, None]).sum(axis=1) > 0.5).all()
+    for name, gt, w in (("dq", dq, wq), ("dk", dk, wk), ("dv", dv, wv)):
+        print(name, assert_bf16_close(as_f64(gt), w, name))
