@@ -92,6 +92,13 @@ __device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t rs, int byte_off
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 4, byte_off, 0, 0, 0);
 }
 
+// x if keep >= 0, else -inf: one bitfield insert keyed on keep's sign bit,
+// so a run of masks needs no per-element condition registers.
+__device__ __forceinline__ float mask_neg_inf(float x, int keep) {
+  const uint32_t sel = (uint32_t)(keep >> 31);  // all ones when keep < 0
+  return __uint_as_float((sel & 0xff800000u) | (~sel & __float_as_uint(x)));
+}
+
 // A wave-uniform copy of a value every lane holds (kept in an SGPR).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

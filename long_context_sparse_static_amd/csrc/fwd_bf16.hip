@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * t + 8 * (r >> 2) + (r & 3) > lim) sc[t][r] = -INFINITY;
+          sc[t][r] = mask_neg_inf(sc[t][r], lim - (32 * t + 8 * (r >> 2) + (r & 3)));
     }
     if constexpr (WIN) {
       // token window: keys k <= q - window of blocks past the sink blocks
@@ -237,14 +237,14 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (32 * t + 8 * (r >> 2) + (r & 3) <= lo) sc[t][r] = -INFINITY;
+            sc[t][r] = mask_neg_inf(sc[t][r], (32 * t + 8 * (r >> 2) + (r & 3)) - lo - 1);
       }
     }
     // P = exp2(s c - msub) of the block, packed into pk for the next P V;
     // returns this lane's sum of the packed (bf16) P.  k-step ks of P V
     // takes registers 8 (ks % 2) .. +7 of tile ks / 2.
     auto exps = [&](float msub) -> float {
-      float lb = 0.f;
+      float lb[4] = {0.f, 0.f, 0.f, 0.f};   // four short sum chains, not one long one
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         u32x4 w;
@@ -257,11 +257,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
           // extracting 32-bit words of a bit-cast bf16x8 for the dot2
           // compiled to four reads of word 0 (hipcc, ROCm 7.2).
           w[e] = pack_bf16x2(p0, p1);
-          lb = sum_bf16x2(w[e], lb);
+          lb[e] = sum_bf16x2(w[e], lb[e]);
         }
         pk[ks] = __builtin_bit_cast(bf16x8, w);
       }
-      return lb;
+      return (lb[0] + lb[1]) + (lb[2] + lb[3]);
     };
     // Lazy running max without a per-block max.  A block's P (against the
     // current m_run) can exceed 2^8 only if its sum does, so a block whose P
