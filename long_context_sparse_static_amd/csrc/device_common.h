@@ -3,6 +3,9 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
+#include <utility>
 #include <stdint.h>
 
 #include "kernels.h"
@@ -97,6 +100,18 @@ __device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t rs, int byte_off
 __device__ __forceinline__ float mask_neg_inf(float x, int keep) {
   const uint32_t sel = (uint32_t)(keep >> 31);  // all ones when keep < 0
   return __uint_as_float((sel & 0xff800000u) | (~sel & __float_as_uint(x)));
+}
+
+// f(std::integral_constant<int, K>{}) for K = 0 .. N-1, fully expanded at
+// compile time (a #pragma unroll is only a hint, and a loop left rolled
+// turns register arrays indexed by its counter into scratch memory).
+template <class F, int... K>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, K...>) {
+  (f(std::integral_constant<int, K>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // A wave-uniform copy of a value every lane holds (kept in an SGPR).

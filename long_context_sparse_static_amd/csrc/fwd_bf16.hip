@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     goff_k[i] = 2 * (r * lk + ((pc ^ Lay::kswz(r)) << 3));   // bytes
     goff_v[i] = 2 * (r * lv + ((pc ^ Lay::vswz(r)) << 3));
   }
-  auto load_tile = [&](const bf16 *g, char *lds, const int (&goff)[Lay::LPW]) {
+  auto load_tile = [&](const bf16 *g, char *lds, const int (&goff)[Lay::LPW]) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g);
 #pragma unroll
     for (int i = 0; i < Lay::LPW; ++i)
@@ -159,15 +159,15 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // dim tile mt) is one per-lane base XOR a constant: kofs(ks) = kbase ^
   // 32 ks, vofs(mt) = vbase ^ 64 mt (D = 128; D = 64 analogously).
   const int kbase = n * RB + ((hh ^ Lay::kswz(n)) << 4);
-  auto kofs = [&](int ks) { return kbase ^ (ks << 5); };
+  auto kofs = [&](int ks) __attribute__((always_inline)) { return kbase ^ (ks << 5); };
   int vbase;
   {
     const int s = lane & 15, gi = (lane >> 4) & 1;
     vbase = (4 * hh + (s >> 2)) * RB + (((2 * gi + ((s & 3) >> 1)) ^ Lay::vswz(s >> 2)) << 4) +
             ((s & 1) << 3);
   }
-  auto vofs = [&](int mt) { return vbase ^ (mt << 6); };
-  auto v_operand = [&](const char *vt, int mt, int ks) -> bf16x8 {
+  auto vofs = [&](int mt) __attribute__((always_inline)) { return vbase ^ (mt << 6); };
+  auto v_operand = [&](const char *vt, int mt, int ks) __attribute__((always_inline)) -> bf16x8 {
     typedef short s4 __attribute__((ext_vector_type(4)));
     typedef short s8 __attribute__((ext_vector_type(8)));
     typedef __attribute__((address_space(3))) s4 lds_s4;
@@ -196,72 +196,89 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // not this wave's are computed but never read.  The LDS operands of MFMA
   // pair i + PF are read while pair i runs; a scheduling barrier per pair
   // keeps the compiler from hoisting every read.
-  auto mfma_step = [&](const char *vt, const char *kt) {
-    constexpr int PF = 2;  // prefetch distance in MFMA pairs
-    bf16x8 ak[PF + 1], av[PF + 1];
-    auto fetch = [&](int i) {
-      ak[i % (PF + 1)] = *(const bf16x8 *)(kt + kofs(i >> 1) + (i & 1) * 32 * RB);
-      av[i % (PF + 1)] = v_operand(vt, i % MT, i / MT);
+  // MFMA k of the step: the first 3 NS / 2 follow the pattern S, S, PV (S
+  // MFMA number (k / 3) 2 + k % 3, PV MFMA number k / 3), the last NS / 2 are
+  // PV MFMAs NS / 2 .. NS - 1.  Front-loading the scores lets the next vector
+  // step start on them while the step's last P V products still run; every
+  // accumulator's chain keeps at least 2 other MFMAs between its links.  The
+  // LDS operand of MFMA k + PF is read while MFMA k runs.
+  auto mfma_step = [&](const char *vt, const char *kt) __attribute__((always_inline)) {
+    constexpr int NM = 2 * NS, NSP = 3 * NS / 2, PF = 4;
+    bf16x8 op[PF + 1];
+    auto fetch = [&](auto K) __attribute__((always_inline)) {
+      constexpr int k = decltype(K)::value;
+      if constexpr (k < NSP && k % 3 != 2) {
+        constexpr int si = (k / 3) * 2 + k % 3;
+        op[k % (PF + 1)] = *(const bf16x8 *)(kt + kofs(si >> 1) + (si & 1) * 32 * RB);
+      } else {
+        constexpr int pi = k < NSP ? k / 3 : k - NS;
+        op[k % (PF + 1)] = v_operand(vt, pi % MT, pi / MT);
+      }
     };
     sc[0] = sc[1] = f32x16{};
-#pragma unroll
-    for (int i = 0; i < PF; ++i) fetch(i);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      if (i + PF < NS) fetch(i + PF);
-      sc[i & 1] = mfma_32x32x16(ak[i % (PF + 1)], bq[i >> 1], sc[i & 1]);
-      oacc[i % MT] = mfma_32x32x16(av[i % (PF + 1)], pk[i / MT], oacc[i % MT]);
+    static_for<PF>(fetch);
+    static_for<NM>([&](auto K) __attribute__((always_inline)) {
+      constexpr int k = decltype(K)::value;
+      if constexpr (k + PF < NM) fetch(std::integral_constant<int, k + PF>{});
+      if constexpr (k < NSP && k % 3 != 2) {
+        constexpr int si = (k / 3) * 2 + k % 3;
+        sc[si & 1] = mfma_32x32x16(op[k % (PF + 1)], bq[si >> 1], sc[si & 1]);
+      } else {
+        constexpr int pi = k < NSP ? k / 3 : k - NS;
+        oacc[pi % MT] = mfma_32x32x16(op[k % (PF + 1)], pk[pi / MT], oacc[pi % MT]);
+      }
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   };
 
   // Vector step of block j: causal mask, running max with rare rescale,
   // exps, packing of P and the row sum.
-  auto vector_step = [&](int j) {
+  auto vector_step = [&](int j) __attribute__((always_inline)) {
+    // (the per-element loops below are expanded with static_for: in the
+    // larger kernel variants a rolled loop would index the score registers
+    // at run time and move them to scratch memory)
     if (a.causal && j >= qb) {
       // key offset in the block = 32 t + 8 (r / 4) + 4 hh + r % 4; compared
       // against a per-lane limit so the per-register part stays an immediate
       const int lim = q_tok - j * kBlock - 4 * hh;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sc[t][r] = mask_neg_inf(sc[t][r], lim - (32 * t + 8 * (r >> 2) + (r & 3)));
+      static_for<32>([&](auto E) __attribute__((always_inline)) {
+        constexpr int t = decltype(E)::value / 16, r = decltype(E)::value % 16;
+        sc[t][r] = mask_neg_inf(sc[t][r], lim - (32 * t + 8 * (r >> 2) + (r & 3)));
+      });
     }
     if constexpr (WIN) {
       // token window: keys k <= q - window of blocks past the sink blocks
       // (only blocks holding such a key for one of this wave's queries)
       if (j >= a.sink_blk && j * kBlock <= q_wave + 31 - a.window) {
         const int lo = q_tok - a.window - j * kBlock - 4 * hh;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sc[t][r] = mask_neg_inf(sc[t][r], (32 * t + 8 * (r >> 2) + (r & 3)) - lo - 1);
+        static_for<32>([&](auto E) __attribute__((always_inline)) {
+          constexpr int t = decltype(E)::value / 16, r = decltype(E)::value % 16;
+          sc[t][r] = mask_neg_inf(sc[t][r], (32 * t + 8 * (r >> 2) + (r & 3)) - lo - 1);
+        });
       }
     }
     // P = exp2(s c - msub) of the block, packed into pk for the next P V;
     // returns this lane's sum of the packed (bf16) P.  k-step ks of P V
     // takes registers 8 (ks % 2) .. +7 of tile ks / 2.
-    auto exps = [&](float msub) -> float {
-      float lb[4] = {0.f, 0.f, 0.f, 0.f};   // four short sum chains, not one long one
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+    auto exps = [&](float msub) __attribute__((always_inline)) -> float {
+      float lb0 = 0.f, lb1 = 0.f, lb2 = 0.f, lb3 = 0.f;   // four short sum chains
+      static_for<4>([&](auto KS) __attribute__((always_inline)) {
+        constexpr int ks = decltype(KS)::value;
         u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * (ks & 1) + 2 * e;
+        static_for<4>([&](auto EE) __attribute__((always_inline)) {
+          constexpr int e = decltype(EE)::value, r = 8 * (ks & 1) + 2 * e;
           const float p0 = fast_exp2(__builtin_fmaf(sc[ks >> 1][r], c, -msub));
           const float p1 = fast_exp2(__builtin_fmaf(sc[ks >> 1][r + 1], c, -msub));
           // The packed words are built here, not read back out of a bf16x8:
           // extracting 32-bit words of a bit-cast bf16x8 for the dot2
           // compiled to four reads of word 0 (hipcc, ROCm 7.2).
           w[e] = pack_bf16x2(p0, p1);
-          lb[e] = sum_bf16x2(w[e], lb[e]);
-        }
+          float &lb = e == 0 ? lb0 : e == 1 ? lb1 : e == 2 ? lb2 : lb3;
+          lb = sum_bf16x2(w[e], lb);
+        });
         pk[ks] = __builtin_bit_cast(bf16x8, w);
-      }
-      return (lb[0] + lb[1]) + (lb[2] + lb[3]);
+      });
+      return (lb0 + lb1) + (lb2 + lb3);
     };
     // Lazy running max without a per-block max.  A block's P (against the
     // current m_run) can exceed 2^8 only if its sum does, so a block whose P
@@ -298,14 +315,14 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
            a.ix.n_kblocks, kFwdThreads);
   RowsIter<kFwdQB> it;
   it.start(a.ix.n_kblocks, min(tile * kFwdQB + kFwdQB - 1, nqb - 1) & ~63);
-  auto advance = [&]() -> WalkPos {
+  auto advance = [&]() __attribute__((always_inline)) -> WalkPos {
     WalkPos p;
     p.valid = it.next(pb);
     p.j = it.j;
     p.mask = it.mask;
     return p;
   };
-  auto listed = [&](const WalkPos &p) { return p.valid && q_valid && ((p.mask >> my_r) & 1u); };
+  auto listed = [&](const WalkPos &p) __attribute__((always_inline)) { return p.valid && q_valid && ((p.mask >> my_r) & 1u); };
 
   // Walk window at even phase 2t: prev = block t-1, cur = t, nxt = t+1.
   WalkPos prev{false, 0, 0u}, cur = advance(), nxt{false, 0, 0u};
@@ -326,28 +343,28 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // "matrix-core step, then vector step": the register allocator then sees
   // straight-line state updates (a shared loop that switched roles by wave
   // made it copy the accumulators on every step).
-  auto shift = [&]() {
+  auto shift = [&]() __attribute__((always_inline)) {
     prev = cur;
     cur = nxt;
     if (nxt.valid) nxt = advance();
   };
-  auto even_phase = [&]() {
+  auto even_phase = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   // Tile loads of even phase 2t, issued by group B (in its vector step, so
   // the matrix-core waves never queue behind the address unit).
-  auto issue_loads = [&](auto PAR) {
+  auto issue_loads = [&](auto PAR) __attribute__((always_inline)) {
     constexpr int P = decltype(PAR)::value;
     if (nxt.valid) load_tile(kg + (size_t)nxt.j * kBlock * lk, P ? k0 : k1, goff_k);
     if (cur.valid) load_tile(vg + (size_t)cur.j * kBlock * lv, P ? v1 : v0, goff_v);
   };
-  auto matrix_phase = [&](auto PAR) {
+  auto matrix_phase = [&](auto PAR) __attribute__((always_inline)) {
     constexpr int P = decltype(PAR)::value;
     mfma_step(P ? v0 : v1, P ? k1 : k0);
   };
   // vector step of a listed block; otherwise P = 0 for the next P V
-  auto vector_or_zero = [&](const WalkPos &p) {
+  auto vector_or_zero = [&](const WalkPos &p) __attribute__((always_inline)) {
     if (listed(p)) {
       vector_step(p.j);
     } else {
@@ -355,7 +372,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
       for (int ks = 0; ks < 4; ++ks) pk[ks] = bf16x8{};
     }
   };
-  auto step_a = [&](auto PAR, int t) -> bool {
+  auto step_a = [&](auto PAR, int t) __attribute__((always_inline)) -> bool {
     if (t > 0) shift();
     if (!prev.valid && !cur.valid) return false;
     even_phase();
@@ -364,7 +381,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     vector_or_zero(cur);
     return true;
   };
-  auto step_b = [&](auto PAR, int t) -> bool {
+  auto step_b = [&](auto PAR, int t) __attribute__((always_inline)) -> bool {
     if (t > 0) shift();
     if (!prev.valid && !cur.valid) return false;
     even_phase();
