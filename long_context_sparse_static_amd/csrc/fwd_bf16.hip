@@ -13,9 +13,9 @@
 // blocks of one (batch, head); each wave owns 32 query rows.  Waves 0-3
 // (group A, query blocks 0-1) and 4-7 (group B, query blocks 2-3) sit in
 // pairs on the four SIMDs (wave w and w+4 share SIMD w).
-//   * Ping-pong: per key block a wave runs a matrix-core step (P V of the
-//     previous block and S of this block: 32 MFMAs) and a vector step
-//     (mask, max, exp, pack: ~120 VALU).  Group B runs one step behind group
+//   * Ping-pong: per key block a wave runs a matrix-core step (P V and row
+//     sum of the previous block and S of this block: 32 + 4 MFMAs) and a
+//     vector step (mask, exp, pack, overflow test: ~100 VALU).  Group B runs one step behind group
 //     A and every step ends at a workgroup barrier, so on each SIMD one wave
 //     is in its matrix-core step while the other is in its vector step: the
 //     two kinds of work overlap instead of queueing behind each other.
@@ -36,12 +36,14 @@
 //     V reaches the matrix cores through the transposing LDS read
 //     (ds_read_b64_tr_b16) for O^T += V^T P^T; P goes fp32 -> bf16 (RNE).
 //   * Online softmax in base 2 with scale*log2(e) folded into one FMA; the
-//     running max is only moved when a block's P sum (against it) exceeds
-//     2^8, so neither a per-block max nor the O rescale runs on most blocks
-//     (exact: the final O / l uses the same reference point for both sums,
-//     and no P exceeds 2^8).  The row sum l adds the same
-//     bf16-rounded P that enters the P V product (two per dot2 instruction),
-//     so numerator and denominator see identical weights.
+//     running max is only moved when a block holds a P (against it) of 2^64
+//     or more, found from the top exponent bit of the packed bf16 P (held
+//     as 2^-63 P), so neither a per-block max nor the O rescale runs on most
+//     blocks (exact: the final O / l uses the same reference point for both
+//     sums).  The row sum l runs on the matrix cores (four 16x16x32 MFMAs
+//     per block against a 0/1 selector) over the same bf16-rounded P that
+//     enters the P V product, so numerator and denominator see identical
+//     weights; on the vector units a row sum cost more than the MFMAs do.
 #include <type_traits>
 
 #include "device_common.h"
@@ -55,6 +57,7 @@ constexpr int kFwdWaves = 8;                 // waves per workgroup
 constexpr int kFwdThreads = kFwdWaves * 64;
 constexpr int kFwdQB = 4;                    // query blocks per workgroup
 constexpr int kLoadWaves = 4;                // waves that issue the tile loads (group B)
+constexpr float kFwdBias = 63.f;             // P is held as 2^-63 P (see the vector step; 0x1p63f below)
 
 // LDS tile layout for direct global->LDS loads: 64 token rows of RB bytes,
 // no padding; 16-byte chunk c of row r is stored at chunk c ^ swz(r).
@@ -180,8 +183,23 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   f32x16 oacc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x16{};
-  float m_run = -INFINITY, l_part = 0.f;
+  float m_run = -INFINITY;
   const float c = a.scale * kLog2e;
+  // Row sums on the matrix cores: D += A P^T with v_mfma_f32_16x16x32_bf16,
+  // P^T (the registers of one P V k-step) as its B operand and a 0/1
+  // selector as A.  That B operand's k index 8 g + i (g = lane / 16) holds
+  // key 8 (g / 2) + i of query 16 (g % 2) + lane % 16, so selector rows 0
+  // and 8 take the groups with g even and rows 4 and 12 those with g odd;
+  // D register 0 of lane l (rows 0, 4, 8, 12) is then the sum of its own
+  // query l % 32.
+  bf16x8 lsel;
+  {
+    const int m = lane & 15, g_odd = (lane >> 4) & 1;
+    const bool one = g_odd ? (m == 4 || m == 12) : (m == 0 || m == 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lsel[i] = one ? (bf16)1.0f : (bf16)0.0f;
+  }
+  f32x4 lacc = f32x4{};
 
   f32x16 sc[2];   // S^T of the current block (matrix-core step -> vector step)
   bf16x8 pk[4];   // packed P of the previous block (vector step -> matrix-core step)
@@ -204,6 +222,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // LDS operand of MFMA k + PF is read while MFMA k runs.
   auto mfma_step = [&](const char *vt, const char *kt) __attribute__((always_inline)) {
     constexpr int NM = 2 * NS, NSP = 3 * NS / 2, PF = 4;
+    constexpr int RS = NS / 8;   // one row-sum MFMA after every RS trailing P V MFMAs
     bf16x8 op[PF + 1];
     auto fetch = [&](auto K) __attribute__((always_inline)) {
       constexpr int k = decltype(K)::value;
@@ -227,6 +246,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
         constexpr int pi = k < NSP ? k / 3 : k - NS;
         oacc[pi % MT] = mfma_32x32x16(op[k % (PF + 1)], pk[pi / MT], oacc[pi % MT]);
       }
+      if constexpr (k >= NSP && (k - NSP) % RS == RS - 1)
+        lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pk[(k - NSP) / RS], lacc, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -257,11 +278,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
         });
       }
     }
-    // P = exp2(s c - msub) of the block, packed into pk for the next P V;
-    // returns this lane's sum of the packed (bf16) P.  k-step ks of P V
-    // takes registers 8 (ks % 2) .. +7 of tile ks / 2.
-    auto exps = [&](float msub) __attribute__((always_inline)) -> float {
-      float lb0 = 0.f, lb1 = 0.f, lb2 = 0.f, lb3 = 0.f;   // four short sum chains
+    // P' = exp2(s c - msub) of the block, packed into pk for the next P V;
+    // returns the OR of the packed words.  k-step ks of P V takes registers
+    // 8 (ks % 2) .. +7 of tile ks / 2.
+    auto exps = [&](float msub) __attribute__((always_inline)) -> uint32_t {
+      uint32_t o0 = 0u, o1 = 0u;   // two short OR chains
       static_for<4>([&](auto KS) __attribute__((always_inline)) {
         constexpr int ks = decltype(KS)::value;
         u32x4 w;
@@ -269,24 +290,25 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
           constexpr int e = decltype(EE)::value, r = 8 * (ks & 1) + 2 * e;
           const float p0 = fast_exp2(__builtin_fmaf(sc[ks >> 1][r], c, -msub));
           const float p1 = fast_exp2(__builtin_fmaf(sc[ks >> 1][r + 1], c, -msub));
-          // The packed words are built here, not read back out of a bf16x8:
-          // extracting 32-bit words of a bit-cast bf16x8 for the dot2
-          // compiled to four reads of word 0 (hipcc, ROCm 7.2).
           w[e] = pack_bf16x2(p0, p1);
-          float &lb = e == 0 ? lb0 : e == 1 ? lb1 : e == 2 ? lb2 : lb3;
-          lb = sum_bf16x2(w[e], lb);
+          uint32_t &o = (e & 1) ? o1 : o0;
+          o |= w[e];
         });
         pk[ks] = __builtin_bit_cast(bf16x8, w);
       });
-      return (lb0 + lb1) + (lb2 + lb3);
+      return o0 | o1;
     };
-    // Lazy running max without a per-block max.  A block's P (against the
-    // current m_run) can exceed 2^8 only if its sum does, so a block whose P
-    // sum is not <= 2^8 (which also catches inf and NaN), or a row with no
-    // max yet, takes the exact path: block max, rescale to it if it is
-    // higher (so later blocks see P <= 1 again), P again.
-    float lb = exps(m_run);
-    if (__any(m_run == -INFINITY || !(lb <= 256.0f))) {
+    // Lazy running max without a per-block max.  P is kept as
+    // P' = 2^-kFwdBias P, P taken against the running max m_run, so the
+    // top exponent bit of a packed bf16 P' (bit 14 of each half) is set
+    // exactly when P >= 2^(kFwdBias + 1), and for inf and NaN.  A block with
+    // such a P', or a row with no max yet, takes the exact path: block max,
+    // rescale to it if it is higher (so later blocks start from P <= 1
+    // again), P' again.  Between rescales P stays below 2^64, far from
+    // fp32 overflow, and a P' of 2^-63 at the running max keeps every
+    // P that matters (P >= 2^-63) a normal number.
+    const uint32_t ow = exps(m_run + kFwdBias);
+    if (__any(m_run == -INFINITY || (ow & 0x40004000u) != 0u)) {
       float mx = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -297,13 +319,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
       const bool need = mc > m_run;
       const float m_new = need ? mc : m_run;
       const float alpha = m_new == m_run ? 1.0f : fast_exp2(m_run - m_new);
-      l_part *= alpha;
+      lacc[0] *= alpha;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) oacc[mt] *= alpha;
       m_run = m_new;
-      lb = exps(m_run == -INFINITY ? 0.f : m_run);
+      exps(m_run == -INFINITY ? 0.f : m_run + kFwdBias);
     }
-    l_part += lb;
   };
 
   // The first matrix-core step multiplies pk = 0 by slot v1 before any
@@ -405,7 +426,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   }
 
   if (!q_valid) return;
-  const float l_tot = xor32_sum(l_part);
+  const float l_tot = lacc[0];   // sum of P' of the row (bf16-rounded, as in P V)
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   bf16 *orow = (bf16 *)a.o + (DENSE ? dense_base : a.os.at(bb, head)) + (size_t)q_tok * lo_;
 #pragma unroll
@@ -418,7 +439,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
       *(u32x2 *)(orow + 32 * mt + 8 * g + 4 * hh) = w;
     }
   if (hh == 0)
-    a.lse[(size_t)bh * a.L + q_tok] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    // 2^63 l' = l exactly (a power-of-two scale): log2 of it, not of l', so
+    // the LSE keeps full precision
+    a.lse[(size_t)bh * a.L + q_tok] = l_tot > 0.f ? (m_run + fast_log2(l_tot * 0x1p63f)) * kLn2 : -INFINITY;
 }
 
 template <int D, bool WIN, bool DENSE>
