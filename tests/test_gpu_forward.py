@@ -222,7 +222,7 @@ def test_bf16_mixed_heads_32k_sampled():
         assert_bf16_close(as_f64(lse[0, h, idx]), wlse, f"mixed LSE head {h}")
 
 
-@pytest.mark.parametrize("kind", ["rising", "spikes"])
+@pytest.mark.parametrize("kind", ["rising", "spikes", "thresholds"])
 def test_running_max_paths(kind):
     """Inputs that drive the forward's running-max paths hard: scores that
     rise block after block along the key axis (the max moves again and
@@ -240,6 +240,14 @@ def test_running_max_paths(kind):
         u = torch.randn(d, generator=g)
         q += 2.0 * u
         k += (torch.arange(L, dtype=torch.float32) / 64.0 * 0.35)[:, None] * u
+    elif kind == "thresholds":
+        # one query meets keys whose scores (base 2, scale folded in) sit about
+        # 50, 70 and 330 above the rest, in that walk order: 50 stays under
+        # the forward's 2^64 rescale threshold (P up to 2^50 against a stale
+        # max), 70 crosses it, and 330 would overflow fp32 without the rescale
+        qi = L - 5
+        for blk, alpha in ((2, 3.07), (5, 4.3), (8, 20.2)):
+            k[:, :, blk * 64 + 11] = q[:, :, qi] * alpha
     else:
         k[:, :, 5 * 64 + 7] = q[:, :, -1] * 10.0     # scores ~160 (base 2) above the rest
         k[:, :, 9 * 64 + 40] = -q[:, :, -1] * 10.0
