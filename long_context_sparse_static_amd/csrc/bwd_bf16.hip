@@ -440,7 +440,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
     const bool wedge = WIN && kb >= a.sink_blk && i * kBlock + 63 >= k_wave + a.window;
     f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
     bf16x8 bp[2][2], bds[2][2];
-    float l2[16], dl[16];
+    // LSE2 and D of both query halves, read from LDS during the score stage
+    // (one 4-float read per MFMA slot), long before the gradient VALU needs
+    // them: read right before their use, each read waited for every operand
+    // read still in flight and stalled the matrix stream on every fourth
+    // element.
+    f32x4 l2v[2][4], dlv[2][4];
     bf16x8 opnd[PF + 1];
     // operand of MFMA k
     auto fetch = [&](int k) __attribute__((always_inline)) {
@@ -470,28 +475,38 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
     };
     // softmax-gradient VALU of half m, element r (query offset 32 m +
     // 8 (r / 4) + 4 hh + r % 4; masked when the key is later)
-    auto grad_elem = [&](int m, int r) __attribute__((always_inline)) {
-      if ((r & 3) == 0) {
-        const f32x4 lq = *(const f32x4 *)(lv + 32 * m + 8 * (r >> 2) + 4 * hh);
-        const f32x4 dq = *(const f32x4 *)(ev + 32 * m + 8 * (r >> 2) + 4 * hh);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          l2[r + e] = lq[e];
-          dl[r + e] = dq[e];
-        }
-      }
+    // vector read v (0 .. 15) of the score stage: half v / 8, LSE2 or D,
+    // group v % 4 (query offset 8 g + 4 hh .. +3 of the half)
+    auto read_vec = [&](int v) __attribute__((always_inline)) {
+      const int m = v >> 3, g = v & 3;
+      const float *src = (v & 4) ? ev : lv;
+      const f32x4 x = *(const f32x4 *)(src + 32 * m + 8 * g + 4 * hh);
+      if (v & 4) dlv[m][g] = x;
+      else l2v[m][g] = x;
+    };
+    // The softmax-gradient VALU of element r of half m in two parts, each a
+    // short dependency chain; a slot runs part A of its elements and part B
+    // of the previous slot's, so no slot waits on its own exp before the
+    // next MFMA can issue.
+    //   A: P = exp2(S c - LSE2), into s
+    auto grad_a = [&](int m, int r) __attribute__((always_inline)) {
+      s[m][r] = fast_exp2(__builtin_fmaf(s[m][r], c, -l2v[m][r >> 2][r & 3]));
+    };
+    //   B: masks, dS = P (dP - D) into dp; packing of each completed 8
+    auto grad_b = [&](int m, int r) __attribute__((always_inline)) {
       const int lim = k_tok - i * kBlock - 32 * m - 4 * hh;
-      float p = fast_exp2(__builtin_fmaf(s[m][r], c, -l2[r]));
+      float p = s[m][r];
       if (diag && 8 * (r >> 2) + (r & 3) < lim) p = 0.f;
       if (wedge && 8 * (r >> 2) + (r & 3) >= lim + a.window) p = 0.f;
       s[m][r] = p;
-      dp[m][r] = p * (dp[m][r] - dl[r]);
+      dp[m][r] = p * (dp[m][r] - dlv[m][r >> 2][r & 3]);
       if (r == 7 || r == 15) {
         const int half = r >> 3;
         bp[m][half] = pack_half(s[m], half);
         bds[m][half] = pack_half(dp[m], half);
       }
     };
+    constexpr int E = 16 / (2 * KS);   // gradient elements per MFMA slot
     auto stage = [&](auto STAGE) __attribute__((always_inline)) {
       constexpr int st = decltype(STAGE)::value;
 #pragma unroll
@@ -499,10 +514,27 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
         const int k = st * 2 * KS + kk;
         if (k + PF < NM) fetch(k + PF);
         mfma_k(k);
-        // 16 VALU elements of a half spread over the 2 KS MFMAs of a stage
+        if constexpr (st == 0) {
+#pragma unroll
+          for (int v = kk * E; v < (kk + 1) * E; ++v) read_vec(v);
+        }
+        // the 16 elements of half st - 1 over the 2 KS slots of stages 1
+        // and 2; part B of a stage's last slot runs in the next stage's
+        // first slot (its packed P and dS are needed from that stage's
+        // middle on)
         if constexpr (st == 1 || st == 2) {
 #pragma unroll
-          for (int r = kk * 16 / (2 * KS); r < (kk + 1) * 16 / (2 * KS); ++r) grad_elem(st - 1, r);
+          for (int r = kk * E; r < (kk + 1) * E; ++r) grad_a(st - 1, r);
+        }
+        if constexpr (st >= 1 && st <= 3) {
+          if (kk > 0 && st <= 2) {
+#pragma unroll
+            for (int r = (kk - 1) * E; r < kk * E; ++r) grad_b(st - 1, r);
+          }
+          if (kk == 0 && st >= 2) {
+#pragma unroll
+            for (int r = 16 - E; r < 16; ++r) grad_b(st - 2, r);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
