@@ -303,14 +303,24 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
 // ----------------------------------------------------------------------------
 // dK, dV: one workgroup per 128 key tokens (two key blocks), union of their
-// CSC lists.  Per wave (32 keys, lane = key), per 32-query half m of a listed
-// query block:
-//   S = Q K^T, dP = dO V^T, P = exp2(S c - LSE2), dS = P * (dP - D)
-//   dV^T += dO^T P,  dK^T += Q^T dS
+// CSC lists.  8 waves as 4 pairs; pair p (waves p and p + 4, which share
+// SIMD p) owns 32 keys (lane = key).  Per listed query block, per 32-query
+// half m:
+//   wave p      S = Q K^T, P = exp2(S c - LSE2) (masked);  P (fp32) to LDS;
+//               dV^T += dO^T P
+//   wave p + 4  dP = dO V^T;  after the exchange barrier, with the pair's P:
+//               dS = P * (dP - D);  dK^T += Q^T dS
+// Each wave holds one accumulator set and one of K / V, so both waves of a
+// pair fit on their SIMD at once and the SIMD interleaves the pair's matrix
+// and vector work (a single wave holding everything needs about 400
+// registers and runs alone, issuing the vector work between its own MFMAs).
 // Q and dO are read as rows and transposed (kBothRead).
 // ----------------------------------------------------------------------------
+constexpr int kDkvWaves = 8;
+constexpr int kDkvThreads = kDkvWaves * 64;
+
 template <int D, bool WIN, bool DENSE>
-__global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using QT = SwzTile<D, kBothRead>;
   constexpr int KS = D / 16, MT = D / 32;
   __shared__ __attribute__((aligned(1024))) char q0[QT::TILE];
@@ -321,6 +331,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
   __shared__ __attribute__((aligned(256))) float l1[kBlock];
   __shared__ __attribute__((aligned(256))) float e0[kBlock];
   __shared__ __attribute__((aligned(256))) float e1[kBlock];
+  // the pairs' P exchange: pex[pair][c][lane] holds registers 4 (c % 4) ..
+  // +3 of half c / 4 of that lane (consecutive lanes, consecutive 16 bytes)
+  __shared__ __attribute__((aligned(1024))) f32x4 pex[4][8][64];
   extern __shared__ uint32_t dyn_lds[];
 
   const int nkb = a.ix.n_kblocks, nqb = a.ix.n_qblocks;
@@ -367,30 +380,32 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, hh = lane >> 5;
-  const int my_r = wave >> 1;
+  const bool is_x = wave < 4;      // P / dV side of the pair (else dS / dK)
+  const int pair = wave & 3;
+  const int my_r = pair >> 1;
   const int kb = krows[my_r];
   const bool k_valid = kb >= 0;
-  const int k_wave = kb * kBlock + (wave & 1) * 32;  // first key of this wave
+  const int k_wave = kb * kBlock + (pair & 1) * 32;  // first key of this pair
   const int k_tok = k_wave + n;
-  const bf16 *kp = (const bf16 *)a.k + (DENSE ? dense_base : a.ks.at(bb, head)) +
-                   (size_t)k_tok * (DENSE ? D : a.ks.l);
-  const bf16 *vp = (const bf16 *)a.v + (DENSE ? dense_base : a.vs.at(bb, head)) +
-                   (size_t)k_tok * (DENSE ? D : a.vs.l);
 
-  bf16x8 bk[KS], bv[KS];
+  // K (P side) or V (dS side) of the pair's keys: the B operand of S / dP
+  bf16x8 bkv[KS];
+  {
+    const bf16 *src = is_x ? (const bf16 *)a.k + (DENSE ? dense_base : a.ks.at(bb, head)) +
+                                 (size_t)k_tok * (DENSE ? D : a.ks.l)
+                           : (const bf16 *)a.v + (DENSE ? dense_base : a.vs.at(bb, head)) +
+                                 (size_t)k_tok * (DENSE ? D : a.vs.l);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    bk[ks] = k_valid ? *(const bf16x8 *)(kp + ks * 16 + hh * 8) : bf16x8{};
-    bv[ks] = k_valid ? *(const bf16x8 *)(vp + ks * 16 + hh * 8) : bf16x8{};
+    for (int ks = 0; ks < KS; ++ks) bkv[ks] = k_valid ? *(const bf16x8 *)(src + ks * 16 + hh * 8) : bf16x8{};
   }
   const float c = a.scale * kLog2e;
-  f32x16 dk[MT], dv[MT];
+  f32x16 acc[MT];   // dV^T (P side) or dK^T (dS side) of the pair's keys
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) dk[mt] = dv[mt] = f32x16{};
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
 
   QT rd;
   rd.init_reads(lane);
-  typename QT::template Loader<kBwdWaves> ldq, ldo;   // Q and dO tiles (own row strides)
+  typename QT::template Loader<kDkvWaves> ldq, ldo;   // Q and dO tiles (own row strides)
   ldq.init(wave, lane, lq);
   ldo.init(wave, lane, ldo_l);
   // the two 64-float per-token vectors of a query block: wave 0 loads LSE2,
@@ -410,7 +425,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
   RowsBitmap<kBwdTB> pb;
   pb.init(dyn_lds, nqb);
   pb.build_rows(a.ix.col_ptr + (size_t)hidx * (nkb + 1), krows, a.ix.nnz, a.ix.row_idx, nqb,
-                kBwdThreads);
+                kDkvThreads);
   RowsIter<kBwdTB> it;
   it.start(nqb, (krows[0] + 63) & ~63);
   auto advance = [&]() __attribute__((always_inline)) -> BwdPos {
@@ -422,129 +437,153 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
   };
   auto listed = [&](const BwdPos &p) __attribute__((always_inline)) { return p.valid && k_valid && ((p.mask >> my_r) & 1u); };
 
-  // One query block as one explicit stream of 8 KS MFMAs (one wave per SIMD,
-  // so the wave itself must keep the matrix core fed):
-  //   i in [0, 2KS)      S and dP of query half 0 (row operands)
-  //   i in [2KS, 4KS)    S and dP of half 1, with half 0's softmax-gradient
-  //                      VALU spread between them
-  //   i in [4KS, 6KS)    dV, dK of half 0 (transposed operands), with half
-  //                      1's VALU spread between them
-  //   i in [6KS, 8KS)    dV, dK of half 1
-  // The LDS operand of MFMA i + PF is read while MFMA i runs; a scheduling
-  // barrier after each MFMA keeps this order.
-  auto block_work = [&](const char *qt, const char *ot, const float *lv, const float *ev, int i) __attribute__((always_inline)) {
-    constexpr int NM = 8 * KS;       // MFMAs per query block
-    constexpr int PF = 4;            // operand prefetch distance
+  // An explicit stream of N MFMAs whose A operands come from LDS: the
+  // operand of MFMA k + PF is read while MFMA k runs; a scheduling barrier
+  // after each MFMA keeps this order.
+  // between(K) runs after MFMA K: vector work placed in the stream.
+  auto stream = [&](auto NN, auto fetch, auto mfma, auto between) __attribute__((always_inline)) {
+    constexpr int N = decltype(NN)::value, PF = 4;
+    bf16x8 op[PF + 1];
+    static_for<PF>([&](auto K) __attribute__((always_inline)) { op[decltype(K)::value] = fetch(K); });
+    static_for<N>([&](auto K) __attribute__((always_inline)) {
+      constexpr int k = decltype(K)::value;
+      if constexpr (k + PF < N) op[(k + PF) % (PF + 1)] = fetch(std::integral_constant<int, k + PF>{});
+      mfma(K, op[k % (PF + 1)]);
+      between(K);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // S or dP, half 0 then half 1: MFMA k is half k / KS, k-step k % KS
+  auto scores = [&](const char *tile, f32x16 (&sc)[2], auto between) __attribute__((always_inline)) {
+    sc[0] = sc[1] = f32x16{};
+    stream(
+        std::integral_constant<int, 2 * KS>{},
+        [&](auto K) __attribute__((always_inline)) {
+          constexpr int k = decltype(K)::value;
+          return rd.row(tile, k / KS, k % KS);
+        },
+        [&](auto K, const bf16x8 &op) __attribute__((always_inline)) {
+          constexpr int k = decltype(K)::value;
+          sc[k / KS] = mfma_32x32x16(op, bkv[k % KS], sc[k / KS]);
+        },
+        between);
+  };
+  // acc^T += tile^T X for both halves: MFMA k is half k / (2 MT), operand
+  // half (k / MT) % 2, dim tile k % MT
+  auto accumulate = [&](const char *tile, const bf16x8 (&bx)[2][2], auto between) __attribute__((always_inline)) {
+    stream(
+        std::integral_constant<int, 4 * MT>{},
+        [&](auto K) __attribute__((always_inline)) {
+          constexpr int k = decltype(K)::value, m = k / (2 * MT), half = (k / MT) % 2;
+          return rd.tr(tile, k % MT, 2 * m + half);
+        },
+        [&](auto K, const bf16x8 &op) __attribute__((always_inline)) {
+          constexpr int k = decltype(K)::value, m = k / (2 * MT), half = (k / MT) % 2;
+          acc[k % MT] = mfma_32x32x16(op, bx[m][half], acc[k % MT]);
+        },
+        between);
+  };
+  auto nothing = [](auto) __attribute__((always_inline)) {};
+  // P side, before the exchange: S; per half the causal / token-window
+  // masks as -inf scores (a uniform branch per block; element r of half m is
+  // query 32 m + 8 (r / 4) + 4 hh + r % 4 of block i), P, P to LDS, packed
+  // P.  Half 0's vector work runs between half 1's score MFMAs.
+  auto p_side = [&](const char *qt, const float *lv, int i, bf16x8 (&bp)[2][2]) __attribute__((always_inline)) {
+    f32x16 s[2];
+    const int lim0 = k_tok - i * kBlock - 4 * hh;   // keys later than the query: offset < lim
     const bool diag = a.causal && kb >= i;
-    // token window: queries q >= k + window, for keys past the sink blocks
     const bool wedge = WIN && kb >= a.sink_blk && i * kBlock + 63 >= k_wave + a.window;
-    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-    bf16x8 bp[2][2], bds[2][2];
-    // LSE2 and D of both query halves, read from LDS during the score stage
-    // (one 4-float read per MFMA slot), long before the gradient VALU needs
-    // them: read right before their use, each read waited for every operand
-    // read still in flight and stalled the matrix stream on every fourth
-    // element.
-    f32x4 l2v[2][4], dlv[2][4];
-    bf16x8 opnd[PF + 1];
-    // operand of MFMA k
-    auto fetch = [&](int k) __attribute__((always_inline)) {
-      bf16x8 v;
-      if (k < 4 * KS) {                 // scores: k = 4 ks' + 2 m' + which
-        const int m = k / (2 * KS), kk = k % (2 * KS), ks = kk >> 1;
-        v = rd.row((kk & 1) ? ot : qt, m, ks);
-      } else {                          // accumulation: half, mt, which
-        const int kk = k - 4 * KS, m = kk / (4 * MT), r = kk % (4 * MT);
-        const int half = r / (2 * MT), mt = (r % (2 * MT)) >> 1;
-        v = rd.tr((r & 1) ? qt : ot, mt, 2 * m + half);
-      }
-      opnd[k % (PF + 1)] = v;
-    };
-    auto mfma_k = [&](int k) __attribute__((always_inline)) {
-      const bf16x8 av = opnd[k % (PF + 1)];
-      if (k < 4 * KS) {
-        const int m = k / (2 * KS), kk = k % (2 * KS), ks = kk >> 1;
-        if (kk & 1) dp[m] = mfma_32x32x16(av, bv[ks], dp[m]);
-        else s[m] = mfma_32x32x16(av, bk[ks], s[m]);
+    // item t of half m: 0 masks, 1 .. 4 P of register group t - 1, 5 packing
+    auto item = [&](auto M, auto T) __attribute__((always_inline)) {
+      constexpr int m = decltype(M)::value, t = decltype(T)::value;
+      if constexpr (t == 0) {
+        if (diag) {
+          static_for<16>([&](auto R) __attribute__((always_inline)) {
+            constexpr int r = decltype(R)::value;
+            s[m][r] = mask_neg_inf(s[m][r], (32 * m + 8 * (r >> 2) + (r & 3)) - lim0);
+          });
+        }
+        if constexpr (WIN) {
+          // queries at or past key + window: offset >= lim + window
+          if (wedge) {
+            const int hi = lim0 + a.window - 1;
+            static_for<16>([&](auto R) __attribute__((always_inline)) {
+              constexpr int r = decltype(R)::value;
+              s[m][r] = mask_neg_inf(s[m][r], hi - (32 * m + 8 * (r >> 2) + (r & 3)));
+            });
+          }
+        }
+      } else if constexpr (t <= 4) {
+        constexpr int g = t - 1;
+        const f32x4 l2 = *(const f32x4 *)(lv + 32 * m + 8 * g + 4 * hh);
+        f32x4 p;
+        static_for<4>([&](auto E) __attribute__((always_inline)) {
+          constexpr int e = decltype(E)::value, r = 4 * g + e;
+          p[e] = fast_exp2(__builtin_fmaf(s[m][r], c, -l2[e]));
+          s[m][r] = p[e];
+        });
+        pex[pair][4 * m + g][lane] = p;
       } else {
-        const int kk = k - 4 * KS, m = kk / (4 * MT), r = kk % (4 * MT);
-        const int half = r / (2 * MT), mt = (r % (2 * MT)) >> 1;
-        if (r & 1) dk[mt] = mfma_32x32x16(av, bds[m][half], dk[mt]);
-        else dv[mt] = mfma_32x32x16(av, bp[m][half], dv[mt]);
+        bp[m][0] = pack_half(s[m], 0);
+        bp[m][1] = pack_half(s[m], 1);
       }
     };
-    // softmax-gradient VALU of half m, element r (query offset 32 m +
-    // 8 (r / 4) + 4 hh + r % 4; masked when the key is later)
-    // vector read v (0 .. 15) of the score stage: half v / 8, LSE2 or D,
-    // group v % 4 (query offset 8 g + 4 hh .. +3 of the half)
-    auto read_vec = [&](int v) __attribute__((always_inline)) {
-      const int m = v >> 3, g = v & 3;
-      const float *src = (v & 4) ? ev : lv;
-      const f32x4 x = *(const f32x4 *)(src + 32 * m + 8 * g + 4 * hh);
-      if (v & 4) dlv[m][g] = x;
-      else l2v[m][g] = x;
-    };
-    // The softmax-gradient VALU of element r of half m in two parts, each a
-    // short dependency chain; a slot runs part A of its elements and part B
-    // of the previous slot's, so no slot waits on its own exp before the
-    // next MFMA can issue.
-    //   A: P = exp2(S c - LSE2), into s
-    auto grad_a = [&](int m, int r) __attribute__((always_inline)) {
-      s[m][r] = fast_exp2(__builtin_fmaf(s[m][r], c, -l2v[m][r >> 2][r & 3]));
-    };
-    //   B: masks, dS = P (dP - D) into dp; packing of each completed 8
-    auto grad_b = [&](int m, int r) __attribute__((always_inline)) {
-      const int lim = k_tok - i * kBlock - 32 * m - 4 * hh;
-      float p = s[m][r];
-      if (diag && 8 * (r >> 2) + (r & 3) < lim) p = 0.f;
-      if (wedge && 8 * (r >> 2) + (r & 3) >= lim + a.window) p = 0.f;
-      s[m][r] = p;
-      dp[m][r] = p * (dp[m][r] - dlv[m][r >> 2][r & 3]);
-      if (r == 7 || r == 15) {
-        const int half = r >> 3;
-        bp[m][half] = pack_half(s[m], half);
-        bds[m][half] = pack_half(dp[m], half);
+    const std::integral_constant<int, 0> h0;
+    const std::integral_constant<int, 1> h1;
+    scores(qt, s, [&](auto K) __attribute__((always_inline)) {
+      constexpr int k = decltype(K)::value;
+      if constexpr (k >= KS) {
+        static_for<6>([&](auto T) __attribute__((always_inline)) {
+          constexpr int t = decltype(T)::value;
+          if constexpr (KS + t * KS / 6 == k) item(h0, T);
+        });
+      }
+    });
+    static_for<6>([&](auto T) __attribute__((always_inline)) { item(h1, T); });
+  };
+  // dS side, after the exchange: dS = P (dP - D), packed; half 1's vector
+  // work runs between half 0's dK MFMAs
+  auto ds_side = [&](const char *qt, const f32x16 (&dp)[2], const float *ev) __attribute__((always_inline)) {
+    bf16x8 bds[2][2];
+    f32x4 pv[2][4], dv[2][4];
+    f32x16 ds[2];
+    // item t of half m, in the order reads of groups 0 and 1, dS of group 0,
+    // read 2, dS 1, read 3, dS 2, dS 3, packing (a group's reads two items
+    // ahead of its use)
+    auto item = [&](auto M, auto T) __attribute__((always_inline)) {
+      constexpr int m = decltype(M)::value, t = decltype(T)::value;
+      constexpr int kind = t == 8 ? 2 : (t == 0 || t == 1 || t == 3 || t == 5) ? 0 : 1;
+      constexpr int g = t == 0 ? 0 : t == 1 ? 1 : t == 2 ? 0 : t == 3 ? 2 : t == 4 ? 1 : t == 5 ? 3 : t == 6 ? 2 : 3;
+      if constexpr (kind == 0) {
+        pv[m][g] = pex[pair][4 * m + g][lane];
+        dv[m][g] = *(const f32x4 *)(ev + 32 * m + 8 * g + 4 * hh);
+      } else if constexpr (kind == 1) {
+        static_for<4>([&](auto E) __attribute__((always_inline)) {
+          constexpr int e = decltype(E)::value, r = 4 * g + e;
+          ds[m][r] = pv[m][g][e] * (dp[m][r] - dv[m][g][e]);
+        });
+      } else {
+        bds[m][0] = pack_half(ds[m], 0);
+        bds[m][1] = pack_half(ds[m], 1);
       }
     };
-    constexpr int E = 16 / (2 * KS);   // gradient elements per MFMA slot
-    auto stage = [&](auto STAGE) __attribute__((always_inline)) {
-      constexpr int st = decltype(STAGE)::value;
-#pragma unroll
-      for (int kk = 0; kk < 2 * KS; ++kk) {
-        const int k = st * 2 * KS + kk;
-        if (k + PF < NM) fetch(k + PF);
-        mfma_k(k);
-        if constexpr (st == 0) {
-#pragma unroll
-          for (int v = kk * E; v < (kk + 1) * E; ++v) read_vec(v);
-        }
-        // the 16 elements of half st - 1 over the 2 KS slots of stages 1
-        // and 2; part B of a stage's last slot runs in the next stage's
-        // first slot (its packed P and dS are needed from that stage's
-        // middle on)
-        if constexpr (st == 1 || st == 2) {
-#pragma unroll
-          for (int r = kk * E; r < (kk + 1) * E; ++r) grad_a(st - 1, r);
-        }
-        if constexpr (st >= 1 && st <= 3) {
-          if (kk > 0 && st <= 2) {
-#pragma unroll
-            for (int r = (kk - 1) * E; r < kk * E; ++r) grad_b(st - 1, r);
-          }
-          if (kk == 0 && st >= 2) {
-#pragma unroll
-            for (int r = 16 - E; r < 16; ++r) grad_b(st - 2, r);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    const std::integral_constant<int, 0> h0;
+    const std::integral_constant<int, 1> h1;
+    static_for<9>([&](auto T) __attribute__((always_inline)) { item(h0, T); });
+    accumulate(qt, bds, [&](auto K) __attribute__((always_inline)) {
+      constexpr int k = decltype(K)::value;
+      if constexpr (k < 2 * MT - 1) {
+        static_for<9>([&](auto T) __attribute__((always_inline)) {
+          constexpr int t = decltype(T)::value;
+          if constexpr (t * (2 * MT - 1) / 9 == k) item(h1, T);
+        });
       }
-    };
-#pragma unroll
-    for (int k = 0; k < PF; ++k) fetch(k);
-    stage(std::integral_constant<int, 0>{});
-    stage(std::integral_constant<int, 1>{});
-    stage(std::integral_constant<int, 2>{});
-    stage(std::integral_constant<int, 3>{});
+    });
+  };
+  // the exchange barrier: the pair's P writes are complete in LDS (not the
+  // tile loads in flight: no vmcnt wait)
+  auto exchange_barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
   BwdPos cur = advance(), nxt{false, 0, 0u};
@@ -552,37 +591,69 @@ __global__ __launch_bounds__(kBwdThreads, 1) __attribute__((amdgpu_waves_per_eu(
     nxt = advance();
     load_block(cur.j, q0, o0, l0, e0);
   }
-  auto step = [&](auto PAR) __attribute__((always_inline)) -> bool {
+  // Block of walk step t lives in slot t & 1; the next block's tiles load into
+  // the other slot while this one is computed.  Per step: barrier (tiles in,
+  // the previous P consumed), S / dP, exchange barrier, dV / dS and dK.
+  // The two roles run separate copies of the loop, so the register
+  // allocator never sees one role's values live in the other's code.
+  auto step = [&](auto PAR, auto ROLE_X) __attribute__((always_inline)) -> bool {
     constexpr int P = decltype(PAR)::value;
     if (!cur.valid) return false;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (nxt.valid) load_block(nxt.j, P ? q0 : q1, P ? o0 : o1, P ? l0 : l1, P ? e0 : e1);
-    if (listed(cur)) block_work(P ? q1 : q0, P ? o1 : o0, P ? l1 : l0, P ? e1 : e0, cur.j);
+    const char *qt = P ? q1 : q0, *ot = P ? o1 : o0;
+    const float *lv = P ? l1 : l0, *ev = P ? e1 : e0;
+    const bool lst = listed(cur);
+    if constexpr (decltype(ROLE_X)::value) {
+      bf16x8 bp[2][2];
+      if (lst) p_side(qt, lv, cur.j, bp);
+      exchange_barrier();
+      if (lst) accumulate(ot, bp, nothing);
+    } else {
+      f32x16 dp[2];
+      if (lst) scores(ot, dp, nothing);
+      exchange_barrier();
+      if (lst) ds_side(qt, dp, ev);
+    }
     cur = nxt;
     if (nxt.valid) nxt = advance();
     return true;
   };
   const std::integral_constant<int, 0> even;
   const std::integral_constant<int, 1> odd;
-  while (step(even) && step(odd)) {
+  if (is_x) {
+    while (step(even, std::true_type{}) && step(odd, std::true_type{})) {
+    }
+  } else {
+    while (step(even, std::false_type{}) && step(odd, std::false_type{})) {
+    }
   }
 
   if (!k_valid) return;
-  bf16 *dko = (bf16 *)a.dk + (DENSE ? dense_base : a.dks.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.dks.l);
-  bf16 *dvo = (bf16 *)a.dv + (DENSE ? dense_base : a.dvs.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.dvs.l);
+  if (is_x) {
+    bf16 *dvo = (bf16 *)a.dv + (DENSE ? dense_base : a.dvs.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.dvs.l);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x2 wk, wv;
-      wk[0] = pack_bf16x2(dk[mt][4 * g] * a.scale, dk[mt][4 * g + 1] * a.scale);
-      wk[1] = pack_bf16x2(dk[mt][4 * g + 2] * a.scale, dk[mt][4 * g + 3] * a.scale);
-      wv[0] = pack_bf16x2(dv[mt][4 * g], dv[mt][4 * g + 1]);
-      wv[1] = pack_bf16x2(dv[mt][4 * g + 2], dv[mt][4 * g + 3]);
-      *(u32x2 *)(dko + 32 * mt + 8 * g + 4 * hh) = wk;
-      *(u32x2 *)(dvo + 32 * mt + 8 * g + 4 * hh) = wv;
-    }
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[mt][4 * g], acc[mt][4 * g + 1]);
+        w[1] = pack_bf16x2(acc[mt][4 * g + 2], acc[mt][4 * g + 3]);
+        *(u32x2 *)(dvo + 32 * mt + 8 * g + 4 * hh) = w;
+      }
+  } else {
+    bf16 *dko = (bf16 *)a.dk + (DENSE ? dense_base : a.dks.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.dks.l);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[mt][4 * g] * a.scale, acc[mt][4 * g + 1] * a.scale);
+        w[1] = pack_bf16x2(acc[mt][4 * g + 2] * a.scale, acc[mt][4 * g + 3] * a.scale);
+        *(u32x2 *)(dko + 32 * mt + 8 * g + 4 * hh) = w;
+      }
+  }
 }
 
 template <int D, bool WIN, bool DENSE>
@@ -602,7 +673,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_q);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3(grid_delta), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, WIN, DENSE>), dim3(BH * k_tiles), dim3(kBwdThreads), dyn_k, s, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, WIN, DENSE>), dim3(BH * k_tiles), dim3(kDkvThreads), dyn_k, s, a);
   hipLaunchKernelGGL((bwd_dq_kernel<D, WIN, DENSE>), dim3(BH * q_tiles), dim3(kBwdThreads), dyn_q, s, a);
   return hipGetLastError();
 }
@@ -610,8 +681,9 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
 }  // namespace
 
 size_t bwd_bf16_lds_bytes(int d, int n_blocks) {
-  // dK/dV kernel: two Q and two dO slots, four 64-float vectors, bitmaps
-  const size_t tiles = 4 * (size_t)kBlock * 2 * d + 4 * kBlock * sizeof(float);
+  // dK/dV kernel: two Q and two dO slots, four 64-float vectors, the P
+  // exchange (4 pairs x 8 KB), bitmaps
+  const size_t tiles = 4 * (size_t)kBlock * 2 * d + 4 * kBlock * sizeof(float) + 4 * 8 * 64 * 16;
   return tiles + RowsBitmap<kBwdTB>::lds_bytes(n_blocks);
 }
 

@@ -31,7 +31,7 @@ def kernel_resources(src, tmp_path):
             cur = m.group(1)
             out[cur] = {}
             continue
-        m = re.search(r"remark: (VGPRs|AGPRs|ScratchSize \[bytes/lane\]): (\d+)", line)
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|ScratchSize \[bytes/lane\]): (\d+)", line)
         if m and cur:
             out[cur][m.group(1).split()[0]] = int(m.group(2))
     return out
@@ -44,5 +44,8 @@ def test_no_scratch_and_registers_fit(src, tmp_path):
     kernels = {k: v for k, v in res.items() if "kernel" in k}
     assert kernels, "no kernels reported"
     for name, r in kernels.items():
-        assert r.get("ScratchSize", 0) == 0, f"{name} uses {r['ScratchSize']} bytes of scratch per lane"
+        # every figure must have been read: a report format the parser does
+        # not match would otherwise pass vacuously
+        assert {"VGPRs", "AGPRs", "ScratchSize"} <= set(r), f"{name}: resource report not parsed: {r}"
+        assert r["ScratchSize"] == 0, f"{name} uses {r['ScratchSize']} bytes of scratch per lane"
         assert r.get("VGPRs", 0) + r.get("AGPRs", 0) <= 512, f"{name} uses too many registers: {r}"
