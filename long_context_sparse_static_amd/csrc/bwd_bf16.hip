@@ -37,7 +37,7 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = kBwdWaves * 64;
 constexpr int kBwdTB = kBwdWaves / 2;  // 64-token blocks per tile (32 rows per wave)
 
-// D = rowsum(dO * O) and the base-2 LSE (lse * log2 e; +inf for an empty
+// -D = -rowsum(dO * O) and the base-2 LSE (lse * log2 e; +inf for an empty
 // row, so that P = exp2(s - lse2) = 0 there) per token.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
@@ -61,11 +61,17 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
 #pragma unroll
   for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
   if (row < total && c == 0) {
-    a.delta[row] = acc;
+    a.delta[row] = -acc;   // -D: the dK/dV kernel starts its dP accumulator from it
     const float l = a.lse[row];
     a.lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
 }
+
+// A compile-time order of k-steps: KOrder<...>::value[i].
+template <int... J>
+struct KOrder {
+  static constexpr int value[sizeof...(J)] = {J...};
+};
 
 // Reads 16 consecutive fp32 values of a per-token vector laid out in LDS as
 // the rows of a 32x32 accumulator tile: element r is token
@@ -198,7 +204,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   float lse2 = INFINITY, dlt = 0.f;
   if (q_valid) {
     lse2 = a.lse2[(size_t)bh * a.L + q_tok];
-    dlt = a.delta[(size_t)bh * a.L + q_tok];
+    dlt = -a.delta[(size_t)bh * a.L + q_tok];
   }
 
   KT kr;
@@ -304,17 +310,18 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 // ----------------------------------------------------------------------------
 // dK, dV: one workgroup per 128 key tokens (two key blocks), union of their
 // CSC lists.  8 waves as 4 pairs; pair p (waves p and p + 4, which share
-// SIMD p) owns 32 keys (lane = key).  Per listed query block, per 32-query
-// half m:
-//   wave p      S = Q K^T, P = exp2(S c - LSE2) (masked);  P (fp32) to LDS;
-//               dV^T += dO^T P
-//   wave p + 4  dP = dO V^T;  after the exchange barrier, with the pair's P:
-//               dS = P * (dP - D);  dK^T += Q^T dS
-// Each wave holds one accumulator set and one of K / V, so both waves of a
-// pair fit on their SIMD at once and the SIMD interleaves the pair's matrix
-// and vector work (a single wave holding everything needs about 400
-// registers and runs alone, issuing the vector work between its own MFMAs).
-// Q and dO are read as rows and transposed (kBothRead).
+// SIMD p) owns 32 keys (lane = key) and splits each listed query block by
+// its 32-query halves: wave p takes half 0 and accumulates dV, wave p + 4
+// takes half 1 and accumulates dK.  Per block, each wave on its half:
+//   S = Q K^T, dP = dO V^T - D (the accumulator starts at -D),
+//   P = exp2(S c - LSE2) (masked), dS = P dP, both packed to bf16;
+// then the pair trades through LDS what the other's product needs (wave p
+// sends its dS, wave p + 4 its P) and, after the exchange barrier,
+//   wave p:      dV^T += dO^T P       wave p + 4:  dK^T += Q^T dS
+// over the whole block.  Each wave holds one accumulator set, so both fit
+// on their SIMD at once (a single wave holding all of it needs about 400
+// registers and runs alone), and the two halves of the vector work run on
+// the two waves.  Q and dO are read as rows and transposed (kBothRead).
 // ----------------------------------------------------------------------------
 constexpr int kDkvWaves = 8;
 constexpr int kDkvThreads = kDkvWaves * 64;
@@ -331,9 +338,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(256))) float l1[kBlock];
   __shared__ __attribute__((aligned(256))) float e0[kBlock];
   __shared__ __attribute__((aligned(256))) float e1[kBlock];
-  // the pairs' P exchange: pex[pair][c][lane] holds registers 4 (c % 4) ..
-  // +3 of half c / 4 of that lane (consecutive lanes, consecutive 16 bytes)
-  __shared__ __attribute__((aligned(1024))) f32x4 pex[4][8][64];
+  // the pairs' exchange: xch[pair][side][j][lane] is packed operand j (the
+  // B operand of k-step j of that half) sent by side 0 (dS of half 0) or
+  // side 1 (P of half 1); consecutive lanes, consecutive 16 bytes
+  __shared__ __attribute__((aligned(1024))) bf16x8 xch[4][2][2][64];
   extern __shared__ uint32_t dyn_lds[];
 
   const int nkb = a.ix.n_kblocks, nqb = a.ix.n_qblocks;
@@ -375,12 +383,12 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const bf16 *qg = (const bf16 *)a.q + (DENSE ? dense_base : a.qs.at(bb, head));
   const bf16 *dog = (const bf16 *)a.dout + (DENSE ? dense_base : a.dos.at(bb, head));
   const float *lseg = a.lse2 + (size_t)bh * a.L;
-  const float *dltg = a.delta + (size_t)bh * a.L;
+  const float *ndltg = a.delta + (size_t)bh * a.L;   // -D
 
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, hh = lane >> 5;
-  const bool is_x = wave < 4;      // P / dV side of the pair (else dS / dK)
+  const bool side0 = wave < 4;     // query half 0 and dV (else half 1 and dK)
   const int pair = wave & 3;
   const int my_r = pair >> 1;
   const int kb = krows[my_r];
@@ -388,18 +396,19 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int k_wave = kb * kBlock + (pair & 1) * 32;  // first key of this pair
   const int k_tok = k_wave + n;
 
-  // K (P side) or V (dS side) of the pair's keys: the B operand of S / dP
-  bf16x8 bkv[KS];
+  // K and V of the pair's keys: the B operands of S and dP
+  bf16x8 bk[KS], bv[KS];
   {
-    const bf16 *src = is_x ? (const bf16 *)a.k + (DENSE ? dense_base : a.ks.at(bb, head)) +
-                                 (size_t)k_tok * (DENSE ? D : a.ks.l)
-                           : (const bf16 *)a.v + (DENSE ? dense_base : a.vs.at(bb, head)) +
-                                 (size_t)k_tok * (DENSE ? D : a.vs.l);
+    const bf16 *kp = (const bf16 *)a.k + (DENSE ? dense_base : a.ks.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.ks.l);
+    const bf16 *vp = (const bf16 *)a.v + (DENSE ? dense_base : a.vs.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.vs.l);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) bkv[ks] = k_valid ? *(const bf16x8 *)(src + ks * 16 + hh * 8) : bf16x8{};
+    for (int ks = 0; ks < KS; ++ks) {
+      bk[ks] = k_valid ? *(const bf16x8 *)(kp + ks * 16 + hh * 8) : bf16x8{};
+      bv[ks] = k_valid ? *(const bf16x8 *)(vp + ks * 16 + hh * 8) : bf16x8{};
+    }
   }
   const float c = a.scale * kLog2e;
-  f32x16 acc[MT];   // dV^T (P side) or dK^T (dS side) of the pair's keys
+  f32x16 acc[MT];   // dV^T (side 0) or dK^T (side 1) of the pair's keys
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
 
@@ -409,12 +418,12 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   ldq.init(wave, lane, lq);
   ldo.init(wave, lane, ldo_l);
   // the two 64-float per-token vectors of a query block: wave 0 loads LSE2,
-  // wave 1 the D values (4 bytes per lane)
+  // wave 1 the -D values (4 bytes per lane)
   auto load_vec = [&](int i, float *lv, float *ev) __attribute__((always_inline)) {
     if (wave == 0)
       load_lds<4>(buffer_rsrc(lseg + (size_t)i * kBlock), 4 * lane, lv);
     else if (wave == 1)
-      load_lds<4>(buffer_rsrc(dltg + (size_t)i * kBlock), 4 * lane, ev);
+      load_lds<4>(buffer_rsrc(ndltg + (size_t)i * kBlock), 4 * lane, ev);
   };
   auto load_block = [&](int i, char *qt, char *ot, float *lv, float *ev) __attribute__((always_inline)) {
     ldq.load(qg + (size_t)i * kBlock * lq, qt);
@@ -440,8 +449,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // An explicit stream of N MFMAs whose A operands come from LDS: the
   // operand of MFMA k + PF is read while MFMA k runs; a scheduling barrier
   // after each MFMA keeps this order.
-  // between(K) runs after MFMA K: vector work placed in the stream.
-  auto stream = [&](auto NN, auto fetch, auto mfma, auto between) __attribute__((always_inline)) {
+  auto stream = [&](auto NN, auto fetch, auto mfma) __attribute__((always_inline)) {
     constexpr int N = decltype(NN)::value, PF = 4;
     bf16x8 op[PF + 1];
     static_for<PF>([&](auto K) __attribute__((always_inline)) { op[decltype(K)::value] = fetch(K); });
@@ -449,141 +457,85 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       constexpr int k = decltype(K)::value;
       if constexpr (k + PF < N) op[(k + PF) % (PF + 1)] = fetch(std::integral_constant<int, k + PF>{});
       mfma(K, op[k % (PF + 1)]);
-      between(K);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  // S or dP, half 0 then half 1: MFMA k is half k / KS, k-step k % KS
-  auto scores = [&](const char *tile, f32x16 (&sc)[2], auto between) __attribute__((always_inline)) {
-    sc[0] = sc[1] = f32x16{};
+  // the exchange barrier: the pair's operand writes are complete in LDS (not
+  // the tile loads in flight: no vmcnt wait)
+  auto exchange_barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  // Half H of block i (tiles qt / ot, vectors lv / ev): S and dP, masks,
+  // P and dS packed into bp / bds (the B operands of k-steps 2 H, 2 H + 1).
+  // Element r of a score register set is query 32 H + 8 (r / 4) + 4 hh + r % 4.
+  auto half_block = [&](auto HALF, const char *qt, const char *ot, const float *lv, const float *ev, int i,
+                        bf16x8 (&bp)[2], bf16x8 (&bds)[2]) __attribute__((always_inline)) {
+    constexpr int h = decltype(HALF)::value;
+    f32x16 s = f32x16{}, dp;
+    static_for<4>([&](auto G) __attribute__((always_inline)) {
+      constexpr int g = decltype(G)::value;
+      const f32x4 x = *(const f32x4 *)(ev + 32 * h + 8 * g + 4 * hh);
+      static_for<4>([&](auto E) __attribute__((always_inline)) { dp[4 * g + decltype(E)::value] = x[decltype(E)::value]; });
+    });
+    // S and dP interleaved (two accumulator chains): MFMA k is S (k even) or
+    // dP (k odd) of k-step k / 2
     stream(
         std::integral_constant<int, 2 * KS>{},
         [&](auto K) __attribute__((always_inline)) {
           constexpr int k = decltype(K)::value;
-          return rd.row(tile, k / KS, k % KS);
+          return rd.row(k % 2 ? ot : qt, h, k / 2);
         },
         [&](auto K, const bf16x8 &op) __attribute__((always_inline)) {
           constexpr int k = decltype(K)::value;
-          sc[k / KS] = mfma_32x32x16(op, bkv[k % KS], sc[k / KS]);
-        },
-        between);
+          if constexpr (k % 2) dp = mfma_32x32x16(op, bv[k / 2], dp);
+          else s = mfma_32x32x16(op, bk[k / 2], s);
+        });
+    // causal / token-window masks as -inf scores, one uniform branch each
+    const int lim = k_tok - i * kBlock - 32 * h - 4 * hh;   // keys later than the query: offset < lim
+    if (a.causal && kb >= i) {
+      static_for<16>([&](auto R) __attribute__((always_inline)) {
+        constexpr int r = decltype(R)::value;
+        s[r] = mask_neg_inf(s[r], (8 * (r >> 2) + (r & 3)) - lim);
+      });
+    }
+    if constexpr (WIN) {
+      // queries at or past key + window: offset >= lim + window
+      if (kb >= a.sink_blk && i * kBlock + 63 >= k_wave + a.window) {
+        const int hi = lim + a.window - 1;
+        static_for<16>([&](auto R) __attribute__((always_inline)) {
+          constexpr int r = decltype(R)::value;
+          s[r] = mask_neg_inf(s[r], hi - (8 * (r >> 2) + (r & 3)));
+        });
+      }
+    }
+    static_for<4>([&](auto G) __attribute__((always_inline)) {
+      constexpr int g = decltype(G)::value;
+      const f32x4 l2 = *(const f32x4 *)(lv + 32 * h + 8 * g + 4 * hh);
+      static_for<4>([&](auto E) __attribute__((always_inline)) {
+        constexpr int e = decltype(E)::value, r = 4 * g + e;
+        s[r] = fast_exp2(__builtin_fmaf(s[r], c, -l2[e]));   // P
+        dp[r] = s[r] * dp[r];                                  // dS
+      });
+    });
+    bp[0] = pack_half(s, 0);
+    bp[1] = pack_half(s, 1);
+    bds[0] = pack_half(dp, 0);
+    bds[1] = pack_half(dp, 1);
   };
-  // acc^T += tile^T X for both halves: MFMA k is half k / (2 MT), operand
-  // half (k / MT) % 2, dim tile k % MT
-  auto accumulate = [&](const char *tile, const bf16x8 (&bx)[2][2], auto between) __attribute__((always_inline)) {
+  // acc^T += tile^T X over the block's four k-steps: x[j] is the B operand
+  // of k-step j; MFMA k is k-step order[k / MT], dim tile k % MT
+  auto accumulate = [&](const char *tile, const bf16x8 (&x)[4], auto ORDER) __attribute__((always_inline)) {
     stream(
         std::integral_constant<int, 4 * MT>{},
         [&](auto K) __attribute__((always_inline)) {
-          constexpr int k = decltype(K)::value, m = k / (2 * MT), half = (k / MT) % 2;
-          return rd.tr(tile, k % MT, 2 * m + half);
+          constexpr int k = decltype(K)::value, j = decltype(ORDER)::value[k / MT];
+          return rd.tr(tile, k % MT, j);
         },
         [&](auto K, const bf16x8 &op) __attribute__((always_inline)) {
-          constexpr int k = decltype(K)::value, m = k / (2 * MT), half = (k / MT) % 2;
-          acc[k % MT] = mfma_32x32x16(op, bx[m][half], acc[k % MT]);
-        },
-        between);
-  };
-  auto nothing = [](auto) __attribute__((always_inline)) {};
-  // P side, before the exchange: S; per half the causal / token-window
-  // masks as -inf scores (a uniform branch per block; element r of half m is
-  // query 32 m + 8 (r / 4) + 4 hh + r % 4 of block i), P, P to LDS, packed
-  // P.  Half 0's vector work runs between half 1's score MFMAs.
-  auto p_side = [&](const char *qt, const float *lv, int i, bf16x8 (&bp)[2][2]) __attribute__((always_inline)) {
-    f32x16 s[2];
-    const int lim0 = k_tok - i * kBlock - 4 * hh;   // keys later than the query: offset < lim
-    const bool diag = a.causal && kb >= i;
-    const bool wedge = WIN && kb >= a.sink_blk && i * kBlock + 63 >= k_wave + a.window;
-    // item t of half m: 0 masks, 1 .. 4 P of register group t - 1, 5 packing
-    auto item = [&](auto M, auto T) __attribute__((always_inline)) {
-      constexpr int m = decltype(M)::value, t = decltype(T)::value;
-      if constexpr (t == 0) {
-        if (diag) {
-          static_for<16>([&](auto R) __attribute__((always_inline)) {
-            constexpr int r = decltype(R)::value;
-            s[m][r] = mask_neg_inf(s[m][r], (32 * m + 8 * (r >> 2) + (r & 3)) - lim0);
-          });
-        }
-        if constexpr (WIN) {
-          // queries at or past key + window: offset >= lim + window
-          if (wedge) {
-            const int hi = lim0 + a.window - 1;
-            static_for<16>([&](auto R) __attribute__((always_inline)) {
-              constexpr int r = decltype(R)::value;
-              s[m][r] = mask_neg_inf(s[m][r], hi - (32 * m + 8 * (r >> 2) + (r & 3)));
-            });
-          }
-        }
-      } else if constexpr (t <= 4) {
-        constexpr int g = t - 1;
-        const f32x4 l2 = *(const f32x4 *)(lv + 32 * m + 8 * g + 4 * hh);
-        f32x4 p;
-        static_for<4>([&](auto E) __attribute__((always_inline)) {
-          constexpr int e = decltype(E)::value, r = 4 * g + e;
-          p[e] = fast_exp2(__builtin_fmaf(s[m][r], c, -l2[e]));
-          s[m][r] = p[e];
+          constexpr int k = decltype(K)::value, j = decltype(ORDER)::value[k / MT];
+          acc[k % MT] = mfma_32x32x16(op, x[j], acc[k % MT]);
         });
-        pex[pair][4 * m + g][lane] = p;
-      } else {
-        bp[m][0] = pack_half(s[m], 0);
-        bp[m][1] = pack_half(s[m], 1);
-      }
-    };
-    const std::integral_constant<int, 0> h0;
-    const std::integral_constant<int, 1> h1;
-    scores(qt, s, [&](auto K) __attribute__((always_inline)) {
-      constexpr int k = decltype(K)::value;
-      if constexpr (k >= KS) {
-        static_for<6>([&](auto T) __attribute__((always_inline)) {
-          constexpr int t = decltype(T)::value;
-          if constexpr (KS + t * KS / 6 == k) item(h0, T);
-        });
-      }
-    });
-    static_for<6>([&](auto T) __attribute__((always_inline)) { item(h1, T); });
-  };
-  // dS side, after the exchange: dS = P (dP - D), packed; half 1's vector
-  // work runs between half 0's dK MFMAs
-  auto ds_side = [&](const char *qt, const f32x16 (&dp)[2], const float *ev) __attribute__((always_inline)) {
-    bf16x8 bds[2][2];
-    f32x4 pv[2][4], dv[2][4];
-    f32x16 ds[2];
-    // item t of half m, in the order reads of groups 0 and 1, dS of group 0,
-    // read 2, dS 1, read 3, dS 2, dS 3, packing (a group's reads two items
-    // ahead of its use)
-    auto item = [&](auto M, auto T) __attribute__((always_inline)) {
-      constexpr int m = decltype(M)::value, t = decltype(T)::value;
-      constexpr int kind = t == 8 ? 2 : (t == 0 || t == 1 || t == 3 || t == 5) ? 0 : 1;
-      constexpr int g = t == 0 ? 0 : t == 1 ? 1 : t == 2 ? 0 : t == 3 ? 2 : t == 4 ? 1 : t == 5 ? 3 : t == 6 ? 2 : 3;
-      if constexpr (kind == 0) {
-        pv[m][g] = pex[pair][4 * m + g][lane];
-        dv[m][g] = *(const f32x4 *)(ev + 32 * m + 8 * g + 4 * hh);
-      } else if constexpr (kind == 1) {
-        static_for<4>([&](auto E) __attribute__((always_inline)) {
-          constexpr int e = decltype(E)::value, r = 4 * g + e;
-          ds[m][r] = pv[m][g][e] * (dp[m][r] - dv[m][g][e]);
-        });
-      } else {
-        bds[m][0] = pack_half(ds[m], 0);
-        bds[m][1] = pack_half(ds[m], 1);
-      }
-    };
-    const std::integral_constant<int, 0> h0;
-    const std::integral_constant<int, 1> h1;
-    static_for<9>([&](auto T) __attribute__((always_inline)) { item(h0, T); });
-    accumulate(qt, bds, [&](auto K) __attribute__((always_inline)) {
-      constexpr int k = decltype(K)::value;
-      if constexpr (k < 2 * MT - 1) {
-        static_for<9>([&](auto T) __attribute__((always_inline)) {
-          constexpr int t = decltype(T)::value;
-          if constexpr (t * (2 * MT - 1) / 9 == k) item(h1, T);
-        });
-      }
-    });
-  };
-  // the exchange barrier: the pair's P writes are complete in LDS (not the
-  // tile loads in flight: no vmcnt wait)
-  auto exchange_barrier = [&]() __attribute__((always_inline)) {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
   BwdPos cur = advance(), nxt{false, 0, 0u};
@@ -591,13 +543,14 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     nxt = advance();
     load_block(cur.j, q0, o0, l0, e0);
   }
-  // Block of walk step t lives in slot t & 1; the next block's tiles load into
-  // the other slot while this one is computed.  Per step: barrier (tiles in,
-  // the previous P consumed), S / dP, exchange barrier, dV / dS and dK.
-  // The two roles run separate copies of the loop, so the register
-  // allocator never sees one role's values live in the other's code.
-  auto step = [&](auto PAR, auto ROLE_X) __attribute__((always_inline)) -> bool {
+  // Block of walk step t lives in slot t & 1; the next block's tiles load
+  // into the other slot while this one is computed.  Per step: barrier
+  // (tiles in, the previous exchange consumed), half block, exchange
+  // barrier, dV / dK.  The two sides run separate copies of the loop, so
+  // the register allocator never sees one side's values live in the other's.
+  auto step = [&](auto PAR, auto SIDE1) __attribute__((always_inline)) -> bool {
     constexpr int P = decltype(PAR)::value;
+    constexpr bool s1 = decltype(SIDE1)::value;
     if (!cur.valid) return false;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -605,16 +558,25 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const char *qt = P ? q1 : q0, *ot = P ? o1 : o0;
     const float *lv = P ? l1 : l0, *ev = P ? e1 : e0;
     const bool lst = listed(cur);
-    if constexpr (decltype(ROLE_X)::value) {
-      bf16x8 bp[2][2];
-      if (lst) p_side(qt, lv, cur.j, bp);
-      exchange_barrier();
-      if (lst) accumulate(ot, bp, nothing);
-    } else {
-      f32x16 dp[2];
-      if (lst) scores(ot, dp, nothing);
-      exchange_barrier();
-      if (lst) ds_side(qt, dp, ev);
+    bf16x8 x[4];   // B operands of the block's k-steps (P for dV, dS for dK)
+    if (lst) {
+      bf16x8 bp[2], bds[2];
+      half_block(std::integral_constant<int, s1 ? 1 : 0>{}, qt, ot, lv, ev, cur.j, bp, bds);
+      // send what the partner's product needs, keep the own part
+      xch[pair][s1][0][lane] = s1 ? bp[0] : bds[0];
+      xch[pair][s1][1][lane] = s1 ? bp[1] : bds[1];
+      x[2 * s1] = s1 ? bds[0] : bp[0];
+      x[2 * s1 + 1] = s1 ? bds[1] : bp[1];
+    }
+    exchange_barrier();
+    if (lst) {
+      x[2 * !s1] = xch[pair][!s1][0][lane];
+      x[2 * !s1 + 1] = xch[pair][!s1][1][lane];
+      // the own k-steps first, so the partner's operands have arrived
+      if constexpr (s1)
+        accumulate(qt, x, KOrder<2, 3, 0, 1>{});
+      else
+        accumulate(ot, x, KOrder<0, 1, 2, 3>{});
     }
     cur = nxt;
     if (nxt.valid) nxt = advance();
@@ -622,38 +584,27 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   };
   const std::integral_constant<int, 0> even;
   const std::integral_constant<int, 1> odd;
-  if (is_x) {
-    while (step(even, std::true_type{}) && step(odd, std::true_type{})) {
+  if (side0) {
+    while (step(even, std::false_type{}) && step(odd, std::false_type{})) {
     }
   } else {
-    while (step(even, std::false_type{}) && step(odd, std::false_type{})) {
+    while (step(even, std::true_type{}) && step(odd, std::true_type{})) {
     }
   }
 
   if (!k_valid) return;
-  if (is_x) {
-    bf16 *dvo = (bf16 *)a.dv + (DENSE ? dense_base : a.dvs.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.dvs.l);
+  bf16 *out = side0 ? (bf16 *)a.dv + (DENSE ? dense_base : a.dvs.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.dvs.l)
+                    : (bf16 *)a.dk + (DENSE ? dense_base : a.dks.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.dks.l);
+  const float sc = side0 ? 1.0f : a.scale;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[mt][4 * g], acc[mt][4 * g + 1]);
-        w[1] = pack_bf16x2(acc[mt][4 * g + 2], acc[mt][4 * g + 3]);
-        *(u32x2 *)(dvo + 32 * mt + 8 * g + 4 * hh) = w;
-      }
-  } else {
-    bf16 *dko = (bf16 *)a.dk + (DENSE ? dense_base : a.dks.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.dks.l);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[mt][4 * g] * a.scale, acc[mt][4 * g + 1] * a.scale);
-        w[1] = pack_bf16x2(acc[mt][4 * g + 2] * a.scale, acc[mt][4 * g + 3] * a.scale);
-        *(u32x2 *)(dko + 32 * mt + 8 * g + 4 * hh) = w;
-      }
-  }
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[mt][4 * g] * sc, acc[mt][4 * g + 1] * sc);
+      w[1] = pack_bf16x2(acc[mt][4 * g + 2] * sc, acc[mt][4 * g + 3] * sc);
+      *(u32x2 *)(out + 32 * mt + 8 * g + 4 * hh) = w;
+    }
 }
 
 template <int D, bool WIN, bool DENSE>
@@ -681,9 +632,9 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
 }  // namespace
 
 size_t bwd_bf16_lds_bytes(int d, int n_blocks) {
-  // dK/dV kernel: two Q and two dO slots, four 64-float vectors, the P
-  // exchange (4 pairs x 8 KB), bitmaps
-  const size_t tiles = 4 * (size_t)kBlock * 2 * d + 4 * kBlock * sizeof(float) + 4 * 8 * 64 * 16;
+  // dK/dV kernel: two Q and two dO slots, four 64-float vectors, the
+  // packed-operand exchange (4 pairs x 4 KB), bitmaps
+  const size_t tiles = 4 * (size_t)kBlock * 2 * d + 4 * kBlock * sizeof(float) + 4 * 4 * 64 * 16;
   return tiles + RowsBitmap<kBwdTB>::lds_bytes(n_blocks);
 }
 

@@ -58,7 +58,7 @@ struct BwdArgs {
   const float *lse;
   void *dq, *dk, *dv;
   Strides qs, ks, vs, os, dos, dqs, dks, dvs;
-  float *delta;        // workspace: D = rowsum(dO * O), [B,H,L] fp32
+  float *delta;        // workspace: -D = -rowsum(dO * O), [B,H,L] fp32
   float *lse2;         // workspace: LSE * log2(e) (+inf for empty rows), [B,H,L] fp32
   IndexView ix;
   int32_t B, H, L, d;
