@@ -70,6 +70,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
 // A compile-time order of k-steps: KOrder<...>::value[i].
 template <int... J>
 struct KOrder {
+  static constexpr int size = sizeof...(J);
   static constexpr int value[sizeof...(J)] = {J...};
 };
 
@@ -523,11 +524,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     bds[0] = pack_half(dp, 0);
     bds[1] = pack_half(dp, 1);
   };
-  // acc^T += tile^T X over the block's four k-steps: x[j] is the B operand
-  // of k-step j; MFMA k is k-step order[k / MT], dim tile k % MT
+  // acc^T += tile^T X over k-steps ORDER of the block: x[j] is the B
+  // operand of k-step j; MFMA k is k-step order[k / MT], dim tile k % MT
   auto accumulate = [&](const char *tile, const bf16x8 (&x)[4], auto ORDER) __attribute__((always_inline)) {
     stream(
-        std::integral_constant<int, 4 * MT>{},
+        std::integral_constant<int, decltype(ORDER)::size * MT>{},
         [&](auto K) __attribute__((always_inline)) {
           constexpr int k = decltype(K)::value, j = decltype(ORDER)::value[k / MT];
           return rd.tr(tile, k % MT, j);
@@ -559,24 +560,30 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const float *lv = P ? l1 : l0, *ev = P ? e1 : e0;
     const bool lst = listed(cur);
     bf16x8 x[4];   // B operands of the block's k-steps (P for dV, dS for dK)
+    const char *at = s1 ? qt : ot;   // A tile of the product: Q for dK, dO for dV
     if (lst) {
       bf16x8 bp[2], bds[2];
       half_block(std::integral_constant<int, s1 ? 1 : 0>{}, qt, ot, lv, ev, cur.j, bp, bds);
-      // send what the partner's product needs, keep the own part
+      // send what the partner's product needs, keep the own part and run
+      // its k-steps before the exchange barrier (they overlap the partner's
+      // vector work)
       xch[pair][s1][0][lane] = s1 ? bp[0] : bds[0];
       xch[pair][s1][1][lane] = s1 ? bp[1] : bds[1];
       x[2 * s1] = s1 ? bds[0] : bp[0];
       x[2 * s1 + 1] = s1 ? bds[1] : bp[1];
+      if constexpr (s1)
+        accumulate(at, x, KOrder<2, 3>{});
+      else
+        accumulate(at, x, KOrder<0, 1>{});
     }
     exchange_barrier();
     if (lst) {
       x[2 * !s1] = xch[pair][!s1][0][lane];
       x[2 * !s1 + 1] = xch[pair][!s1][1][lane];
-      // the own k-steps first, so the partner's operands have arrived
       if constexpr (s1)
-        accumulate(qt, x, KOrder<2, 3, 0, 1>{});
+        accumulate(at, x, KOrder<0, 1>{});
       else
-        accumulate(ot, x, KOrder<0, 1, 2, 3>{});
+        accumulate(at, x, KOrder<2, 3>{});
     }
     cur = nxt;
     if (nxt.valid) nxt = advance();
