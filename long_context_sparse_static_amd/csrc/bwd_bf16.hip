@@ -245,21 +245,31 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         s[t] = mfma_32x32x16(kr.row(kt, t, ks), bq[ks], s[t]);
         dp[t] = mfma_32x32x16(vr.row(vt, t, ks), bdo[ks], dp[t]);
       }
-    const bool diag = a.causal && j >= qb;
-    // key offset in the block = 32 t + 8 (r / 4) + 4 hh + r % 4
-    const int lim = q_tok - j * kBlock - 4 * hh;
-    // token window: keys k <= q - window of blocks past the sink blocks
-    const bool wedge = WIN && j >= a.sink_blk && j * kBlock <= q_wave + 31 - a.window;
-    const int lo = lim - a.window;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(__builtin_fmaf(s[t][r], c, -lse2));
-        if (diag && 32 * t + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
-        if (wedge && 32 * t + 8 * (r >> 2) + (r & 3) <= lo) p = 0.f;
-        s[t][r] = p * (dp[t][r] - dlt);  // dS^T
+    // causal / token-window masks as -inf scores under one uniform branch
+    // each (key offset in the block = 32 t + 8 (r / 4) + 4 hh + r % 4)
+    const int lim = q_tok - j * kBlock - 4 * hh;   // later keys: offset > lim
+    if (a.causal && j >= qb) {
+      static_for<32>([&](auto E) __attribute__((always_inline)) {
+        constexpr int t = decltype(E)::value / 16, r = decltype(E)::value % 16;
+        s[t][r] = mask_neg_inf(s[t][r], lim - (32 * t + 8 * (r >> 2) + (r & 3)));
+      });
+    }
+    if constexpr (WIN) {
+      // token window: keys k <= q - window (offset <= lim - window) of blocks
+      // past the sink blocks
+      if (j >= a.sink_blk && j * kBlock <= q_wave + 31 - a.window) {
+        const int lo = lim - a.window;
+        static_for<32>([&](auto E) __attribute__((always_inline)) {
+          constexpr int t = decltype(E)::value / 16, r = decltype(E)::value % 16;
+          s[t][r] = mask_neg_inf(s[t][r], (32 * t + 8 * (r >> 2) + (r & 3)) - lo - 1);
+        });
       }
+    }
+    static_for<32>([&](auto E) __attribute__((always_inline)) {
+      constexpr int t = decltype(E)::value / 16, r = decltype(E)::value % 16;
+      const float p = fast_exp2(__builtin_fmaf(s[t][r], c, -lse2));
+      s[t][r] = p * (dp[t][r] - dlt);  // dS^T
+    });
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 bds = pack_half(s[ks >> 1], ks & 1);
