@@ -74,18 +74,6 @@ struct KOrder {
   static constexpr int value[sizeof...(J)] = {J...};
 };
 
-// Reads 16 consecutive fp32 values of a per-token vector laid out in LDS as
-// the rows of a 32x32 accumulator tile: element r is token
-// 32*tile + 8*(r/4) + 4*hh + r%4.
-__device__ __forceinline__ void load_rows16(const float *lds, int tile, int hh, float out[16]) {
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const f32x4 v = *(const f32x4 *)(lds + 32 * tile + 8 * g + 4 * hh);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[4 * g + e] = v[e];
-  }
-}
-
 // Packs registers 8 half .. 8 half + 7 of a 32x32 accumulator tile (scaled
 // by nothing) into the B operand of a 32x32x16 MFMA whose k index runs over
 // the tile's rows (see pack_acc_operand in tiles.h).

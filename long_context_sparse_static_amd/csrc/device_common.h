@@ -44,13 +44,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// acc + the sum of the two bf16 values packed in w (v_dot2_f32_bf16 against
-// ones)
-__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
-  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
-}
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -64,14 +57,10 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
-// max / sum of x over lane l and lane l ^ 32 (the two halves of a wave64).
+// max of x over lane l and lane l ^ 32 (the two halves of a wave64).
 __device__ __forceinline__ float xor32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Direct global -> LDS loads through a raw buffer descriptor: lane i's BYTES
