@@ -152,3 +152,36 @@ def test_peaky_sink_forward_backward(pat):
     assert (np.exp(s[:, :64] - wl[0, 0, -64:, None]).sum(axis=1) > 0.5).all()
     for name, gt, w in (("dq", dq, wq), ("dk", dk, wk), ("dv", dv, wv)):
         print(name, assert_bf16_close(as_f64(gt), w, name))
+
+
+def test_backward_custom_index_empty_rows_and_columns():
+    """A hand-built index: query block 1 lists nothing, key block 3 is listed
+    by no query block, and query block 4 reads a far earlier block and its
+    own.  The backward (through the CSC transpose) matches the oracle on the
+    same lists, and the gradients of the empty row and the unread key block
+    are exactly zero."""
+    need_gpu()
+    from oracle import attention_backward, dense_token_mask, transpose_lists
+    lists = [[0], [], [0, 2], [0, 2], [1, 4], [0, 5]]
+    nb, d, H = len(lists), 128, 3
+    L = 64 * nb
+    cols = transpose_lists(lists, nb)
+    row_ptr = np.cumsum([0] + [len(r) for r in lists]).astype(np.int32)
+    col_ptr = np.cumsum([0] + [len(c) for c in cols]).astype(np.int32)
+    host = lcs.HostIndex(1, nb, nb, row_ptr, np.array([j for r in lists for j in r], dtype=np.int32),
+                         col_ptr, np.array([i for c in cols for i in c], dtype=np.int32))
+    lcs.attn_index_validate(host)
+    pat = lcs.attnsink_pattern(1, 1)          # only its causal flag applies with a given index
+    q, k, v, do = _inputs((1, H, L, d), 640)
+    ix = lcs.DeviceIndex(host, q.device)
+    o, lse = lcs.attn_sparse_fwd(q, k, v, ix, pat)
+    dq, dk, dv = lcs.attn_sparse_bwd(q, k, v, o, lse, do, ix, pat)
+    torch.cuda.synchronize()
+    mask = dense_token_mask(lists, 64, L, L, causal=True)
+    for h in range(H):
+        wq, wk, wv, _, _ = attention_backward(as_f64(q[0, h]), as_f64(k[0, h]), as_f64(v[0, h]),
+                                              as_f64(do[0, h]), mask, 1 / math.sqrt(d))
+        for name, g, w in (("dq", dq[0, h], wq), ("dk", dk[0, h], wk), ("dv", dv[0, h], wv)):
+            assert_bf16_close(as_f64(g), w, f"{name} head {h}")
+    assert torch.all(dq[:, :, 64:128] == 0)
+    assert torch.all(dk[:, :, 192:256] == 0) and torch.all(dv[:, :, 192:256] == 0)
