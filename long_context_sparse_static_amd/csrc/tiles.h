@@ -289,21 +289,54 @@ struct RowsBitmap {
   }
 
   // Caller: every thread of the workgroup, nt threads.  Ends with a barrier.
-  // Bitmap row r holds list rows[r] (none if rows[r] < 0).
+  // Bitmap row r holds list rows[r] (none if rows[r] < 0).  The R row
+  // extents are read first and the R lists then read as one flat range, kU
+  // entries per thread in flight, so the build waits for two dependent
+  // global reads rather than two per row (and one per entry and thread).
   __device__ void build_rows(const int32_t *ptr, const int (&rows)[R], int nnz, const int32_t *ids,
                              int n_ids, int nt) {
-    for (int i = threadIdx.x; i < R * nw + nsw; i += nt) bm[i] = 0u;
-    __syncthreads();
+    constexpr int kU = R >= 4 ? 8 : 1;   // the two-row (backward) tiles gained nothing from more
+    int beg[R], len[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int row = rows[r];
-      if (row >= 0) {
-        const int p = clamp_i(ptr[row], 0, nnz);
-        const int e = clamp_i(ptr[row + 1], p, nnz);
-        for (int x = p + threadIdx.x; x < e; x += nt) {
-          const int j = ids[x];
-          if (j >= 0 && j < n_ids) atomicOr(&bm[r * nw + (j >> 5)], 1u << (j & 31));
+      const int p = row >= 0 ? clamp_i(ptr[row], 0, nnz) : 0;
+      const int e = row >= 0 ? clamp_i(ptr[row + 1], p, nnz) : 0;
+      beg[r] = p;
+      len[r] = e - p;
+    }
+    for (int i = threadIdx.x; i < R * nw + nsw; i += nt) bm[i] = 0u;
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) total += len[r];
+    // flat entry x -> (row, global position)
+    auto locate = [&](int x, int &row) -> int {
+      int pos = beg[0] + x;
+      row = 0;
+#pragma unroll
+      for (int r = 1; r < R; ++r) {
+        if (row == r - 1 && x >= len[r - 1]) {   // past rows 0 .. r-1
+          x -= len[r - 1];
+          pos = beg[r] + x;
+          row = r;
         }
+      }
+      return pos;
+    };
+    for (int x0 = threadIdx.x; x0 < total; x0 += kU * nt) {
+      int jv[kU], rv[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int x = x0 + u * nt;
+        jv[u] = -1;
+        rv[u] = 0;
+        if (x < total) jv[u] = ids[locate(x, rv[u])];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int j = jv[u];
+        if (j >= 0 && j < n_ids) atomicOr(&bm[rv[u] * nw + (j >> 5)], 1u << (j & 31));
       }
     }
     __syncthreads();
