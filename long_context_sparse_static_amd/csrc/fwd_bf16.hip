@@ -302,13 +302,14 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     // P' = 2^-kFwdBias P, P taken against the running max m_run, so the
     // top exponent bit of a packed bf16 P' (bit 14 of each half) is set
     // exactly when P >= 2^(kFwdBias + 1), and for inf and NaN.  A block with
-    // such a P', or a row with no max yet, takes the exact path: block max,
-    // rescale to it if it is higher (so later blocks start from P <= 1
-    // again), P' again.  Between rescales P stays below 2^64, far from
-    // fp32 overflow, and a P' of 2^-63 at the running max keeps every
-    // P that matters (P >= 2^-63) a normal number.
+    // such a P' takes the exact path: block max, rescale to it if it is
+    // higher (so later blocks start from P <= 1 again), P' again.  A row with
+    // no max yet needs no test of its own: m_run = -inf makes every P' +inf
+    // (or NaN for a masked score), which sets that bit.  Between rescales P
+    // stays below 2^64, far from fp32 overflow, and a P' of 2^-63 at the
+    // running max keeps every P that matters (P >= 2^-63) a normal number.
     const uint32_t ow = exps(m_run + kFwdBias);
-    if (__any(m_run == -INFINITY || (ow & 0x40004000u) != 0u)) {
+    if (__any((ow & 0x40004000u) != 0u)) {
       float mx = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
