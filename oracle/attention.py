@@ -235,14 +235,17 @@ def pattern_lists_for_head(pattern, n_qblocks, head):
                        block=pattern.get("block", 64))
 
 
-def pattern_token_mask(pattern, head, L, rows=None):
+def pattern_token_mask(pattern, head, L, rows=None, lists=None):
     """Dense [n_rows, L] mask of head ``head``: the token rule for a sliding
-    pattern, else the block lists expanded to tokens (causal inside blocks)."""
+    pattern, else the block lists expanded to tokens (causal inside blocks).
+    ``lists``: this head's block lists if the caller already holds them
+    (pattern_lists_for_head's result), to skip building them again."""
     p = head_pattern(pattern, head)
     if p["kind"] == SLIDING:
         return sliding_token_mask(L, L, p["block"] * p.get("sink_blocks", 0),
                                   p["window_tokens"], rows=rows)
-    lists = pattern_lists_for_head(pattern, L // p["block"], head)
+    if lists is None:
+        lists = pattern_lists_for_head(pattern, L // p["block"], head)
     return dense_token_mask(lists, p["block"], L, L, p.get("causal", True), rows=rows)
 
 

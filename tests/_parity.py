@@ -65,7 +65,7 @@ def sample_rows_forward(q, k, v, pattern, head, b, rows, scale=None):
     rows = np.asarray(sorted(rows))
     kblocks = sorted({j for r in rows for j in lists[r // pattern.block]})
     keys = np.concatenate([np.arange(j * pattern.block, (j + 1) * pattern.block) for j in kblocks])
-    mask = pattern_token_mask(oracle_pattern(pattern), head, L, rows=rows)[:, keys]
+    mask = pattern_token_mask(oracle_pattern(pattern), head, L, rows=rows, lists=lists)[:, keys]
     qh = as_f64(q[b, head, torch.as_tensor(rows, device=q.device)])
     kh = as_f64(k[b, head, torch.as_tensor(keys, device=k.device)])
     vh = as_f64(v[b, head, torch.as_tensor(keys, device=v.device)])
@@ -82,7 +82,8 @@ def sample_backward(q, k, v, do, pattern, head, b, qblocks, kblocks, scale=None)
     B_ = pattern.block
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     nb = L // B_
-    lists = pattern_lists_for_head(oracle_pattern(pattern), nb, head)
+    opat = oracle_pattern(pattern)
+    lists = pattern_lists_for_head(opat, nb, head)
     cols = transpose_lists(lists, nb)
     tok = lambda blocks: np.concatenate([np.arange(j * B_, (j + 1) * B_) for j in blocks])
     qh, kh, vh, doh = (as_f64(t[b, head]) for t in (q, k, v, do))
@@ -91,7 +92,7 @@ def sample_backward(q, k, v, do, pattern, head, b, qblocks, kblocks, scale=None)
     def sub(i):
         if i not in cache:
             rows, keys = tok([i]), tok(lists[i])
-            mask = pattern_token_mask(oracle_pattern(pattern), head, L, rows=rows)[:, keys]
+            mask = pattern_token_mask(opat, head, L, rows=rows, lists=lists)[:, keys]
             cache[i] = attention_backward(qh[rows], kh[keys], vh[keys], doh[rows], mask, scale)[:3]
         return cache[i]
 

@@ -319,8 +319,21 @@ def test_batched_wrapper_and_row_sampling_agree():
     np.testing.assert_array_equal(o2[:, 1:, rows], o[:, 1:, rows])
     np.testing.assert_array_equal(lse2[:, 1:, rows], lse[:, 1:, rows])
     assert np.isnan(o2[:, 0]).all()
-    # head-dependent stride offset: heads 1 and 2 differ in their strided blocks
-    assert not np.allclose(o[0, 1], o[0, 2]) or True
+    # head-dependent stride offset: heads 1 and 2 read different strided blocks
+    assert (pattern_token_mask(pat, 1, L) != pattern_token_mask(pat, 2, L)).any()
+
+
+@pytest.mark.parametrize("kind,extra", [(BLOCKSPARSE, dict(sink_blocks=1, local_blocks=2, stride=3)),
+                                        (ATTNSINK, dict(sink_blocks=1, local_blocks=2)),
+                                        (SLIDING, dict(sink_blocks=1, window_tokens=23))])
+def test_token_mask_with_given_lists_is_the_same(kind, extra):
+    """Handing pattern_token_mask the head's lists only skips rebuilding them."""
+    pat = dict(kind=kind, block=16, causal=True, **extra)
+    L, rows = 16 * 9, np.array([0, 15, 16, 40, 100, 143])
+    for h in range(3):
+        lists = block_lists(kind, 9, head=h, block=16, **extra)
+        np.testing.assert_array_equal(pattern_token_mask(pat, h, L, rows=rows, lists=lists),
+                                      pattern_token_mask(pat, h, L, rows=rows))
 
 
 # --------------------------------------------------------------------------
