@@ -635,6 +635,9 @@ def main():
         "config": rep["config"],
         "roofline": rep["roofline"],
         **rep["extra"],
+        # every timed span (one launch of an op, or one layer's launches) by label
+        "span_ms": {k: {"n": len(v), "median": float(np.median(v)), "min": float(min(v))}
+                    for k, v in sorted(times.items())},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline")
