@@ -264,6 +264,54 @@ def test_decode_validation_errors():
     assert rf(lcs.ATTN_BF16, 1, 1, 100, 64, 64, FAKE, FAKE, FAKE, 10, FAKE, FAKE, None) == lcs.ATTN_ERR_UNSUPPORTED
 
 
+def test_blocksparse_decode_validation_errors():
+    """The compacted-cache decode and its fill reject a pattern that is not
+    BlockSparse with 64-token blocks, a negative strided capacity, a cache
+    beyond int32 slots, missing pointers, and a short workspace."""
+    L_ = lcs.lib()
+    good = lcs.blocksparse_pattern(1, 16, 8)
+
+    def pat(kind=lcs.ATTN_BLOCKSPARSE, block=64, sink=1, local=16, stride=8):
+        p = good.c_struct()
+        p.kind, p.block, p.sink_blocks, p.local_blocks, p.stride = kind, block, sink, local, stride
+        return p
+
+    def dec(p=None, cap=256, B=2, H=4, d=128, scale=0.1, pos=FAKE, dtype=lcs.ATTN_BF16, ws=FAKE,
+            wsb=1 << 30):
+        p = pat() if p is None else p
+        return L_.attn_blocksparse_decode(dtype, B, H, d, scale, ctypes.byref(p), cap, pos, FAKE, FAKE,
+                                          FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb, None)
+    assert dec(p=pat(kind=lcs.ATTN_ATTNSINK)) == lcs.ATTN_ERR_INVALID_ARG
+    assert dec(p=pat(block=32)) == lcs.ATTN_ERR_INVALID_ARG
+    assert dec(p=pat(local=0)) == lcs.ATTN_ERR_INVALID_ARG
+    assert dec(p=pat(stride=0)) == lcs.ATTN_ERR_INVALID_ARG
+    assert dec(p=pat(sink=-1)) == lcs.ATTN_ERR_INVALID_ARG
+    assert dec(cap=-1) == lcs.ATTN_ERR_INVALID_ARG
+    assert dec(cap=1 << 25) == lcs.ATTN_ERR_INVALID_ARG           # more than 2^31 slots
+    assert dec(scale=0.0) == lcs.ATTN_ERR_INVALID_ARG
+    assert dec(scale=float("nan")) == lcs.ATTN_ERR_INVALID_ARG
+    assert dec(pos=None) == lcs.ATTN_ERR_INVALID_ARG
+    assert dec(B=300, H=300) == lcs.ATTN_ERR_INVALID_ARG           # B*H beyond the grid
+    assert dec(d=96) == lcs.ATTN_ERR_UNSUPPORTED
+    assert dec(dtype=lcs.ATTN_F32) == lcs.ATTN_ERR_UNSUPPORTED
+    assert dec(ws=None) == lcs.ATTN_ERR_WORKSPACE
+    assert dec(wsb=16) == lcs.ATTN_ERR_WORKSPACE
+    need = lcs.attn_workspace_bytes(lcs.ATTN_OP_BLOCKSPARSE_DECODE, lcs.ATTN_BF16, 2, 4,
+                                    64 * (1 + 16 + 256), 128)
+    assert dec(wsb=need - 1) == lcs.ATTN_ERR_WORKSPACE
+
+    def fill(p=None, cap=256, src_len=100, ln=FAKE, d=128, dtype=lcs.ATTN_BF16):
+        p = pat() if p is None else p
+        return L_.attn_blocksparse_cache_fill(dtype, 2, 4, d, ctypes.byref(p), cap, ln, FAKE, FAKE,
+                                              src_len, FAKE, FAKE, None)
+    assert fill(p=pat(kind=lcs.ATTN_FULL)) == lcs.ATTN_ERR_INVALID_ARG
+    assert fill(cap=-2) == lcs.ATTN_ERR_INVALID_ARG
+    assert fill(src_len=-1) == lcs.ATTN_ERR_INVALID_ARG
+    assert fill(ln=None) == lcs.ATTN_ERR_INVALID_ARG
+    assert fill(d=80) == lcs.ATTN_ERR_UNSUPPORTED
+    assert fill(dtype=lcs.ATTN_F32) == lcs.ATTN_ERR_UNSUPPORTED
+
+
 def test_strided_validation_errors():
     """Strides that are not whole 16-byte vectors, negative strides, a token
     stride beyond 64-row int32 offsets and a misaligned base are rejected
