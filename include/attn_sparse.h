@@ -195,7 +195,9 @@ size_t attn_workspace_bytes(int32_t op, attn_dtype_t dtype, int32_t B,
  * For every (b, h) and query token i: O[i] = softmax(scale * q_i K_S^T) V_S
  * over the allowed key set S of i, LSE[i] = log sum exp(scale * q_i K_S^T).
  *   dtype: ATTN_BF16 (q/k/v/o bf16, fp32 accumulation) or ATTN_F32 (all
- *          fp32).  d in {64, 128}.  pattern->block == 64, L % 64 == 0.
+ *          fp32).  d in {64, 128}.  pattern->block == 64; B, H >= 1 and
+ *          L >= 64 with L % 64 == 0 (an empty batch or sequence is
+ *          ATTN_ERR_INVALID_ARG).
  *   dev_index: device CSR for L/64 query and key blocks (CSC unused).
  *   pattern: its causal flag applies to every head; for kind ATTN_SLIDING
  *   its token window (sink_blocks, window_tokens) also masks keys inside

@@ -208,6 +208,9 @@ def _fwd(dtype=lcs.ATTN_BF16, B=1, H=2, L=256, d=128, scale=0.1, pattern=None, i
 def test_forward_validation_errors():
     assert _fwd(L=1000) == lcs.ATTN_ERR_INVALID_ARG                   # L % 64
     assert _fwd(B=0) == lcs.ATTN_ERR_INVALID_ARG
+    assert _fwd(H=0) == lcs.ATTN_ERR_INVALID_ARG
+    assert _fwd(L=0) == lcs.ATTN_ERR_INVALID_ARG                      # empty sequence
+    assert _fwd(L=-64) == lcs.ATTN_ERR_INVALID_ARG
     assert _fwd(scale=0.0) == lcs.ATTN_ERR_INVALID_ARG
     assert _fwd(scale=float("nan")) == lcs.ATTN_ERR_INVALID_ARG
     assert _fwd(q=None) == lcs.ATTN_ERR_INVALID_ARG
