@@ -551,6 +551,37 @@ def _counter_means(path, counter):
     return acc
 
 
+N_XCD, N_SIMD = 8, 1024   # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def summarize_mfma(path):
+    """Per attention kernel, from one rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+    GRBM_GUI_ACTIVE run: the matrix-core busy fraction (busy cycles summed
+    over SIMDs / (GPU-active cycles of one XCD x SIMDs), the profiler's own
+    MfmaUtil) and the clock the kernel ran at (GPU-active cycles of one XCD /
+    dispatch time), averaged over dispatches."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if "attn::" not in r["Kernel_Name"]:
+            continue
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        d = per.setdefault(key, {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    acc = {}
+    for (name, _), d in per.items():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in d or "GRBM_GUI_ACTIVE" not in d:
+            continue
+        active = d["GRBM_GUI_ACTIVE"] / N_XCD
+        acc.setdefault(name, []).append((d["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * N_SIMD),
+                                         active / d["ns"], d["ns"] / 1e6))
+    out = [f"{'kernel':72s} {'n':>3s} {'avg ms':>8s} {'MFMA busy':>10s} {'clock GHz':>10s}"]
+    for name, v in sorted(acc.items(), key=lambda kv: -sum(x[2] for x in kv[1])):
+        busy, clk, ms = (sum(x[i] for x in v) / len(v) for i in range(3))
+        out.append(f"{_short(name):72s} {len(v):3d} {ms:8.3f} {100 * busy:9.1f}% {clk:10.3f}")
+    return "\n".join(out)
+
+
 def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel, scaled so that
     the copy1g kernel reads 1 GiB and writes 1 GiB."""
@@ -586,6 +617,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
                     help="print a summary of a rocprofv3 --stats kernel_stats.csv and exit")
+    ap.add_argument("--summarize-mfma", metavar="COUNTER_CSV",
+                    help="print matrix-core busy fraction and clock per attention kernel from a "
+                         "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
+                         "counter_collection.csv, and exit")
     ap.add_argument("--summarize-traffic", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="print per-kernel HBM bytes from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
@@ -593,6 +628,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_stats:
         print(summarize_stats(args.summarize_stats))
+        return
+    if args.summarize_mfma:
+        print(summarize_mfma(args.summarize_mfma))
         return
     if args.summarize_traffic:
         print(summarize_traffic(*args.summarize_traffic)[0])
