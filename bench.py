@@ -636,7 +636,7 @@ def main():
         print(summarize_traffic(*args.summarize_traffic)[0])
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1"}))
         raise SystemExit(2)
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")

@@ -46,7 +46,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = -1, /* null pointer, bad size, L % 64 != 0, ...      */
-  ATTN_ERR_UNSUPPORTED = -2, /* valid request this build does not implement  */
+  ATTN_ERR_UNSUPPORTED = -2, /* valid request the library does not implement */
   ATTN_ERR_BAD_INDEX = -3,   /* malformed block index (host validation)      */
   ATTN_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required   */
   ATTN_ERR_HIP = -5          /* HIP runtime error (launch / device query)    */
