@@ -1,0 +1,57 @@
+"""CPU tests of bench.py's readers of rocprofv3 output, on small hand-made
+CSV files whose answers follow from their definitions: the traffic
+calibration against the 1 GiB copy, and the matrix-core busy fraction and
+clock from SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE."""
+
+import csv
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+COUNTER_FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                  "Start_Timestamp", "End_Timestamp"]
+
+
+def _write(path, rows, fields=COUNTER_FIELDS):
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=fields)
+        w.writeheader()
+        for r in rows:
+            w.writerow(dict(zip(fields, r)))
+    return str(path)
+
+
+def test_mfma_busy_and_clock(tmp_path):
+    name = "void attn::(anonymous namespace)::fwd_bf16_kernel<128, false, true>(attn::FwdArgs)"
+    ns = 2_000_000                                   # 2 ms dispatches
+    active = 3.6e6 * bench.N_XCD                     # 3.6e6 cycles per XCD -> 1.8 GHz
+    rows = []
+    for disp, busy in ((1, 0.5), (2, 0.7)):
+        rows.append((disp, name, "GRBM_GUI_ACTIVE", active, 10 ** 9, 10 ** 9 + ns))
+        rows.append((disp, name, "SQ_VALU_MFMA_BUSY_CYCLES", busy * 3.6e6 * bench.N_SIMD,
+                     10 ** 9, 10 ** 9 + ns))
+    rows.append((3, "void at::native::fill_kernel", "GRBM_GUI_ACTIVE", 1.0, 0, 10))  # not attention
+    out = bench.summarize_mfma(_write(tmp_path / "c.csv", rows)).splitlines()
+    assert len(out) == 2
+    fields = out[1].split()
+    assert fields[-4:] == ["2", "2.000", "60.0%", "1.800"]
+
+
+def test_traffic_calibration(tmp_path):
+    copy = "void at::native::vectorized_elementwise_kernel<4, copy>"
+    kern = "void attn::fwd_bf16_kernel<128, false, true>(attn::FwdArgs)"
+    # the copy reads and writes 1 GiB; the counters read half of the fetch
+    cf = _write(tmp_path / "cf.csv", [(1, copy, "FETCH_SIZE", 524288, 0, 1)])
+    cw = _write(tmp_path / "cw.csv", [(1, copy, "WRITE_SIZE", 1048576, 0, 1)])
+    f = _write(tmp_path / "f.csv", [(1, kern, "FETCH_SIZE", 1000000, 0, 1),
+                                    (2, kern, "FETCH_SIZE", 3000000, 0, 1)])
+    w = _write(tmp_path / "w.csv", [(1, kern, "WRITE_SIZE", 500000, 0, 1),
+                                    (2, kern, "WRITE_SIZE", 500000, 0, 1)])
+    text = bench.summarize_traffic(f, w, cf, cw)[0]
+    line = [x for x in text.splitlines() if "fwd_bf16_kernel" in x][0]
+    # mean fetch 2e6 KiB x 2 + mean write 5e5 KiB x 1, in GB
+    assert abs(float(line.split()[-1]) - (2e6 * 2 + 5e5) * 1024 / 1e9) < 1e-3
