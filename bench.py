@@ -62,7 +62,7 @@ DEC_BATCH = 16
 KERNEL_SOURCES = ("fwd_bf16.hip", "tiles.h", "device_common.h", "kernels.h")
 TRAFFIC = {
     # fwd_bf16_kernel<128>, average over the 32 launches of one hybrid128k step
-    ("hybrid128k", "b42e0236864b4dd2"): 10.932e9,
+    ("hybrid128k", "7da5c91cec6ccb60"): 10.927e9,
 }
 
 

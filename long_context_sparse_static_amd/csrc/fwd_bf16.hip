@@ -56,6 +56,7 @@ namespace {
 constexpr int kFwdWaves = 8;                 // waves per workgroup
 constexpr int kFwdThreads = kFwdWaves * 64;
 constexpr int kFwdQB = 4;                    // query blocks per workgroup
+constexpr int kFwdTileMajorTiles = 32;       // at most this many tiles per head (L <= 8192): tile-major block order
 constexpr int kLoadWaves = 4;                // waves that issue the tile loads (group B)
 constexpr float kFwdBias = 63.f;             // P is held as 2^-63 P (see the vector step; 0x1p63f below)
 
@@ -104,9 +105,23 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
 
   const int nqb = a.ix.n_qblocks;
   const int n_tiles = (nqb + kFwdQB - 1) / kFwdQB;
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lin / n_tiles;
-  const int tile = n_tiles - 1 - lin % n_tiles;  // heaviest (latest) tiles first
+  // Latest (heaviest) tiles first.  With many tiles per head, each XCD takes
+  // a contiguous run of heads, tile by tile, so a head's tiles share its K/V
+  // in that XCD's L2.  With few, that order would end each XCD's share on its
+  // last head's heavy tiles, so blocks go tile-major over all heads instead:
+  // the hardware deals consecutive blocks to the 8 XCDs in turn, so each XCD
+  // holds every tile of the heads bh = x mod 8, heaviest first (3% faster at
+  // 8K AttnSink; at 32K BlockSparse the L2 sharing weighs more, 1% slower).
+  int bh, tile;
+  if (n_tiles <= kFwdTileMajorTiles) {
+    const int n_bh = gridDim.x / n_tiles;
+    bh = blockIdx.x % n_bh;
+    tile = n_tiles - 1 - blockIdx.x / n_bh;
+  } else {
+    const int lin = xcd_remap(blockIdx.x, gridDim.x);
+    bh = lin / n_tiles;
+    tile = n_tiles - 1 - lin % n_tiles;
+  }
   const int hidx = a.ix.n_heads == 1 ? 0 : bh % a.H;
 
   // Token-row strides: compile-time for contiguous [B,H,L,d] tensors (so tile
