@@ -76,7 +76,7 @@ struct KOrder {
 
 // Packs registers 8 half .. 8 half + 7 of a 32x32 accumulator tile (scaled
 // by nothing) into the B operand of a 32x32x16 MFMA whose k index runs over
-// the tile's rows (see pack_acc_operand in tiles.h).
+// the tile's rows (the register order described at the top of tiles.h).
 __device__ __forceinline__ bf16x8 pack_half(const f32x16 &t, int half) {
   u32x4 w;
 #pragma unroll

@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // Per-lane LDS read offsets.  K row operand for k-step ks: row n (+32 t),
   // logical chunk 2 ks + hh.  V through the transposing read: source lane s
   // of 16-lane group gi addresses token 16 ks + 8 r + 4 hh + s/4 at dims
-  // 32 mt + 16 gi + 4 (s % 4) (see TrRead in tiles.h for the lane algebra).
+  // 32 mt + 16 gi + 4 (s % 4) (the lane algebra of SwzTile::tr in tiles.h).
   // The swizzles only touch chunk bits, so the offset of k-step ks (V:
   // dim tile mt) is one per-lane base XOR a constant: kofs(ks) = kbase ^
   // 32 ks, vofs(mt) = vbase ^ 64 mt (D = 128; D = 64 analogously).

@@ -1,21 +1,5 @@
 // LDS staging of 64-token tiles and the CSR union walk, shared by the MFMA
 // forward and backward kernels.
-//
-// Two LDS layouts of a 64 x D bf16 tile (64 tokens, D head dims):
-//   row-major   [token][d], rows padded to D + 8 elements, read as the
-//               row-operand of a 32x32x16 MFMA (16 contiguous bytes per lane);
-//               the padding puts 16 consecutive lanes on distinct banks.
-//   transposed  [d][token], 128-byte rows (64 tokens) without padding, read
-//               as the operand whose k index runs over tokens.  Within a row
-//               the tokens are permuted by tpos() (bits 2 and 3 swapped) so
-//               that the 8 tokens one lane feeds into a k-step are 16
-//               contiguous bytes, matching the register order of a 32x32
-//               accumulator reused as an operand (pack_acc_operand()); and
-//               the eight 16-byte chunks of row d are XOR-swizzled by
-//               tswz(d) so that both the 16-lane operand reads and the
-//               transposing 8-byte writes spread over all 64 banks.  (With
-//               plain padding the transposing writes ran ~25x slower than the
-//               reads on gfx950 and stalled the whole CU's LDS.)
 #pragma once
 
 #include "device_common.h"
@@ -23,162 +7,11 @@
 
 namespace attn {
 
-__host__ __device__ __forceinline__ int tpos(int u) {
-  return (u & ~0xC) | ((u & 4) << 1) | ((u & 8) >> 1);
-}
-
-// XOR key of the 16-byte chunks of transposed row d (0..7).
-__host__ __device__ __forceinline__ int tswz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
-
-// Element offset of logical 16-byte chunk q (0..7) of transposed row d.
-__host__ __device__ __forceinline__ int t_off(int d, int q) { return d * kBlock + ((q ^ tswz(d)) << 3); }
-
-template <int D>
-struct TileGeom {
-  static constexpr int ROW = D + 8;        // row-major LDS row (elements)
-  static constexpr int CPR = D / 8;        // 16-byte chunks per token row
-  static constexpr int ROW_ELEMS = kBlock * ROW;
-  static constexpr int T_ELEMS = D * kBlock;
-};
-
-// Row-major staging of one 64 x D tile by NT threads into LDS rows of RS
-// elements (RS >= D).
-template <int D, int NT, int RS = TileGeom<D>::ROW>
-struct RowStage {
-  static constexpr int CPR = D / 8;
-  static constexpr int N = kBlock * CPR / NT;
-  static_assert(N >= 1 && kBlock * CPR % NT == 0, "row stage shape");
-  u32x4 r[N];
-
-  __device__ __forceinline__ void load(const bf16 *g) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int ch = threadIdx.x + i * NT;
-      r[i] = *(const u32x4 *)(g + (ch / CPR) * D + (ch % CPR) * 8);
-    }
-  }
-  __device__ __forceinline__ void store(bf16 *lds) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int ch = threadIdx.x + i * NT;
-      *(u32x4 *)(lds + (ch / CPR) * RS + (ch % CPR) * 8) = r[i];
-    }
-  }
-};
-
-// Transposed staging of one 64 x D tile by NT threads: each thread loads KPT
-// consecutive token rows of one 8-dim chunk c and writes 8 transposed rows
-// (dims 8c..8c+7) of KPT tokens.  Lanes with odd c write each pair of rows in
-// the opposite order, so every store instruction covers both bank halves.
-template <int D, int NT>
-struct TStage {
-  static constexpr int CPR = D / 8;
-  static constexpr int KPT = kBlock * CPR / NT;
-  static_assert(KPT == 2 || KPT == 4, "transposed stage shape");
-  u32x4 r[KPT];
-
-  __device__ __forceinline__ void load(const bf16 *g) {
-    const int c = threadIdx.x % CPR, grp = threadIdx.x / CPR;
-#pragma unroll
-    for (int kk = 0; kk < KPT; ++kk) r[kk] = *(const u32x4 *)(g + (grp * KPT + kk) * D + c * 8);
-  }
-  // byte offset of this thread's KPT tokens inside transposed row d
-  __device__ __forceinline__ static int unit_off(int d, int grp) {
-    if constexpr (KPT == 4) {
-      const int u = tpos(grp * 4) >> 2;               // 8-byte unit 0..15
-      return (((u >> 1) ^ tswz(d)) << 4) + ((u & 1) << 3);
-    } else {
-      const int u = tpos(grp * 2) >> 1;               // 4-byte unit 0..31
-      return (((u >> 2) ^ tswz(d)) << 4) + ((u & 3) << 2);
-    }
-  }
-  __device__ __forceinline__ void store(bf16 *lds) const {
-    const int c = threadIdx.x % CPR, grp = threadIdx.x / CPR;
-    const bool odd = c & 1;
-    // v_perm selectors: the low halves (dims 8c+2w) or the high halves
-    // (dims 8c+2w+1) of two 32-bit words; odd lanes take them swapped.
-    const uint32_t sel_a = odd ? 0x07060302u : 0x05040100u;
-    const uint32_t sel_b = odd ? 0x05040100u : 0x07060302u;
-    char *base = (char *)lds;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {  // word w holds dims 8c+2w (low half), 8c+2w+1 (high half)
-      const int dA = c * 8 + 2 * w + (odd ? 1 : 0);
-      const int dB = dA ^ 1;
-      if constexpr (KPT == 4) {
-        u32x2 va, vb;
-        va[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], sel_a);
-        va[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], sel_a);
-        vb[0] = __builtin_amdgcn_perm(r[1][w], r[0][w], sel_b);
-        vb[1] = __builtin_amdgcn_perm(r[3][w], r[2][w], sel_b);
-        *(u32x2 *)(base + dA * (kBlock * 2) + unit_off(dA, grp)) = va;
-        *(u32x2 *)(base + dB * (kBlock * 2) + unit_off(dB, grp)) = vb;
-      } else {
-        *(uint32_t *)(base + dA * (kBlock * 2) + unit_off(dA, grp)) = __builtin_amdgcn_perm(r[1][w], r[0][w], sel_a);
-        *(uint32_t *)(base + dB * (kBlock * 2) + unit_off(dB, grp)) = __builtin_amdgcn_perm(r[1][w], r[0][w], sel_b);
-      }
-    }
-  }
-};
-
-// Row-major 64 x D tile read through the gfx950 transposing LDS load
-// (ds_read_b64_tr_b16) as the A operand of a 32x32x16 MFMA whose k index
-// runs over the 64 tokens: A[m = d][k = token].  Within each 16-lane group
-// the instruction hands output lane i element i%4 of the 8-byte chunks that
-// source lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4 address.  Source lane s of
-// group gi (lane = 16*gi + s, plus 32*hh) therefore addresses token
-// 16*ks + 8*r + 4*hh + s/4 at dims 32*mt + 16*gi + 4*(s%4); two reads
-// (r = 0, 1) give the lane d = 32*mt + lane%32 and the 8 tokens that the
-// register order of pack_acc_operand() assigns to logical k = 8*hh .. +7.
-// Row stride TRS = D + 32 elements puts the 32 lanes of one read phase on
-// all 64 banks (row r starts at bank 16*r mod 64).
-template <int D>
-struct TrRead {
-  static constexpr int TRS = D + 32;           // row stride (elements)
-  static constexpr int ELEMS = kBlock * TRS;
-  int base;                                    // byte offset of this lane
-  __device__ __forceinline__ void init(int lane) {
-    const int s = lane & 15, gi = (lane >> 4) & 1, hh = lane >> 5;
-    base = ((s >> 2) + 4 * hh) * TRS * 2 + (16 * gi + 4 * (s & 3)) * 2;
-  }
-  __device__ __forceinline__ bf16x8 load(const bf16 *tile, int mt, int ks) const {
-    typedef short s4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s4 lds_s4;
-    const char *p = (const char *)tile + base + (16 * ks) * TRS * 2 + 64 * mt;
-    const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)p);
-    const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(p + 8 * TRS * 2));
-    typedef short s8 __attribute__((ext_vector_type(8)));
-    const s8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, v);
-  }
-};
-
-// Byte offsets of one lane's reads of a transposed tile as the A operand of
-// a 32x32x16 MFMA: row d = 32*mt + n (n = lane % 32), logical chunk
-// q = 2*ks + hh.  Because tswz(32*mt + n) = tswz(n) ^ 2*mt for mt < 4, the
-// physical chunk is (2*(ks ^ mt)) ^ sigma with a per-lane sigma, so four
-// per-lane bases (one per value of ks ^ mt) plus the immediate mt * 4096
-// cover every read: no address arithmetic inside the loop.
-struct TReadBases {
-  int b[4];
-  __device__ __forceinline__ void init(int n, int hh) {
-    const int sigma = (hh ^ tswz(n)) & 7;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) b[x] = n * (kBlock * 2) + (((2 * x) ^ sigma) << 4);
-  }
-  // byte offset of (mt, ks)
-  __device__ __forceinline__ int at(int mt, int ks) const { return b[ks ^ mt] + mt * 32 * kBlock * 2; }
-};
-
-// Rows of a 32x32 accumulator pair (64 tokens x 32 columns, fp32) converted to
-// the bf16 operand of a k-step that runs over those 64 tokens: k-step ks takes
-// registers 8*(ks%2)..+7 of tile ks/2.  Logical k = 8*hh + 4*a + b is token
-// 16*ks + 8*a + 4*hh + b, which tpos() places at 16*ks + 8*hh + 4*a + b.
-__device__ __forceinline__ bf16x8 pack_acc_operand(const f32x16 &t, int half) {
-  u32x4 w;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(t[8 * half + 2 * e], t[8 * half + 2 * e + 1]);
-  return __builtin_bit_cast(bf16x8, w);
-}
+// Register order of a 32x32 fp32 accumulator pair (64 tokens x 32 columns)
+// reused as the bf16 B operand of a k-step that runs over those 64 tokens:
+// k-step ks takes registers 8 (ks % 2) .. +7 of tile ks / 2, so the lane's
+// logical k = 8 hh + 4 a + b (hh = lane / 32) is token 16 ks + 8 a + 4 hh + b.
+// Every transposing read below hands the A operand over in this same order.
 
 // A 64 x D bf16 tile staged straight from global memory into LDS
 // (buffer_load_dwordx4 ... lds) as 64 unpadded rows of RB = 2 D bytes whose
@@ -235,7 +68,7 @@ struct SwzTile {
   // Transposing reads: lane (hh, gi, s) = 32 hh + 16 gi + s addresses token
   // 16 ks + 8 h + 4 hh + s / 4 (h = 0, 1) at dims 32 mt + 16 gi + 4 (s % 4);
   // the two reads give lane d = 32 mt + lane % 32 the 8 tokens that
-  // pack_acc_operand() assigns to logical k = 8 hh .. +7.
+  // register order above assigns to logical k = 8 hh .. +7.
   int trb[2];
   __device__ __forceinline__ void init_reads(int lane) {
     const int n = lane & 31, hh = lane >> 5, s = lane & 15, gi = (lane >> 4) & 1;
@@ -429,18 +262,6 @@ struct RowsIter {
 #pragma unroll
     for (int r = 0; r < R; ++r) mask |= ((b[r] >> bit) & 1u) << r;
     return true;
-  }
-};
-
-// Two-row forms used by the backward kernels.
-using PairBitmap = RowsBitmap<2>;
-struct PairIter : RowsIter<2> {
-  bool in0, in1;
-  __device__ __forceinline__ bool next(const PairBitmap &pb) {
-    const bool ok = RowsIter<2>::next(pb);
-    in0 = mask & 1u;
-    in1 = (mask >> 1) & 1u;
-    return ok;
   }
 };
 
