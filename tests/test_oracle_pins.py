@@ -7,7 +7,10 @@ at least one of them:
   * forward: torch's scaled_dot_product_attention (float64, CPU) on the
     special cases that reduce to it; Q = 0 and constant-V closed forms;
   * backward: central finite differences in float64, and torch autograd on
-    the full-causal special case;
+    the full-causal special case and on head-dependent masks built by a
+    separate rule (the batched wrapper's per-head dispatch and output order);
+  * per-head pattern lists: each head runs its own pattern (the same head of
+    a single-pattern run, and per-head Q = 0 closed-form counts);
   * decode: library attention on its reducible cases and a Q = 0 count;
   * KV memory: the pages' own figures (consistency only).
 """
@@ -389,6 +392,97 @@ def test_batched_backward_wrapper():
     np.testing.assert_allclose(o, o2, atol=1e-14)
     np.testing.assert_allclose(lse, lse2, atol=1e-14)
     assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
+
+
+def block_rule_mask(kind, h, L, block, s=0, w=0, stride=0):
+    """Token mask of a block pattern written as one vectorised rule (NOT the
+    oracle's brute-force scan): key block kj is read by query block qi when
+    kj <= qi and (kj < s, or qi - w < kj, or -- BlockSparse -- kj < qi with
+    (kj + h) % stride == 0); keys after the query are masked."""
+    qt = np.arange(L)[:, None]
+    kt = np.arange(L)[None, :]
+    qi, kj = qt // block, kt // block
+    if kind == FULL:
+        blk = kj <= qi
+    else:
+        blk = (kj <= qi) & ((kj < s) | (kj > qi - w))
+        if kind == BLOCKSPARSE:
+            blk |= (kj < qi) & ((kj + h) % stride == 0)
+    return blk & (kt <= qt)
+
+
+def autograd_head(q, k, v, do, mask, scale):
+    """O, LSE, dQ, dK, dV of one head by torch autograd (float64, CPU) on the
+    dense masked softmax: an independent route to the textbook gradients."""
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    s = (tq @ tk.T) * scale
+    s = s.masked_fill(~torch.from_numpy(mask), float("-inf"))
+    lse = torch.logsumexp(s, dim=1)
+    o = torch.softmax(s, dim=1) @ tv
+    o.backward(torch.from_numpy(do))
+    return (o.detach().numpy(), lse.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(),
+            tv.grad.numpy())
+
+
+# (kind, sink, local, stride) per head: every head differs from head 0, and
+# heads 2 and 3 share a BlockSparse rule whose phase still differs by head
+MIXED = [(FULL, 0, 0, 0), (ATTNSINK, 1, 2, 0), (BLOCKSPARSE, 1, 1, 3), (BLOCKSPARSE, 1, 1, 3),
+         (ATTNSINK, 0, 1, 0)]
+
+
+def _pattern_dict(kind, s, w, stride, block):
+    return dict(kind=kind, block=block, sink_blocks=s, local_blocks=w, stride=stride, causal=True)
+
+
+def test_per_head_pattern_list_runs_each_heads_own_pattern():
+    """A list of per-head patterns: head h of the list run equals head h of
+    a run with pattern h alone (same H-head tensors, so the BlockSparse
+    phase is h in both), and Q = 0 gives each head its own closed-form key
+    count (which picking pattern 0, or any other head's, would break)."""
+    B, H, block, nb, d = 2, len(MIXED), 8, 7, 4
+    L = block * nb
+    pats = [_pattern_dict(*m, block) for m in MIXED]
+    q, k, v = rand(B, H, L, d), rand(B, H, L, d), rand(B, H, L, d)
+    o, lse = sparse_forward(q, k, v, pats)
+    for h in range(H):
+        o1, l1 = sparse_forward(q, k, v, pats[h], heads=[h])
+        np.testing.assert_array_equal(o[:, h], o1[:, h])
+        np.testing.assert_array_equal(lse[:, h], l1[:, h])
+    _, lse0 = sparse_forward(np.zeros_like(q), k, v, pats)
+    for h, (kind, s, w, stride) in enumerate(MIXED):
+        for p in range(L):
+            bi, r = divmod(p, block)
+            n_blocks = (bi + 1 if kind == FULL else attnsink_row_len(bi, s, w) if kind == ATTNSINK
+                        else blocksparse_row_len(bi, s, w, stride, h))
+            assert lse0[0, h, p] == pytest.approx(math.log(block * (n_blocks - 1) + r + 1), abs=1e-12)
+
+
+@pytest.mark.parametrize("per_head_list", [False, True])
+def test_sparse_backward_per_head_matches_autograd(per_head_list):
+    """The batched backward on head-dependent masks (BlockSparse with stride
+    3, so heads 0, 1, 2 read different strided blocks; or the per-head mix
+    above) against torch autograd on each head's own mask, built by a
+    separate rule: pins the per-head dispatch and the (dq, dk, dv, o, lse)
+    order -- dO is random, so dk and dv differ and a swap fails."""
+    B, block, nb, d, scale = 2, 8, 8, 4, 0.45
+    L = block * nb
+    if per_head_list:
+        heads = MIXED
+        pat = [_pattern_dict(*m, block) for m in MIXED]
+    else:
+        heads = [(BLOCKSPARSE, 1, 1, 3)] * 4
+        pat = _pattern_dict(BLOCKSPARSE, 1, 1, 3, block)
+    H = len(heads)
+    q, k, v, do = (rand(B, H, L, d) for _ in range(4))
+    dq, dk, dv, o, lse = sparse_backward(q, k, v, do, pat, scale=scale)
+    masks = [block_rule_mask(kind, h, L, block, s, w, stride) for h, (kind, s, w, stride) in enumerate(heads)]
+    assert not np.array_equal(masks[1], masks[2]) and not np.array_equal(masks[0], masks[1])
+    for b in range(B):
+        for h in range(H):
+            ro, rl, rq, rk, rv = autograd_head(q[b, h], k[b, h], v[b, h], do[b, h], masks[h], scale)
+            for name, mine, ref in (("o", o, ro), ("lse", lse, rl), ("dq", dq, rq), ("dk", dk, rk),
+                                    ("dv", dv, rv)):
+                np.testing.assert_allclose(mine[b, h], ref, atol=1e-11, err_msg=f"{name} b{b} h{h}")
 
 
 # --------------------------------------------------------------------------
