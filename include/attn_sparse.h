@@ -144,13 +144,23 @@ const char *attn_status_str(attn_status_t status);
  * ------------------------------------------------------------------------- */
 
 /* Total entries of the index of `pattern` for n_heads index heads and L
- * tokens (L % block == 0), written to *nnz_out. */
+ * tokens (L % block == 0), written to *nnz_out.  The index is the static
+ * block list of the sparse layers' fixed patterns -- sink, window and
+ * strided blocks (mlsanity index page "A Little Goes a Long Way...",
+ * "Abstract (arXiv)"), accessed block-wise and fixed ahead of time
+ * (atlas.scime.ai summary, "Approach"): it is built once per shape.
+ * ATTN_ERR_INVALID_ARG for a NULL pointer, n_heads < 1 or an invalid
+ * pattern; ATTN_ERR_UNSUPPORTED if nnz exceeds INT32_MAX (int32 offsets). */
 attn_status_t attn_index_nnz(const attn_pattern_t *pattern, int32_t n_heads,
                              int64_t L, int64_t *nnz_out);
 
-/* Builds the index of `pattern` into caller buffers sized as in attn_index_t
- * (nnz from attn_index_nnz).  Index head hh uses stride phase hh.  col_ptr
- * and row_idx may both be NULL (forward-only index). */
+/* Builds the index of `pattern` (the static block lists of the sparse
+ * patterns: mlsanity index page, "Abstract (arXiv)"; atlas.scime.ai summary,
+ * "Approach") into caller host buffers sized as in attn_index_t (nnz from
+ * attn_index_nnz): CSR rows ascending, and the CSC transpose the backward
+ * walks.  Index head hh uses stride phase hh.  col_ptr and row_idx may both
+ * be NULL (forward-only index); one of them alone is ATTN_ERR_INVALID_ARG.
+ * Errors as attn_index_nnz; nothing is written on an error. */
 attn_status_t attn_index_build(const attn_pattern_t *pattern, int32_t n_heads,
                                int64_t L, int32_t *row_ptr, int32_t *col_idx,
                                int32_t *col_ptr, int32_t *row_idx);
@@ -170,9 +180,13 @@ attn_status_t attn_index_build_mixed(const attn_pattern_t *patterns, int32_t n_h
                                      int64_t L, int32_t *row_ptr, int32_t *col_idx,
                                      int32_t *col_ptr, int32_t *row_idx);
 
-/* Checks a HOST copy of an index: monotone pointers within [0, nnz], block
- * ids in range and strictly ascending, and (when present) that the CSC is
- * exactly the transpose of the CSR.  Returns ATTN_ERR_BAD_INDEX otherwise. */
+/* Checks a HOST copy of an index (the static block lists the sparse layers
+ * walk: mlsanity index page, "Abstract (arXiv)"; atlas.scime.ai summary,
+ * "Approach") before it is uploaded: monotone pointers within [0, nnz],
+ * block ids in range and strictly ascending, and (when present) that the
+ * CSC is exactly the transpose of the CSR.  Returns ATTN_ERR_BAD_INDEX
+ * otherwise, ATTN_ERR_INVALID_ARG for missing pointers or bad sizes.  Reads
+ * only; the caller owns the arrays. */
 attn_status_t attn_index_validate(const attn_index_t *host_index);
 
 /* Hybrid layer map: is_full[l] = 1 for full_first <= l <= full_last, else 0
@@ -191,7 +205,12 @@ size_t attn_workspace_bytes(int32_t op, attn_dtype_t dtype, int32_t B,
  * Device operations: validate synchronously, then enqueue on `stream`.
  * ------------------------------------------------------------------------- */
 
-/* Prefill forward (LongGen sparse layers; full layers with a Full index).
+/* Prefill forward of the hybrid model's attention layers: the sparse layers
+ * with their static block patterns (sink, window, strided blocks: mlsanity
+ * index page "A Little Goes a Long Way...", "Abstract (arXiv)"; static
+ * block-wise access and FlashAttention-2 style tiling: atlas.scime.ai
+ * summary, "Approach"; prefill is where the pages report 1.67x: same
+ * summary, "Key results"), and the full middle layers with a Full index.
  * For every (b, h) and query token i: O[i] = softmax(scale * q_i K_S^T) V_S
  * over the allowed key set S of i, LSE[i] = log sum exp(scale * q_i K_S^T).
  *   dtype: ATTN_BF16 (q/k/v/o bf16, fp32 accumulation) or ATTN_F32 (all
@@ -268,7 +287,10 @@ attn_status_t attn_sparse_bwd_strided(
     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Decode one new token per sequence in a sparse (sink + window) layer,
- * against its reduced ring-buffer cache.
+ * against its reduced ring-buffer cache: the sparse layers keep only the
+ * sink and the recent window (mlsanity index page, "Abstract (arXiv)"),
+ * which is where the pages' KV-memory cut and decode speedup come from
+ * (atlas.scime.ai summary, "Key results": 69.2 GB to 26.5 GB, 1.41x).
  *   Cache layout: k_cache, v_cache [B,H,S,d] with S = sink_tokens +
  *   window_tokens.  Token p lives in slot p if p < sink_tokens, else in slot
  *   sink_tokens + (p - sink_tokens) % window_tokens.
@@ -288,7 +310,9 @@ attn_status_t attn_sparse_decode(attn_dtype_t dtype, int32_t B, int32_t H,
                                  void *workspace, size_t workspace_bytes,
                                  void *stream);
 
-/* Decode one new token per sequence in a full-attention layer.
+/* Decode one new token per sequence in a full-attention layer -- the middle
+ * third of the hybrid, which keeps direct access to every token (mlsanity
+ * index page, "Abstract (arXiv)"; atlas.scime.ai summary, "Approach").
  *   k_cache, v_cache: [B,H,capacity,d]; token p lives in slot p.
  *   dev_pos: [B] int64 device positions t; k_new / v_new go to slot t and q
  *   attends to slots 0..t.  max_pos: a host-side upper bound on every t
@@ -347,6 +371,29 @@ attn_status_t attn_paged_cache_fill(attn_dtype_t dtype, int32_t B, int32_t H,
                                     const void *v_src, int64_t src_len,
                                     void *k_pages, void *v_pages, void *stream);
 
+/* Sizing of a BlockSparse compacted cache (layout as in
+ * attn_blocksparse_decode): the strided area keeps the strided blocks that
+ * have left the window, the part of the block-wise sparse pattern a reduced
+ * KV cache must still hold (mlsanity index page, "Abstract (arXiv)";
+ * atlas.scime.ai summary, "Key results").  Pure host, no HIP calls.
+ *   attn_blocksparse_strided_capacity: *strided_blocks_out = the largest
+ *   number of strided blocks any position t < max_tokens reads outside its
+ *   window, over every head's stride phase -- the strided_blocks argument
+ *   that fits decode of every such position.
+ *   attn_blocksparse_cache_slots: *slots_out = 64 (sink_blocks +
+ *   local_blocks + strided_blocks), the S of the [B,H,S,d] cache.
+ *   pattern: kind ATTN_BLOCKSPARSE, block 64, sink_blocks >= 0,
+ *   local_blocks >= 1, stride >= 1; max_tokens >= 1; strided_blocks >= 0.
+ *   ATTN_ERR_INVALID_ARG otherwise (or for a NULL pointer);
+ *   ATTN_ERR_UNSUPPORTED if the result does not fit (strided blocks beyond
+ *   INT32_MAX, slots beyond INT32_MAX).  Nothing is written on an error. */
+attn_status_t attn_blocksparse_strided_capacity(const attn_pattern_t *pattern,
+                                                int64_t max_tokens,
+                                                int32_t *strided_blocks_out);
+attn_status_t attn_blocksparse_cache_slots(const attn_pattern_t *pattern,
+                                           int32_t strided_blocks,
+                                           int64_t *slots_out);
+
 /* Decode one new token per sequence in a BlockSparse layer against its
  * compacted cache (the block-wise sparse layers of LongGen: mlsanity index
  * page, "Abstract (arXiv)"; their reduced KV cache: atlas.scime.ai summary,
@@ -356,7 +403,9 @@ attn_status_t attn_paged_cache_fill(attn_dtype_t dtype, int32_t B, int32_t H,
  * strided blocks sink_blocks <= j < i-local_blocks+1 with
  * (j + h) % stride == 0, h = head index.
  *   pattern: kind ATTN_BLOCKSPARSE, block 64 (sink_blocks s, local_blocks w,
- *   stride st).  strided_blocks C: capacity of the strided area.
+ *   stride st).  strided_blocks C: capacity of the strided area
+ *   (attn_blocksparse_strided_capacity gives the C that fits every
+ *   position below a bound; attn_blocksparse_cache_slots gives S).
  *   Cache layout: k_cache, v_cache [B,H,S,d], S = 64 (s + w + C):
  *     slots [0, 64 s)            sink blocks;
  *     slots [64 s, 64 (s + w))   ring of the w most recent blocks, block j at

@@ -56,7 +56,8 @@ EXPORTED = (
     "attn_layer_map", "attn_workspace_bytes", "attn_sparse_fwd", "attn_sparse_bwd",
     "attn_sparse_decode", "attn_full_decode", "attn_ring_fill", "attn_blocksparse_decode",
     "attn_blocksparse_cache_fill", "attn_paged_decode", "attn_paged_cache_fill",
-    "attn_sparse_fwd_strided", "attn_sparse_bwd_strided",
+    "attn_sparse_fwd_strided", "attn_sparse_bwd_strided", "attn_blocksparse_strided_capacity",
+    "attn_blocksparse_cache_slots",
 )
 
 
@@ -134,6 +135,10 @@ def lib():
         L.attn_blocksparse_decode.restype = i32
         L.attn_blocksparse_decode.argtypes = [i32, i32, i32, i32, f32, P(attn_pattern_t), i32, vp,
                                               vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_blocksparse_strided_capacity.restype = i32
+        L.attn_blocksparse_strided_capacity.argtypes = [P(attn_pattern_t), i64, P(i32)]
+        L.attn_blocksparse_cache_slots.restype = i32
+        L.attn_blocksparse_cache_slots.argtypes = [P(attn_pattern_t), i32, P(i64)]
         L.attn_blocksparse_cache_fill.restype = i32
         L.attn_blocksparse_cache_fill.argtypes = [i32, i32, i32, i32, P(attn_pattern_t), i32, vp,
                                                   vp, vp, i64, vp, vp, vp]
@@ -602,18 +607,28 @@ def attn_ring_fill(k_src, v_src, lengths, k_cache, v_cache, sink_tokens: int, wi
                                 src_len, kc, vc, _stream()), "attn_ring_fill")
 
 
-def blocksparse_cache_slots(pattern: Pattern, strided_blocks: int) -> int:
+def attn_blocksparse_cache_slots(pattern: Pattern, strided_blocks: int) -> int:
     """Slots per (b, h) of a BlockSparse compacted cache."""
-    return pattern.block * (pattern.sink_blocks + pattern.local_blocks + strided_blocks)
+    out = ctypes.c_int64(0)
+    pat = pattern.c_struct()
+    _check(lib().attn_blocksparse_cache_slots(ctypes.byref(pat), strided_blocks, ctypes.byref(out)),
+           "attn_blocksparse_cache_slots")
+    return out.value
 
 
-def blocksparse_strided_capacity(pattern: Pattern, max_tokens: int) -> int:
+def attn_blocksparse_strided_capacity(pattern: Pattern, max_tokens: int) -> int:
     """Strided-area blocks that positions below ``max_tokens`` can need (the
     largest count over the heads' stride phases)."""
-    nb = (max_tokens + pattern.block - 1) // pattern.block
-    first = max(0, nb - pattern.local_blocks)       # first window block of the last position
-    span = max(0, first - pattern.sink_blocks)
-    return (span + pattern.stride - 1) // pattern.stride
+    out = ctypes.c_int32(0)
+    pat = pattern.c_struct()
+    _check(lib().attn_blocksparse_strided_capacity(ctypes.byref(pat), max_tokens, ctypes.byref(out)),
+           "attn_blocksparse_strided_capacity")
+    return out.value
+
+
+# shorter names used by callers
+blocksparse_cache_slots = attn_blocksparse_cache_slots
+blocksparse_strided_capacity = attn_blocksparse_strided_capacity
 
 
 def attn_blocksparse_decode(q, k_new, v_new, k_cache, v_cache, pos, pattern: Pattern,

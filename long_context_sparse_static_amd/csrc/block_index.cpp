@@ -230,6 +230,37 @@ attn_status_t attn_index_validate(const attn_index_t *ix) {
   return ATTN_OK;
 }
 
+// BlockSparse compacted cache.  Position t (block i = t / block) reads the
+// strided blocks j in [sink, i - local + 1) with (j + h) % stride == 0; the
+// most any phase h can hold in a span of n blocks is ceil(n / stride), and
+// the span only grows with t, so the last position below max_tokens sets the
+// capacity.
+static bool bs_sizing_ok(const attn_pattern_t *p) {
+  return p && p->kind == ATTN_BLOCKSPARSE && p->block == 64 && p->sink_blocks >= 0 &&
+         p->local_blocks >= 1 && p->stride >= 1;
+}
+
+attn_status_t attn_blocksparse_strided_capacity(const attn_pattern_t *p, int64_t max_tokens,
+                                                int32_t *out) {
+  if (!bs_sizing_ok(p) || !out || max_tokens < 1) return ATTN_ERR_INVALID_ARG;
+  const int64_t last_block = (max_tokens - 1) / p->block;
+  const int64_t first_local = std::max<int64_t>(0, last_block - p->local_blocks + 1);
+  const int64_t span = std::max<int64_t>(0, first_local - p->sink_blocks);
+  const int64_t cap = (span + p->stride - 1) / p->stride;
+  if (cap > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+  *out = (int32_t)cap;
+  return ATTN_OK;
+}
+
+attn_status_t attn_blocksparse_cache_slots(const attn_pattern_t *p, int32_t strided_blocks,
+                                           int64_t *out) {
+  if (!bs_sizing_ok(p) || !out || strided_blocks < 0) return ATTN_ERR_INVALID_ARG;
+  const int64_t slots = ((int64_t)p->sink_blocks + p->local_blocks + strided_blocks) * p->block;
+  if (slots > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+  *out = slots;
+  return ATTN_OK;
+}
+
 attn_status_t attn_layer_map(int32_t n_layers, int32_t full_first, int32_t full_last,
                              uint8_t *is_full) {
   if (n_layers < 1 || !is_full) return ATTN_ERR_INVALID_ARG;

@@ -138,6 +138,21 @@ int main() {
   CHECK(attn_layer_map(4, 1, 2, nullptr) != ATTN_OK);
   for (int s = -6; s <= 0; ++s) CHECK(attn_status_str((attn_status_t)s) != nullptr);
 
+  // BlockSparse cache sizing: extreme sizes stay in int64 arithmetic (UBSan
+  // catches overflow), errors write nothing
+  {
+    const attn_pattern_t bs = pat(ATTN_BLOCKSPARSE, 1, 16, 8);
+    int32_t cap = -7;
+    int64_t slots = -7;
+    CHECK(attn_blocksparse_strided_capacity(&bs, 131073, &cap) == ATTN_OK && cap == 254);
+    CHECK(attn_blocksparse_cache_slots(&bs, cap, &slots) == ATTN_OK && slots == 17344);
+    CHECK(attn_blocksparse_strided_capacity(&bs, INT64_MAX, &cap) == ATTN_ERR_UNSUPPORTED && cap == 254);
+    const attn_pattern_t one = pat(ATTN_BLOCKSPARSE, INT32_MAX, INT32_MAX, 1);
+    CHECK(attn_blocksparse_strided_capacity(&one, INT64_MAX, &cap) == ATTN_ERR_UNSUPPORTED && cap == 254);
+    CHECK(attn_blocksparse_cache_slots(&one, INT32_MAX, &slots) == ATTN_ERR_UNSUPPORTED && slots == 17344);
+    CHECK(attn_blocksparse_strided_capacity(&bs, 0, &cap) == ATTN_ERR_INVALID_ARG);
+  }
+
   if (fails) return 1;
   printf("harness ok\n");
   return 0;

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import long_context_sparse_static_amd as lcs
-from oracle import ATTNSINK, BLOCKSPARSE, FULL, SLIDING, block_lists, transpose_lists
+from oracle import (ATTNSINK, BLOCKSPARSE, FULL, SLIDING, block_lists, blocksparse_decode_positions,
+                    transpose_lists)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn_sparse.h")
@@ -24,7 +25,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     assert sorted(lcs.EXPORTED) == names
     L = lcs.lib()
     for n in names:
@@ -363,3 +364,48 @@ def test_paged_validation_errors():
     pf = L_.attn_paged_cache_fill
     assert pf(lcs.ATTN_BF16, 2, 4, 128, 10, 0, FAKE, FAKE, FAKE, FAKE, 100, FAKE, FAKE, None) == lcs.ATTN_ERR_INVALID_ARG
     assert pf(lcs.ATTN_BF16, 2, 4, 96, 10, 4, FAKE, FAKE, FAKE, FAKE, 100, FAKE, FAKE, None) == lcs.ATTN_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------ BlockSparse cache sizing
+@pytest.mark.parametrize("s,w,stride,max_tokens", [(1, 16, 8, 64 * 90 + 5), (1, 16, 8, 64 * 17), (2, 3, 5, 64 * 40),
+                                                   (0, 1, 1, 64 * 12 + 1), (3, 5, 7, 64 * 33 - 1),
+                                                   (1, 4, 2, 10)])
+def test_blocksparse_cache_sizing_against_oracle(s, w, stride, max_tokens):
+    """The strided capacity is the most strided blocks (read, not sink, not
+    in the token's own window) that the oracle's decode row of any position
+    t < max_tokens holds, over every stride phase; the slot count is the
+    cache's S."""
+    pat = lcs.blocksparse_pattern(s, w, stride)
+    opat = dict(kind=BLOCKSPARSE, block=64, sink_blocks=s, local_blocks=w, stride=stride, causal=True)
+    most = 0
+    for h in range(stride):
+        for t in list(range(0, max_tokens, 61)) + [max_tokens - 1]:
+            i = t // 64
+            blocks = set(blocksparse_decode_positions(t, opat, h) // 64)
+            most = max(most, len([j for j in blocks if j >= s and j < i - w + 1]))
+    cap = lcs.attn_blocksparse_strided_capacity(pat, max_tokens)
+    assert cap == most
+    assert lcs.attn_blocksparse_cache_slots(pat, cap) == 64 * (s + w + cap)
+
+
+def test_blocksparse_cache_sizing_workload():
+    """128K BlockSparse (sink 1, local 16, stride 8) decode at t = 131072:
+    254 strided blocks, 17,344 slots."""
+    pat = lcs.blocksparse_pattern(1, 16, 8)
+    assert lcs.attn_blocksparse_strided_capacity(pat, 131073) == 254
+    assert lcs.attn_blocksparse_cache_slots(pat, 254) == 17344
+
+
+def test_blocksparse_cache_sizing_rejections():
+    L = lcs.lib()
+    out32, out64 = ctypes.c_int32(-7), ctypes.c_int64(-7)
+    good = lcs.blocksparse_pattern(1, 16, 8).c_struct()
+    for bad in (lcs.attnsink_pattern(1, 4).c_struct(), lcs.blocksparse_pattern(1, 0, 8).c_struct(),
+                lcs.blocksparse_pattern(1, 4, 0).c_struct(), lcs.blocksparse_pattern(-1, 4, 8).c_struct()):
+        assert L.attn_blocksparse_strided_capacity(ctypes.byref(bad), 1000, ctypes.byref(out32)) == lcs.ATTN_ERR_INVALID_ARG
+        assert L.attn_blocksparse_cache_slots(ctypes.byref(bad), 3, ctypes.byref(out64)) == lcs.ATTN_ERR_INVALID_ARG
+    assert L.attn_blocksparse_strided_capacity(ctypes.byref(good), 0, ctypes.byref(out32)) == lcs.ATTN_ERR_INVALID_ARG
+    assert L.attn_blocksparse_strided_capacity(ctypes.byref(good), 1000, None) == lcs.ATTN_ERR_INVALID_ARG
+    assert L.attn_blocksparse_cache_slots(ctypes.byref(good), -1, ctypes.byref(out64)) == lcs.ATTN_ERR_INVALID_ARG
+    assert L.attn_blocksparse_cache_slots(ctypes.byref(good), 2 ** 31 - 1, ctypes.byref(out64)) == lcs.ATTN_ERR_UNSUPPORTED
+    assert out32.value == -7 and out64.value == -7          # nothing written on an error
