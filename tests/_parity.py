@@ -4,6 +4,8 @@ inputs exactly (a query row depends only on its own key list; a key block's
 dK/dV only on the query blocks that list it)."""
 
 import math
+import multiprocessing
+from concurrent.futures import FIRST_COMPLETED, ProcessPoolExecutor, wait
 
 import numpy as np
 import torch
@@ -111,4 +113,106 @@ def sample_backward(q, k, v, do, pattern, head, b, qblocks, kblocks, scale=None)
                 cache.clear()
         out[("dk", j)] = dk
         out[("dv", j)] = dv
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Every row of whole heads: one oracle sub-problem per query block, run over a
+# pool of spawned worker processes (tests/_oracle_pool.py: numpy and the
+# oracle only, no GPU).
+# ----------------------------------------------------------------------------
+def _run_pool(fn, tasks, on_result):
+    """fn(task) for each task of the iterable, at most two per worker in
+    flight (tasks are built lazily: their input slices can be large);
+    on_result(meta, result) in completion order."""
+    import _oracle_pool as pool
+    n = pool.n_workers()
+    ctx = multiprocessing.get_context("spawn")
+    with ProcessPoolExecutor(n, mp_context=ctx, initializer=pool._init_worker) as ex:
+        pending = {}
+        it = iter(tasks)
+        done_all = False
+        while True:
+            while not done_all and len(pending) < 2 * n:
+                try:
+                    meta, task = next(it)
+                except StopIteration:
+                    done_all = True
+                    break
+                pending[ex.submit(fn, task)] = meta
+            if not pending:
+                break
+            done, _ = wait(pending, return_when=FIRST_COMPLETED)
+            for f in done:
+                on_result(pending.pop(f), f.result())
+
+
+def _blocks_tokens(blocks, block=64):
+    return np.concatenate([np.arange(j * block, (j + 1) * block) for j in blocks])
+
+
+def _head_rows(t, b, h):
+    """One (b, h) of a device tensor as float32 host rows (bf16 values exactly)."""
+    return t[b, h].to("cpu", torch.float32).numpy()
+
+
+def oracle_forward_heads(q, k, v, pattern, heads, b=0, scale=None, chunk=32):
+    """Oracle O [L,d] and LSE [L] (float64) of every row of each head in
+    ``heads``, as {head: (o, lse)}, from exact per-query-block sub-problems."""
+    import _oracle_pool as pool
+    L, d = q.shape[2], q.shape[3]
+    scale = pool.default_scale(d) if scale is None else scale
+    nb = L // pattern.block
+    opat = oracle_pattern(pattern)
+    out = {h: (np.full((L, d), np.nan), np.full(L, np.nan)) for h in heads}
+
+    def tasks():
+        for h in heads:
+            lists = pattern_lists_for_head(opat, nb, h)
+            qh, kh, vh = (_head_rows(t, b, h) for t in (q, k, v))
+            for c0 in range(0, nb, chunk):
+                qblocks = list(range(c0, min(nb, c0 + chunk)))
+                kb = sorted({j for i in qblocks for j in lists[i]})
+                kt = _blocks_tokens(kb)
+                yield (h, qblocks), (opat, h, L, scale, qblocks, qh[_blocks_tokens(qblocks)], kb,
+                                     kh[kt], vh[kt])
+
+    def put(meta, res):
+        h, qblocks = meta
+        rows = _blocks_tokens(qblocks)
+        out[h][0][rows], out[h][1][rows] = res
+
+    _run_pool(pool.forward_chunk, tasks(), put)
+    return out
+
+
+def oracle_backward_heads(q, k, v, do, pattern, heads, b=0, scale=None, chunk=32):
+    """Oracle dQ, dK, dV [L,d] (float64) of each head in ``heads``, as
+    {head: (dq, dk, dv)}: every query block's sub-problem, its dK/dV parts
+    summed over the query blocks that read each key."""
+    import _oracle_pool as pool
+    L, d = q.shape[2], q.shape[3]
+    scale = pool.default_scale(d) if scale is None else scale
+    nb = L // pattern.block
+    opat = oracle_pattern(pattern)
+    out = {h: (np.full((L, d), np.nan), np.zeros((L, d)), np.zeros((L, d))) for h in heads}
+
+    def tasks():
+        for h in heads:
+            lists = pattern_lists_for_head(opat, nb, h)
+            qh, kh, vh, doh = (_head_rows(t, b, h) for t in (q, k, v, do))
+            for c0 in range(0, nb, chunk):
+                qblocks = list(range(c0, min(nb, c0 + chunk)))
+                kb = sorted({j for i in qblocks for j in lists[i]})
+                qt, kt = _blocks_tokens(qblocks), _blocks_tokens(kb)
+                yield (h, qt, kt), (opat, h, L, scale, qblocks, qh[qt], doh[qt], kb, kh[kt], vh[kt])
+
+    def put(meta, res):
+        h, qt, kt = meta
+        dq, dk, dv = res
+        out[h][0][qt] = dq
+        out[h][1][kt] += dk
+        out[h][2][kt] += dv
+
+    _run_pool(pool.backward_chunk, tasks(), put)
     return out

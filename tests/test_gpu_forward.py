@@ -7,8 +7,8 @@ import pytest
 import torch
 
 import long_context_sparse_static_amd as lcs
-from _parity import (assert_bf16_close, assert_f32_close, errors, need_gpu, oracle_pattern,
-                     sample_rows_forward)
+from _parity import (assert_bf16_close, assert_f32_close, errors, need_gpu, oracle_forward_heads,
+                     oracle_pattern, sample_rows_forward)
 from oracle import sparse_forward
 from synth_inputs import as_f64, randn, seed_for
 
@@ -153,34 +153,54 @@ def test_deterministic_repeat():
 
 
 # ----------------------------------------------------------------------------
-# Full-size workloads, in the launch configuration the benchmark times; the
-# oracle checks sampled rows of sampled heads on their exact sub-problems.
+# Full-size workloads, in the launch configuration the benchmark times.  The
+# oracle runs one exact sub-problem per query block (a row depends only on the
+# keys its block lists), so whole heads are checked row by row: every row of
+# all 32 heads at 8K AttnSink and 32K BlockSparse, every row of two heads at
+# 128K AttnSink and BlockSparse, and sampled rows of 128K full attention (a
+# full head is 4.4 TFLOP of float64 work).
 # ----------------------------------------------------------------------------
 FULL_SIZE = {
-    "attnsink_8k": (lcs.attnsink_pattern(1, 64), 8192, 2),
-    "blocksparse_32k": (lcs.blocksparse_pattern(1, 16, 8), 32768, 3),
-    "attnsink_128k": (lcs.attnsink_pattern(1, 64), 131072, 5),
-    "full_128k": (lcs.full_pattern(), 131072, 5),
-    "blocksparse_128k": (lcs.blocksparse_pattern(1, 16, 8), 131072, 33),
+    # name: (pattern, L, workload seed, heads checked on every row)
+    "attnsink_8k": (lcs.attnsink_pattern(1, 64), 8192, 2, list(range(32))),
+    "blocksparse_32k": (lcs.blocksparse_pattern(1, 16, 8), 32768, 3, list(range(32))),
+    "attnsink_128k": (lcs.attnsink_pattern(1, 64), 131072, 5, [0, 29]),
+    "blocksparse_128k": (lcs.blocksparse_pattern(1, 16, 8), 131072, 33, [5, 18]),
 }
 
 
 @pytest.mark.parametrize("name", list(FULL_SIZE))
-def test_bf16_full_size_sampled(name):
+def test_bf16_full_size_every_row(name):
     need_gpu()
-    pat, L, wl = FULL_SIZE[name]
+    pat, L, wl, heads = FULL_SIZE[name]
     H, d = 32, 128
     q, k, v = _inputs((1, H, L, d), wl, torch.bfloat16, big=True)
     o, lse = _run(q, k, v, pat)
-    rng = np.random.default_rng(L)
-    heads = [0, 3, 12, 29] if name.startswith("blocksparse") else [0, 7, 31]
+    want = oracle_forward_heads(q, k, v, pat, heads)
+    err_max = err_sum = 0.0
     for h in heads:
+        wo, wlse = want[h]
+        mx, mean = assert_bf16_close(as_f64(o[0, h]), wo, f"{name} O head {h}")
+        assert_bf16_close(as_f64(lse[0, h]), wlse, f"{name} LSE head {h}")
+        err_max, err_sum = max(err_max, mx), err_sum + mean
+    print(name, f"{len(heads)} heads x {L} rows: O max {err_max:.3e} mean {err_sum / len(heads):.3e}")
+
+
+def test_bf16_full_causal_128k_sampled():
+    """128K full causal attention (the hybrid's middle layers): sampled rows
+    of three heads on their exact sub-problems."""
+    need_gpu()
+    pat, L = lcs.full_pattern(), 131072
+    q, k, v = _inputs((1, 32, L, 128), 5, torch.bfloat16, big=True)
+    o, lse = _run(q, k, v, pat)
+    rng = np.random.default_rng(L)
+    for h in [0, 7, 31]:
         rows = np.unique(np.concatenate([[0, 63, 64, L - 1, L - 64], rng.integers(0, L, 40)]))
         wo, wlse = sample_rows_forward(q, k, v, pat, h, 0, rows)
         idx = torch.as_tensor(rows, device=q.device)
-        mx, mean = assert_bf16_close(as_f64(o[0, h, idx]), wo, f"{name} O head {h}")
-        assert_bf16_close(as_f64(lse[0, h, idx]), wlse, f"{name} LSE head {h}")
-        print(name, h, mx, mean)
+        mx, mean = assert_bf16_close(as_f64(o[0, h, idx]), wo, f"full O head {h}")
+        assert_bf16_close(as_f64(lse[0, h, idx]), wlse, f"full LSE head {h}")
+        print("full_128k", h, mx, mean)
 
 
 # ----------------------------------------------------------------------------
