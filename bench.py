@@ -15,7 +15,12 @@ Printed: one JSON line.  ``value`` is the effective TFLOP/s of the sparse
 (AttnSink) prefill layers -- algorithmic FLOPs of the computed 64x64 blocks
 (4*64*64*d per block pair) divided by their kernel time.  Decode tokens/s,
 the full-layer and whole-hybrid prefill rates, the roofline of the dominant
-kernel and the CPU oracle baseline are reported alongside.
+kernel and the CPU oracle baseline are reported alongside.  After the timed
+hybrid steps the same run times every other configuration of the workload
+definitions ("configs": the fp32 1K AttnSink forward, 8K AttnSink and 32K
+BlockSparse forwards, the 64K AttnSink forward + backward, and the 128K
+BlockSparse forward + backward), each with its median launch time, rate and
+fraction of the bf16 matrix-core peak.
 
 Other workloads (--workload): attnsink8k, blocksparse32k, blocksparse128k,
 attnsink128k, train64k (AttnSink forward + backward), blocksparse32k_train and
@@ -252,20 +257,22 @@ class Hybrid128k:
 # single-kernel workloads
 # ----------------------------------------------------------------------------
 class Prefill:
-    def __init__(self, name, pattern, L, wl, backward=False):
+    def __init__(self, name, pattern, L, wl, backward=False, heads=H, d=D, dtype=torch.bfloat16):
         self.name, self.pattern, self.L, self.backward = name, pattern, L, backward
+        self.H, self.d, self.dtype = heads, d, dtype
         dev = torch.device("cuda")
-        self.ix = lcs.build_device_index(pattern, H, L, dev, with_csc=backward)
-        self.q, self.k, self.v = (fill_randn((1, H, L, D), seed_for(wl, 0, t)) for t in ("q", "k", "v"))
+        self.ix = lcs.build_device_index(pattern, heads, L, dev, with_csc=backward)
+        shape = (1, heads, L, d)
+        self.q, self.k, self.v = (randn(shape, seed_for(wl, 0, t), dtype, "cuda") for t in ("q", "k", "v"))
         self.o = torch.empty_like(self.q)
-        self.lse = torch.empty((1, H, L), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((1, heads, L), dtype=torch.float32, device=dev)
         if backward:
-            self.do = fill_randn((1, H, L, D), seed_for(wl, 0, "do"))
+            self.do = randn(shape, seed_for(wl, 0, "do"), dtype, "cuda")
             self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
-            self.ws = torch.empty(lcs.attn_workspace_bytes(lcs.ATTN_OP_BWD, lcs.ATTN_BF16, 1, H, L, D),
+            self.ws = torch.empty(lcs.attn_workspace_bytes(lcs.ATTN_OP_BWD, lcs.ATTN_BF16, 1, heads, L, d),
                                   dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
-        self.pairs = self.ix.host.nnz * (H if not pattern.head_dependent else 1)
+        self.pairs = self.ix.host.nnz * (heads if not pattern.head_dependent else 1)
 
     def step(self, timer):
         with timer.span("fwd"):
@@ -275,12 +282,33 @@ class Prefill:
                 lcs.attn_sparse_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, self.ix,
                                     self.pattern, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
 
+    def summary(self, times):
+        """Per-launch medians / minima and rates of one timed run (every span
+        is one call)."""
+        fl = self.pairs * pair_flops(self.d)
+        f = times["fwd"]
+        out = dict(block_pairs=self.pairs, fwd_tflop=fl / 1e12, fwd_ms=float(np.median(f)),
+                   fwd_ms_min=float(min(f)))
+        out["fwd_tflops"] = fl / (out["fwd_ms"] * 1e-3) / 1e12
+        out["fwd_frac_of_peak"] = out["fwd_tflops"] / PEAK_BF16_TFLOPS
+        if self.backward:
+            b = times["bwd"]
+            out.update(bwd_tflop=2.5 * fl / 1e12, bwd_ms=float(np.median(b)), bwd_ms_min=float(min(b)))
+            out["bwd_tflops"] = 2.5 * fl / (out["bwd_ms"] * 1e-3) / 1e12
+            out["bwd_frac_of_peak"] = out["bwd_tflops"] / PEAK_BF16_TFLOPS
+            out["step_tflops"] = 3.5 * fl / ((out["fwd_ms"] + out["bwd_ms"]) * 1e-3) / 1e12
+        return out
+
+    def describe(self):
+        dt = "fp32" if self.dtype == torch.float32 else "bf16"
+        return f"{self.name}: B=1 H={self.H} L={self.L} d={self.d} {dt}"
+
     def report(self, times, steps):
-        fl = self.pairs * pair_flops()
+        fl = self.pairs * pair_flops(self.d)
         t_f = sum(times["fwd"]) / steps
         extra = dict(fwd_tflops=fl / (t_f * 1e-3) / 1e12, fwd_ms=t_f, block_pairs=self.pairs)
         value = extra["fwd_tflops"]
-        kernel, per_launch, avg = "fwd_bf16_kernel<128>", fl, t_f
+        kernel, per_launch, avg = f"fwd_bf16_kernel<{self.d}>", fl, t_f
         traffic = traffic_for(self.name)
         if self.backward:
             t_b = sum(times["bwd"]) / steps
@@ -293,8 +321,50 @@ class Prefill:
                     roofline=dict(bound="mfma", kernel=kernel, achieved=ach, peak=PEAK_BF16_TFLOPS,
                                   unit="TFLOP/s", frac=ach / PEAK_BF16_TFLOPS, traffic=traffic,
                                   kernel_source_hash=kernel_source_hash()),
-                    config=dict(workload=f"{self.name}: B=1 H=32 L={self.L} d=128 bf16",
-                                global_batch=1, seq_len=self.L, parallelism="single GPU"))
+                    config=dict(workload=self.describe(), global_batch=1, seq_len=self.L,
+                                parallelism="single GPU"))
+
+
+# The five configurations of the workload definitions plus the 128K
+# BlockSparse layer that the prefill target names, timed in the default run
+# after the hybrid step (each one launch per call, hipEvents on the stream).
+CONFIGS = (
+    ("C1_attnsink1k_fp32", lambda: Prefill("attnsink1k_fp32", lcs.attnsink_pattern(1, 4), 1024, 1,
+                                           heads=1, d=64, dtype=torch.float32)),
+    ("C2_attnsink8k", lambda: Prefill("attnsink8k", lcs.attnsink_pattern(1, 64), 8192, 2)),
+    ("C3_blocksparse32k", lambda: Prefill("blocksparse32k", lcs.blocksparse_pattern(1, 16, 8), 32768, 3)),
+    ("C4_train64k", lambda: Prefill("train64k", lcs.attnsink_pattern(1, 64), 65536, 4, backward=True)),
+    ("blocksparse128k_train", lambda: Prefill("blocksparse128k_train", lcs.blocksparse_pattern(1, 16, 8),
+                                              131072, 3, backward=True)),
+)
+
+
+def config_sweep(warmup=3, iters=10, names=None):
+    """Times every configuration in CONFIGS (warmup untimed calls, then
+    iters timed calls); returns {name: summary}."""
+    out = {}
+    for name, make in CONFIGS:
+        if names and name not in names:
+            continue
+        log(f"[bench] config {name}")
+        wl = make()
+        timer = Timer()
+        for _ in range(warmup):
+            wl.step(timer)
+        timer.collect()
+        for _ in range(iters):
+            wl.step(timer)
+        rep = wl.summary(timer.collect())
+        rep["workload"] = wl.describe()
+        rep["iters"] = iters
+        if wl.dtype == torch.float32:
+            # 73 MFLOP in 16 workgroups: bound by launch latency, not by a roofline
+            rep["bound"] = "launch"
+            rep.pop("fwd_frac_of_peak")
+        out[name] = rep
+        del wl
+        torch.cuda.empty_cache()
+    return out
 
 
 class Copy1G:
@@ -473,52 +543,141 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(budget_s=15.0):
-    """Times the oracle on sampled query rows of one 128K AttnSink layer and
-    scales to effective TFLOP/s over the computed blocks of those rows.  The
-    same rows of the GPU forward on the same inputs are compared with the
-    oracle's, and their errors reported beside the rate."""
-    from oracle import sparse_forward
+def _oracle_pattern(p):
+    kind = {lcs.ATTN_FULL: "full", lcs.ATTN_ATTNSINK: "attnsink", lcs.ATTN_BLOCKSPARSE: "blocksparse",
+            lcs.ATTN_SLIDING: "sliding"}[p.kind]
+    return dict(kind=kind, block=p.block, sink_blocks=p.sink_blocks, local_blocks=p.local_blocks,
+                stride=p.stride, causal=p.causal, window_tokens=p.window_tokens)
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
-    L = 131072
-    g = torch.Generator().manual_seed(seed_for(5, 0, "q"))
-    # one head's Q/K/V, generated on the host (the sample needs the whole key range)
-    qt, kt, vt = (torch.randn((1, 1, L, D), generator=g).to(torch.bfloat16) for _ in range(3))
-    q, k, v = (x.double().numpy() for x in (qt, kt, vt))
-    pat = dict(kind="attnsink", block=BLK, sink_blocks=SINK_BLOCKS, local_blocks=WINDOW_BLOCKS, causal=True)
-    # the GPU forward of the same head
-    gpat = lcs.attnsink_pattern(SINK_BLOCKS, WINDOW_BLOCKS)
-    gq, gk, gv = (x.cuda() for x in (qt, kt, vt))
-    ix = lcs.build_device_index(gpat, 1, L, gq.device, with_csc=False)
-    go, glse = lcs.attn_sparse_fwd(gq, gk, gv, ix, gpat)
-    go, glse = go[0, 0].double().cpu().numpy(), glse[0, 0].double().cpu().numpy()
+        return 1
+
+
+def _host_head(L, d, seed, dtype):
+    """One head's Q, K, V (and dO) generated on the host with the seed
+    recipe, rounded to the workload's dtype."""
+    g = torch.Generator().manual_seed(seed)
+    return [torch.randn((1, 1, L, d), generator=g).to(dtype) for _ in range(4)]
+
+
+def cpu_baseline(spec, budget_s=15.0):
+    """Times the oracle, as it stands, on a bounded sample of the benched
+    workload on the host cores, scaled to the workload's unit:
+      prefill: random query rows of one head (float64 dense-masked rows),
+               effective TFLOP/s over the computed blocks of those rows; the
+               same rows of the GPU forward of that head are compared with
+               the oracle's and the errors reported beside the rate;
+      train:   random query blocks of one head, forward + backward of each
+               block's exact sub-problem, TFLOP/s at 3.5x the forward count;
+      decode:  random heads of one sequence at the benched position, tok/s
+               of one layer (the time for all heads of one token)."""
+    import oracle
+    threads = _blas_threads()
     rng = np.random.default_rng(0)
-    rows_done, pairs_done, t_used, batch = 0, 0.0, 0.0, 64
-    err_o = err_l = 0.0
-    err_sum, n_el = 0.0, 0
-    while t_used < budget_s and rows_done < 4096:
-        rows = np.sort(rng.choice(np.arange(WINDOW_BLOCKS * BLK, L), size=batch, replace=False))
+    common = dict(kind="oracle", cores=threads, affinity_cpus=len(os.sched_getaffinity(0)),
+                  cpu_model=cpu_model())
+    kind = spec["kind"]
+    if kind in ("prefill", "train"):
+        pat, L, d, dtype = spec["pattern"], spec["L"], spec.get("d", D), spec.get("dtype", torch.bfloat16)
+        opat = _oracle_pattern(pat)
+        qt, kt, vt, dot = _host_head(L, d, spec["seed"], dtype)
+        q, k, v, do = (x[0, 0].double().numpy() for x in (qt, kt, vt, dot))
+        host_ix = lcs.attn_index_build(pat, 1, L, with_csc=False)
+        row_len = np.diff(host_ix.row_ptr[:L // BLK + 1])           # listed blocks per query block
+        scale = 1.0 / math.sqrt(d)
+        t_used, flops, n_done = 0.0, 0.0, 0
+        if kind == "prefill":
+            gpat = pat
+            gq, gk, gv = (x.cuda() for x in (qt, kt, vt))
+            ix = lcs.build_device_index(gpat, 1, L, gq.device, with_csc=False)
+            go, glse = lcs.attn_sparse_fwd(gq, gk, gv, ix, gpat)
+            go, glse = go[0, 0].double().cpu().numpy(), glse[0, 0].double().cpu().numpy()
+            err_o = err_l = err_sum = 0.0
+            n_el = 0
+            t0 = time.perf_counter()
+            lists = oracle.pattern_lists_for_head(opat, L // BLK, 0)     # the head's block lists, once
+            t_used += time.perf_counter() - t0
+            lo = min(L - 64, WINDOW_BLOCKS * BLK)
+            while t_used < budget_s and n_done < 65536:
+                rows = np.sort(rng.choice(np.arange(lo, L), size=64, replace=False))
+                t0 = time.perf_counter()
+                mask = oracle.pattern_token_mask(opat, 0, L, rows=rows, lists=lists)
+                o, lse = oracle.attention_forward(q[rows], k, v, mask, scale)
+                t_used += time.perf_counter() - t0
+                d_o = np.abs(go[rows] - o)
+                err_o = max(err_o, float(d_o.max()))
+                err_l = max(err_l, float(np.abs(glse[rows] - lse).max()))
+                err_sum += float(d_o.sum())
+                n_el += d_o.size
+                n_done += len(rows)
+                flops += float(row_len[rows // BLK].sum()) / BLK * pair_flops(d)
+            return dict(value=flops / t_used / 1e12, unit="TFLOP/s", **common,
+                        sample=f"{n_done} query rows (random, past the first window) of one head of "
+                               f"{spec['what']}, float64 dense-masked NumPy; {t_used:.1f} s",
+                        parity_vs_gpu=dict(rows=n_done, o_max_abs=err_o, o_mean_abs=err_sum / max(n_el, 1),
+                                           lse_max_abs=err_l, tolerance="max 2e-2, mean 2e-3"))
         t0 = time.perf_counter()
-        o, lse = sparse_forward(q, k, v, pat, rows=rows)
+        lists = oracle.pattern_lists_for_head(opat, L // BLK, 0)         # the head's block lists, once
         t_used += time.perf_counter() - t0
-        d_o = np.abs(go[rows] - o[0, 0, rows])
-        err_o = max(err_o, float(d_o.max()))
-        err_l = max(err_l, float(np.abs(glse[rows] - lse[0, 0, rows]).max()))
-        err_sum += float(d_o.sum())
-        n_el += d_o.size
-        rows_done += batch
-        pairs_done += batch * (SINK_BLOCKS + WINDOW_BLOCKS) / BLK   # block pairs per query row
-    flops = pairs_done * pair_flops()
-    return dict(value=flops / t_used / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
-                sample=f"{rows_done} query rows (random, past the first window) of one head of one "
-                       f"128K AttnSink layer, float64 dense-masked NumPy; {t_used:.1f} s",
-                affinity_cpus=len(os.sched_getaffinity(0)), cpu_model=cpu_model(),
-                parity_vs_gpu=dict(rows=rows_done, o_max_abs=err_o, o_mean_abs=err_sum / max(n_el, 1),
-                                   lse_max_abs=err_l, tolerance="max 2e-2, mean 2e-3"))
+        blocks = rng.permutation(np.arange(WINDOW_BLOCKS, L // BLK))
+        for i in blocks:
+            if t_used >= budget_s or n_done >= 4096:
+                break
+            rows = np.arange(i * BLK, (i + 1) * BLK)
+            keys = np.concatenate([np.arange(j * BLK, (j + 1) * BLK) for j in lists[i]])
+            t0 = time.perf_counter()
+            mask = oracle.pattern_token_mask(opat, 0, L, rows=rows, lists=lists)[:, keys]
+            oracle.attention_backward(q[rows], k[keys], v[keys], do[rows], mask, scale)
+            t_used += time.perf_counter() - t0
+            n_done += 1
+            flops += 3.5 * len(lists[i]) * pair_flops(d)
+        return dict(value=flops / t_used / 1e12, unit="TFLOP/s", **common,
+                    sample=f"{n_done} query blocks (random, past the first window) of one head of "
+                           f"{spec['what']}: forward + backward of each block's exact sub-problem, "
+                           f"float64 NumPy; {t_used:.1f} s")
+    if kind == "decode":
+        t, d = spec["t"], D
+        g = torch.Generator().manual_seed(spec["seed"])
+        t_used, n_heads = 0.0, 0
+        while t_used < budget_s and n_heads < 4 * H:
+            h = int(rng.integers(0, H))
+            kh = torch.randn((t + 1, d), generator=g).to(torch.bfloat16).double().numpy()
+            vh = torch.randn((t + 1, d), generator=g).to(torch.bfloat16).double().numpy()
+            qh = torch.randn((d,), generator=g).to(torch.bfloat16).double().numpy()
+            t0 = time.perf_counter()
+            keep = spec["positions"](t, h)
+            oracle.decode_one(qh, kh, vh, keep, 1.0 / math.sqrt(d))
+            t_used += time.perf_counter() - t0
+            n_heads += 1
+        return dict(value=(n_heads / H) / t_used, unit="tok/s (one layer)", **common,
+                    sample=f"{n_heads} heads (random) of one sequence at t={t} in {spec['what']}, "
+                           f"float64 NumPy over the token positions the token reads; {t_used:.1f} s")
+    return None
+
+
+def baseline_spec(name, wl):
+    """What the CPU baseline samples for a benched workload (None: no
+    oracle counterpart)."""
+    import oracle
+    if name == "hybrid128k":
+        return dict(kind="prefill", pattern=lcs.attnsink_pattern(SINK_BLOCKS, WINDOW_BLOCKS), L=131072,
+                    seed=seed_for(5, 0, "q"), what="one 128K AttnSink layer (the metric's sparse prefill)")
+    if isinstance(wl, Prefill):
+        return dict(kind="train" if wl.backward else "prefill", pattern=wl.pattern, L=wl.L, d=wl.d,
+                    dtype=wl.dtype, seed=seed_for(9, 0, "q"), what=wl.describe())
+    if name == "bsdecode128k":
+        opat = _oracle_pattern(wl.pat)
+        return dict(kind="decode", t=wl.t, seed=seed_for(6, 0, "cache"), what="a BlockSparse layer",
+                    positions=lambda t, h: oracle.blocksparse_decode_positions(t, opat, h))
+    if name == "pageddecode128k":
+        return dict(kind="decode", t=wl.t, seed=seed_for(8, 0, "cache"), what="a full layer",
+                    positions=lambda t, h: oracle.decode_positions(t))
+    return None
 
 
 # ----------------------------------------------------------------------------
@@ -614,6 +773,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="hybrid128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="hybrid128k: skip timing the other configurations after the step")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
                     help="print a summary of a rocprofv3 --stats kernel_stats.csv and exit")
@@ -657,6 +818,12 @@ def main():
     times = timer.collect()
     log(f"[bench] timed {args.steps} steps in {wall:.2f} s")
     rep = wl.report(times, args.steps)
+    spec = None if args.no_cpu_baseline else baseline_spec(args.workload, wl)
+    del wl
+    torch.cuda.empty_cache()
+    configs = None
+    if args.workload == "hybrid128k" and not args.no_configs:
+        configs = config_sweep()
     line = {
         "metric": "effective TFLOP/s (computed blocks) sparse prefill @128K; decode tok/s",
         "value": rep["value"],
@@ -677,9 +844,12 @@ def main():
         "span_ms": {k: {"n": len(v), "median": float(np.median(v)), "min": float(min(v))}
                     for k, v in sorted(times.items())},
     }
-    if not args.no_cpu_baseline:
+    if configs is not None:
+        # every configuration of the workload definitions, timed in this run
+        line["configs"] = configs
+    if spec is not None:
         log("[bench] timing the CPU oracle baseline")
-        line["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(spec, args.cpu_budget)
     print(json.dumps(line), flush=True)
 
 
