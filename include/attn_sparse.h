@@ -21,8 +21,9 @@
  *  - Device pointers are HIP device (or managed) pointers; `stream` is a
  *    hipStream_t passed as void* (NULL = the default stream).
  *  - Ownership: the caller allocates and frees every buffer (tensors, index,
- *    workspace).  The library allocates no device memory, keeps no mutable
- *    global state, and is reentrant.
+ *    workspace).  The library allocates no device memory and is reentrant.
+ *    Its only global state belongs to attn_full_decode_noalloc: a fixed
+ *    device array per GPU and the cached addresses of those arrays.
  *  - Errors: arguments are checked synchronously.  On a negative status
  *    nothing has been enqueued and no output has been touched.  A failed
  *    kernel launch returns ATTN_ERR_HIP.  Faults inside kernels surface at the
@@ -327,6 +328,28 @@ attn_status_t attn_full_decode(attn_dtype_t dtype, int32_t B, int32_t H,
                                const void *v_new, void *k_cache, void *v_cache,
                                void *o, float *lse, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/* attn_full_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The split-KV partials live in a fixed
+ * 8 MiB device array inside the library (one copy per GPU, held until the
+ * process ends; its address is looked up on the first call on each device,
+ * with the caller's current device, which must be the one holding the
+ * tensors).  The call allocates nothing.  Arguments, layouts and errors as
+ * attn_full_decode; partials beyond 8 MiB -- B*H*n_split*(d+2)*4 bytes, at
+ * most (4096 + B*H)*(d+2)*4: every B*H <= 12000 fits at d = 128 -- give
+ * ATTN_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be ordered by the caller.  Nothing in the
+ * array needs clearing between calls (every partial read is written first
+ * in the same call). */
+attn_status_t attn_full_decode_noalloc(attn_dtype_t dtype, int32_t B, int32_t H,
+                                       int32_t d, float scale, int64_t capacity,
+                                       int64_t max_pos, const int64_t *dev_pos,
+                                       const void *q, const void *k_new,
+                                       const void *v_new, void *k_cache,
+                                       void *v_cache, void *o, float *lse,
+                                       void *stream);
 
 /* Decode one new token per sequence in a full-attention layer whose cache
  * is paged: a pool of 64-token pages shared by the batch, each sequence

@@ -57,7 +57,7 @@ EXPORTED = (
     "attn_sparse_decode", "attn_full_decode", "attn_ring_fill", "attn_blocksparse_decode",
     "attn_blocksparse_cache_fill", "attn_paged_decode", "attn_paged_cache_fill",
     "attn_sparse_fwd_strided", "attn_sparse_bwd_strided", "attn_blocksparse_strided_capacity",
-    "attn_blocksparse_cache_slots",
+    "attn_blocksparse_cache_slots", "attn_full_decode_noalloc",
 )
 
 
@@ -129,6 +129,9 @@ def lib():
         L.attn_full_decode.restype = i32
         L.attn_full_decode.argtypes = [i32, i32, i32, i32, f32, i64, i64, vp, vp, vp, vp,
                                        vp, vp, vp, vp, vp, sz, vp]
+        L.attn_full_decode_noalloc.restype = i32
+        L.attn_full_decode_noalloc.argtypes = [i32, i32, i32, i32, f32, i64, i64, vp, vp, vp, vp,
+                                               vp, vp, vp, vp, vp]
         L.attn_ring_fill.restype = i32
         L.attn_ring_fill.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp, vp,
                                      vp]
@@ -547,6 +550,28 @@ def attn_full_decode(q, k_new, v_new, k_cache, v_cache, pos, max_pos: int, scale
                                   op, lp, wp, workspace.numel() * workspace.element_size(),
                                   _stream()),
            "attn_full_decode")
+    return o, lse
+
+
+def attn_full_decode_noalloc(q, k_new, v_new, k_cache, v_cache, pos, max_pos: int, scale=None,
+                             o=None, lse=None):
+    """attn_full_decode with its split-KV partials in the library's fixed
+    per-GPU scratch array: the C call allocates nothing (pass ``o`` and
+    ``lse`` to allocate nothing here either).  Calls that overlap on one GPU
+    share that array and race."""
+    torch = _torch()
+    B, H, d, o, lse, ptrs = _decode_io(q, k_new, v_new, o, lse)
+    cap = k_cache.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    kc = _dev(k_cache, "k_cache", (B, H, cap, d), q.dtype, q.device)
+    vc = _dev(v_cache, "v_cache", (B, H, cap, d), q.dtype, q.device)
+    pp = _dev(pos, "pos", (B,), torch.int64, q.device)
+    op = _dev(o, "o", q.shape, q.dtype, q.device)
+    lp = _dev(lse, "lse", (B, H), torch.float32, q.device)
+    with torch.cuda.device(q.device):
+        _check(lib().attn_full_decode_noalloc(_dtype_code(q), B, H, d, scale, cap, max_pos, pp, *ptrs,
+                                              kc, vc, op, lp, _stream()),
+               "attn_full_decode_noalloc")
     return o, lse
 
 

@@ -341,6 +341,25 @@ attn_status_t attn_full_decode(attn_dtype_t dtype, int32_t B, int32_t H, int32_t
                        k_cache, v_cache, o, lse, workspace, workspace_bytes, stream);
 }
 
+attn_status_t attn_full_decode_noalloc(attn_dtype_t dtype, int32_t B, int32_t H, int32_t d,
+                                       float scale, int64_t capacity, int64_t max_pos,
+                                       const int64_t *dev_pos, const void *q, const void *k_new,
+                                       const void *v_new, void *k_cache, void *v_cache, void *o,
+                                       float *lse, void *stream) {
+  // Every other argument is checked first: without a workspace,
+  // attn_full_decode returns ATTN_ERR_WORKSPACE exactly when all its other
+  // checks pass (its workspace check comes last), and enqueues nothing.
+  const attn_status_t st = attn_full_decode(dtype, B, H, d, scale, capacity, max_pos, dev_pos, q,
+                                            k_new, v_new, k_cache, v_cache, o, lse, nullptr, 0,
+                                            stream);
+  if (st != ATTN_ERR_WORKSPACE) return st;
+  void *ws = nullptr;
+  if (attn::decode_scratch(&ws) != hipSuccess) return ATTN_ERR_HIP;
+  // partials beyond the fixed scratch: ATTN_ERR_WORKSPACE, nothing enqueued
+  return attn_full_decode(dtype, B, H, d, scale, capacity, max_pos, dev_pos, q, k_new, v_new,
+                          k_cache, v_cache, o, lse, ws, attn::kDecodeScratchBytes, stream);
+}
+
 attn_status_t attn_paged_decode(attn_dtype_t dtype, int32_t B, int32_t H, int32_t d, float scale,
                                 int32_t n_pages, int32_t max_pages,
                                 const int32_t *dev_block_table, int64_t max_pos,

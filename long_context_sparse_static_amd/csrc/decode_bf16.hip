@@ -24,8 +24,17 @@
 // [n_pages, H, 64, d], token p of sequence b in page table[b][p / 64] at
 // row p % 64; a page id outside [0, n_pages) reads nothing and makes the
 // result NaN.
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
+
+// Fixed split-KV partial buffer for callers that cannot allocate device
+// memory (attn_full_decode_noalloc).  Each GPU the library runs on holds its
+// own copy, at its own address, until the process ends; host code reaches it
+// only through the address hipGetSymbolAddress returns for the current device
+// (the name itself is a host-side stand-in, not a device address).
+static __device__ __align__(256) float scratch[attn::kDecodeScratchBytes / sizeof(float)];
 
 namespace attn {
 namespace {
@@ -435,6 +444,27 @@ int32_t decode_split_bound(int32_t B, int32_t H, int64_t n_keys) {
   int64_t ns = (n_keys + 511) / 512;
   if (ns > want) ns = want;
   return (int32_t)(ns < 1 ? 1 : ns);
+}
+
+hipError_t decode_scratch(void **ptr) {
+  // one lookup per device, with that device current; kept for the process
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {

@@ -135,6 +135,13 @@ size_t fwd_bf16_lds_bytes(int d, int n_kblocks);
 size_t bwd_bf16_lds_bytes(int d, int n_blocks);  // the larger (dK/dV) backward kernel
 constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024;
 
+// Size of the fixed per-device decode scratch (split-KV partials of
+// attn_full_decode_noalloc): B*H*n_split*(d+2) floats must fit.
+constexpr size_t kDecodeScratchBytes = 8u << 20;
+// Device address of the current device's decode scratch (looked up once per
+// device, then cached).
+hipError_t decode_scratch(void **ptr);
+
 // Split-KV sizing shared by the workspace query and the decode launcher.
 void decode_split_plan(int32_t B, int32_t H, int64_t n_keys, int32_t *n_split,
                        int32_t *split_len);

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     assert sorted(lcs.EXPORTED) == names
     L = lcs.lib()
     for n in names:
@@ -262,6 +262,14 @@ def test_decode_validation_errors():
     assert fd(max_pos=1000) == lcs.ATTN_ERR_INVALID_ARG       # max_pos >= capacity
     assert fd(max_pos=-1) == lcs.ATTN_ERR_INVALID_ARG
     assert fd(wsb=8) == lcs.ATTN_ERR_WORKSPACE
+
+    def fdn(cap=1000, max_pos=999, B=2, d=128):
+        return L_.attn_full_decode_noalloc(lcs.ATTN_BF16, B, 4, d, 0.1, cap, max_pos, FAKE, FAKE,
+                                           FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    # argument errors come back before the fixed scratch is looked up (no GPU here)
+    assert fdn(max_pos=1000) == lcs.ATTN_ERR_INVALID_ARG
+    assert fdn(B=0) == lcs.ATTN_ERR_INVALID_ARG
+    assert fdn(d=80) == lcs.ATTN_ERR_UNSUPPORTED
 
     rf = L_.attn_ring_fill
     assert rf(lcs.ATTN_BF16, 1, 1, 128, 64, 0, FAKE, FAKE, FAKE, 10, FAKE, FAKE, None) == lcs.ATTN_ERR_INVALID_ARG
