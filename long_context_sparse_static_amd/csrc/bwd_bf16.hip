@@ -307,11 +307,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// dK, dV: one workgroup per 128 key tokens (two key blocks), union of their
-// CSC lists.  8 waves as 4 pairs; pair p (waves p and p + 4, which share
-// SIMD p) owns 32 keys (lane = key) and splits each listed query block by
-// its 32-query halves: wave p takes half 0 and accumulates dV, wave p + 4
-// takes half 1 and accumulates dK.  Per block, each wave on its half:
+// dK, dV: one workgroup per 64 key tokens (one key block, its CSC list),
+// two workgroups per CU.  4 waves as 2 pairs; pair p (waves p and p + 2)
+// owns 32 keys (lane = key) and splits each listed query block by its
+// 32-query halves: wave p takes half 0 and accumulates dV, wave p + 2 takes
+// half 1 and accumulates dK.  The two workgroups on a CU share each SIMD
+// (one wave each) and run unsynchronised, so one's vector work overlaps the
+// other's matrix work; within a workgroup the pair's waves work in step.  Per block, each wave on its half:
 //   S = Q K^T, dP = dO V^T - D (the accumulator starts at -D),
 //   P = exp2(S c - LSE2) (masked), dS = P dP, both packed to bf16;
 // then the pair trades through LDS what the other's product needs (wave p
@@ -322,11 +324,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 // registers and runs alone), and the two halves of the vector work run on
 // the two waves.  Q and dO are read as rows and transposed (kBothRead).
 // ----------------------------------------------------------------------------
-constexpr int kDkvWaves = 8;
+constexpr int kDkvWaves = 4;
 constexpr int kDkvThreads = kDkvWaves * 64;
+constexpr int kDkvPairs = kDkvWaves / 2;
+constexpr int kDkvTB = kDkvPairs / 2;   // key blocks per workgroup (two pairs per block)
 
 template <int D, bool WIN, bool DENSE>
-__global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kDkvThreads, 8 / kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   using QT = SwzTile<D, kBothRead>;
   constexpr int KS = D / 16, MT = D / 32;
   __shared__ __attribute__((aligned(1024))) char q0[QT::TILE];
@@ -340,11 +344,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // the pairs' exchange: xch[pair][side][j][lane] is packed operand j (the
   // B operand of k-step j of that half) sent by side 0 (dS of half 0) or
   // side 1 (P of half 1); consecutive lanes, consecutive 16 bytes
-  __shared__ __attribute__((aligned(1024))) bf16x8 xch[4][2][2][64];
+  __shared__ __attribute__((aligned(1024))) bf16x8 xch[kDkvPairs][2][2][64];
   extern __shared__ uint32_t dyn_lds[];
 
   const int nkb = a.ix.n_kblocks, nqb = a.ix.n_qblocks;
-  using KTiles = KeyTiles<kBwdTB>;
+  using KTiles = KeyTiles<kDkvTB>;
   const int n_tiles = KTiles::per_head(nkb, a.kgroup);
   const int n_first = KTiles::priority(nkb, a.kgroup);
   const int BH = a.B * a.H;
@@ -372,9 +376,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int hidx = a.ix.n_heads == 1 ? 0 : bh % a.H;
   KTiles kt;
   kt.init(nkb, a.kgroup, bh % a.H);
-  int krows[kBwdTB];
+  int krows[kDkvTB];
 #pragma unroll
-  for (int r = 0; r < kBwdTB; ++r) krows[r] = kt.block(tile, r);
+  for (int r = 0; r < kDkvTB; ++r) krows[r] = kt.block(tile, r);
   // token-row strides: compile-time for contiguous [B,H,L,d] tensors
   const int bb = bh / a.H, head = bh % a.H;
   const size_t dense_base = (size_t)bh * a.L * D;
@@ -387,8 +391,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, hh = lane >> 5;
-  const bool side0 = wave < 4;     // query half 0 and dV (else half 1 and dK)
-  const int pair = wave & 3;
+  const bool side0 = wave < kDkvPairs;   // query half 0 and dV (else half 1 and dK)
+  const int pair = wave % kDkvPairs;
   const int my_r = pair >> 1;
   const int kb = krows[my_r];
   const bool k_valid = kb >= 0;
@@ -430,11 +434,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     load_vec(i, lv, ev);
   };
 
-  RowsBitmap<kBwdTB> pb;
+  RowsBitmap<kDkvTB> pb;
   pb.init(dyn_lds, nqb);
   pb.build_rows(a.ix.col_ptr + (size_t)hidx * (nkb + 1), krows, a.ix.nnz, a.ix.row_idx, nqb,
                 kDkvThreads);
-  RowsIter<kBwdTB> it;
+  RowsIter<kDkvTB> it;
   it.start(nqb, (krows[0] + 63) & ~63);
   auto advance = [&]() __attribute__((always_inline)) -> BwdPos {
     BwdPos p;
@@ -618,9 +622,9 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const int rpb = 256 / (D / 8);
   const int grid_delta = (int)((rows + rpb - 1) / rpb);
   const int q_tiles = (a.ix.n_qblocks + kBwdTB - 1) / kBwdTB;
-  const int k_tiles = KeyTiles<kBwdTB>::per_head(a.ix.n_kblocks, a.kgroup);
+  const int k_tiles = KeyTiles<kDkvTB>::per_head(a.ix.n_kblocks, a.kgroup);
   const int BH = a.B * a.H;
-  const size_t dyn_k = RowsBitmap<kBwdTB>::lds_bytes(a.ix.n_qblocks);
+  const size_t dyn_k = RowsBitmap<kDkvTB>::lds_bytes(a.ix.n_qblocks);
   const size_t dyn_q = RowsBitmap<kBwdTB>::lds_bytes(a.ix.n_kblocks);
   hipError_t e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel<D, WIN, DENSE>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_k);
@@ -638,9 +642,9 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
 
 size_t bwd_bf16_lds_bytes(int d, int n_blocks) {
   // dK/dV kernel: two Q and two dO slots, four 64-float vectors, the
-  // packed-operand exchange (4 pairs x 4 KB), bitmaps
-  const size_t tiles = 4 * (size_t)kBlock * 2 * d + 4 * kBlock * sizeof(float) + 4 * 4 * 64 * 16;
-  return tiles + RowsBitmap<kBwdTB>::lds_bytes(n_blocks);
+  // packed-operand exchange (4 KB per pair), bitmaps
+  const size_t tiles = 4 * (size_t)kBlock * 2 * d + 4 * kBlock * sizeof(float) + kDkvPairs * 4 * 64 * 16;
+  return tiles + RowsBitmap<kDkvTB>::lds_bytes(n_blocks);
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s) {
