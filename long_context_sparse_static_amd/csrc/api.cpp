@@ -123,7 +123,7 @@ attn_status_t fwd_impl(attn_dtype_t dtype, int32_t B, int32_t H, int64_t L, int3
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (dtype == ATTN_BF16 && attn::fwd_bf16_lds_bytes(d, dev_index->n_kblocks) > attn::kMaxLdsPerWorkgroup)
-    return ATTN_ERR_UNSUPPORTED;  // union bitmap of more than ~3.4M key blocks
+    return ATTN_ERR_UNSUPPORTED;  // union bitmap of more than ~65K key blocks (~4M tokens)
   attn::FwdArgs a;
   a.q = q;
   a.k = k;

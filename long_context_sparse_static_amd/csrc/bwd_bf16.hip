@@ -293,17 +293,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   while (step(even) && step(odd)) {
   }
 
+  // every wave is done with the K slots (no loads in flight after the walk):
+  // they stage the output rows, waves 0-1 in k0, 2-3 in k1
+  __syncthreads();
   if (!q_valid) return;
-  bf16 *out = (bf16 *)a.dq + (DENSE ? dense_base : a.dqs.at(bb, head)) + (size_t)q_tok * ldq;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x2 w;
-      w[0] = pack_bf16x2(acc[mt][4 * g] * a.scale, acc[mt][4 * g + 1] * a.scale);
-      w[1] = pack_bf16x2(acc[mt][4 * g + 2] * a.scale, acc[mt][4 * g + 3] * a.scale);
-      *(u32x2 *)(out + 32 * mt + 8 * g + 4 * hh) = w;
-    }
+  store_rows_staged<D>(acc, a.scale, (wave < 2 ? k0 : k1) + (wave & 1) * 32 * 2 * D,
+                       (bf16 *)a.dq + (DENSE ? dense_base : a.dqs.at(bb, head)) + (size_t)q_wave * ldq, ldq,
+                       lane);
 }
 
 // ----------------------------------------------------------------------------
@@ -601,19 +597,16 @@ __global__ __launch_bounds__(kDkvThreads, 8 / kDkvWaves) void bwd_dkdv_kernel(Bw
     }
   }
 
+  // every wave is done with the Q slots (no loads in flight after the walk):
+  // they stage the output rows, waves 0-1 in q0, 2-3 in q1
+  static_assert(kDkvWaves == 4, "output staging holds two waves per Q slot");
+  __syncthreads();
   if (!k_valid) return;
-  bf16 *out = side0 ? (bf16 *)a.dv + (DENSE ? dense_base : a.dvs.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.dvs.l)
-                    : (bf16 *)a.dk + (DENSE ? dense_base : a.dks.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.dks.l);
-  const float sc = side0 ? 1.0f : a.scale;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x2 w;
-      w[0] = pack_bf16x2(acc[mt][4 * g] * sc, acc[mt][4 * g + 1] * sc);
-      w[1] = pack_bf16x2(acc[mt][4 * g + 2] * sc, acc[mt][4 * g + 3] * sc);
-      *(u32x2 *)(out + 32 * mt + 8 * g + 4 * hh) = w;
-    }
+  const int ld_out = side0 ? (DENSE ? D : a.dvs.l) : (DENSE ? D : a.dks.l);
+  bf16 *out = side0 ? (bf16 *)a.dv + (DENSE ? dense_base : a.dvs.at(bb, head)) + (size_t)k_wave * ld_out
+                    : (bf16 *)a.dk + (DENSE ? dense_base : a.dks.at(bb, head)) + (size_t)k_wave * ld_out;
+  store_rows_staged<D>(acc, side0 ? 1.0f : a.scale, (wave < 2 ? q0 : q1) + (wave & 1) * 32 * 2 * D, out,
+                       ld_out, lane);
 }
 
 template <int D, bool WIN, bool DENSE>

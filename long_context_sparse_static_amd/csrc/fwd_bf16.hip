@@ -78,6 +78,12 @@ struct FwdLayout {
   __host__ __device__ static int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
+// Byte offset of the output staging inside the dynamic LDS (after the
+// union bitmaps, 16-byte aligned).
+__host__ __device__ inline size_t fwd_ostage_offset(int n_kblocks) {
+  return (RowsBitmap<kFwdQB>::lds_bytes(n_kblocks) + 15) & ~(size_t)15;
+}
+
 // One position of the union walk.
 struct WalkPos {
   bool valid;
@@ -101,6 +107,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char k1[Lay::TILE];
   __shared__ __attribute__((aligned(1024))) char v0[Lay::TILE];
   __shared__ __attribute__((aligned(1024))) char v1[Lay::TILE];
+  // dynamic LDS: the union bitmaps, then each wave's 32 output rows on their
+  // way to global memory (kept after the static tiles, whose offsets then
+  // stay within the 16-bit immediates of the operand reads)
   extern __shared__ uint32_t dyn_lds[];
 
   const int nqb = a.ix.n_qblocks;
@@ -444,16 +453,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   if (!q_valid) return;
   const float l_tot = lacc[0];   // sum of P' of the row (bf16-rounded, as in P V)
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  bf16 *orow = (bf16 *)a.o + (DENSE ? dense_base : a.os.at(bb, head)) + (size_t)q_tok * lo_;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x2 w;
-      w[0] = pack_bf16x2(oacc[mt][4 * g] * inv, oacc[mt][4 * g + 1] * inv);
-      w[1] = pack_bf16x2(oacc[mt][4 * g + 2] * inv, oacc[mt][4 * g + 3] * inv);
-      *(u32x2 *)(orow + 32 * mt + 8 * g + 4 * hh) = w;
-    }
+  // O leaves through the wave's own LDS area as contiguous row runs
+  store_rows_staged<D>(oacc, inv, (char *)dyn_lds + fwd_ostage_offset(a.ix.n_kblocks) + wave * 32 * RB,
+                       (bf16 *)a.o + (DENSE ? dense_base : a.os.at(bb, head)) + (size_t)q_wave * lo_, lo_,
+                       lane);
   if (hh == 0)
     // 2^63 l' = l exactly (a power-of-two scale): log2 of it, not of l', so
     // the LSE keeps full precision
@@ -464,7 +467,7 @@ template <int D, bool WIN, bool DENSE>
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
   const int n_tiles = (a.ix.n_qblocks + kFwdQB - 1) / kFwdQB;
   const int grid = a.B * a.H * n_tiles;
-  const size_t dyn = RowsBitmap<kFwdQB>::lds_bytes(a.ix.n_kblocks);
+  const size_t dyn = fwd_ostage_offset(a.ix.n_kblocks) + (size_t)kFwdWaves * 32 * FwdLayout<D>::RB;
   hipError_t e = hipFuncSetAttribute((const void *)fwd_bf16_kernel<D, WIN, DENSE>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
   if (e != hipSuccess) return e;
@@ -483,8 +486,8 @@ hipError_t launch_fwd_layout(const FwdArgs &a, hipStream_t s) {
 }  // namespace
 
 size_t fwd_bf16_lds_bytes(int d, int n_kblocks) {
-  // two K slots, two V slots, the union bitmaps
-  return 4 * (size_t)kBlock * 2 * d + RowsBitmap<kFwdQB>::lds_bytes(n_kblocks);
+  // two K slots, two V slots, the waves' output staging, the union bitmaps
+  return 4 * (size_t)kBlock * 2 * d + fwd_ostage_offset(n_kblocks) + (size_t)kFwdWaves * 32 * 2 * d;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s) {

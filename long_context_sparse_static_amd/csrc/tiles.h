@@ -94,6 +94,37 @@ struct SwzTile {
   }
 };
 
+// Stores a wave's 32 x D fp32 accumulator (the transposed-product layout:
+// lane (n, hh) = (lane % 32, lane / 32) holds row n, register r of tile mt
+// holds column 32 mt + 8 (r / 4) + 4 hh + r % 4), times sc, rounded to bf16,
+// to rows out[n * ld ..] through the wave's LDS area st (32 * 2 D bytes):
+// written in that layout with the 16-byte chunks of a row XOR-swizzled by
+// the row (the writes spread over the banks), read back as whole chunks of
+// consecutive rows and stored as contiguous 1 KB runs -- not as 8-byte
+// pieces of 32 different rows per store instruction.
+template <int D>
+__device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[D / 32], float sc, char *st,
+                                                  bf16 *out, int ld, int lane) {
+  constexpr int RB = 2 * D, CPR = RB / 16, RPS = 1024 / RB;
+  const int n = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[mt][4 * g] * sc, acc[mt][4 * g + 1] * sc);
+      w[1] = pack_bf16x2(acc[mt][4 * g + 2] * sc, acc[mt][4 * g + 3] * sc);
+      const int ch = 4 * mt + g;   // columns 8 ch + 4 hh .. +3
+      *(u32x2 *)(st + n * RB + ((ch ^ (n & (CPR - 1))) << 4) + (hh << 3)) = w;
+    }
+#pragma unroll
+  for (int i = 0; i < 32 / RPS; ++i) {
+    const int r = i * RPS + lane / CPR, ch = lane % CPR;
+    const u32x4 v = *(const u32x4 *)(st + r * RB + ((ch ^ (r & (CPR - 1))) << 4));
+    *(u32x4 *)(out + (size_t)r * ld + ch * 8) = v;
+  }
+}
+
 // Union of R consecutive CSR (or CSC) rows -- the 64-token blocks of one
 // workgroup tile -- held as R LDS bitmaps over block ids plus a summary
 // bitmap of the non-empty words.  Built once per workgroup (atomicOr per list
