@@ -224,7 +224,10 @@ size_t attn_workspace_bytes(int32_t op, attn_dtype_t dtype, int32_t B,
  *   the listed blocks of every head.  Sliding with causal == 0 is
  *   ATTN_ERR_INVALID_ARG.
  *   q, k, v: [B,H,L,d] in; o: [B,H,L,d] out; lse: [B,H,L] fp32 out.
- *   Rows with no allowed key give O = 0, LSE = -inf.  No workspace. */
+ *   Rows with no allowed key give O = 0, LSE = -inf.  No workspace.
+ *   Length limit of the bf16 path (its per-workgroup LDS holds a bitmap
+ *   over the key blocks): L <= 4,161,536 tokens at d = 128 and about 12.4M
+ *   at d = 64; longer sequences give ATTN_ERR_UNSUPPORTED. */
 attn_status_t attn_sparse_fwd(attn_dtype_t dtype, int32_t B, int32_t H,
                               int64_t L, int32_t d, float scale,
                               const attn_pattern_t *pattern,

@@ -223,6 +223,9 @@ def test_forward_validation_errors():
     assert _fwd(ix=bad_heads) == lcs.ATTN_ERR_INVALID_ARG            # n_heads not 1 or H
     p = lcs.attn_pattern_t(1, 32, 1, 2, 0, 1)
     assert _fwd(pattern=p) == lcs.ATTN_ERR_INVALID_ARG               # block != 64
+    # one key block past the bf16 path's LDS bitmap limit (4,161,536 tokens at
+    # d = 128): rejected before any launch
+    assert _fwd(B=1, H=1, L=4161536 + 64) == lcs.ATTN_ERR_UNSUPPORTED
 
 
 def test_backward_validation_errors():
