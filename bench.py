@@ -714,11 +714,16 @@ N_XCD, N_SIMD = 8, 1024   # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 
 
 def summarize_mfma(path):
-    """Per attention kernel, from one rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
-    GRBM_GUI_ACTIVE run: the matrix-core busy fraction (busy cycles summed
-    over SIMDs / (GPU-active cycles of one XCD x SIMDs), the profiler's own
-    MfmaUtil) and the clock the kernel ran at (GPU-active cycles of one XCD /
-    dispatch time), averaged over dispatches."""
+    """Per attention kernel, from one rocprofv3 --pmc run with
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE (optionally also
+    SQ_ACTIVE_INST_VALU and SQ_VALU_MFMA_COEXEC_CYCLES): the matrix-core busy
+    fraction (busy cycles summed over SIMDs / (GPU-active cycles of one XCD x
+    SIMDs), the profiler's own MfmaUtil), the clock the kernel ran at
+    (GPU-active cycles of one XCD / dispatch time), and -- when present --
+    the fraction of SIMD cycles with a vector instruction at work
+    (SQ_ACTIVE_INST_VALU counts quad-cycles) and the share of those cycles
+    issued while the matrix core was busy (co-issue), averaged over
+    dispatches."""
     import csv
     per = {}
     for r in csv.DictReader(open(path)):
@@ -728,16 +733,25 @@ def summarize_mfma(path):
         d = per.setdefault(key, {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
         d[r["Counter_Name"]] = float(r["Counter_Value"])
     acc = {}
+    extra = False
     for (name, _), d in per.items():
         if "SQ_VALU_MFMA_BUSY_CYCLES" not in d or "GRBM_GUI_ACTIVE" not in d:
             continue
         active = d["GRBM_GUI_ACTIVE"] / N_XCD
-        acc.setdefault(name, []).append((d["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * N_SIMD),
-                                         active / d["ns"], d["ns"] / 1e6))
-    out = [f"{'kernel':72s} {'n':>3s} {'avg ms':>8s} {'MFMA busy':>10s} {'clock GHz':>10s}"]
+        row = [d["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * N_SIMD), active / d["ns"], d["ns"] / 1e6]
+        if "SQ_ACTIVE_INST_VALU" in d and "SQ_VALU_MFMA_COEXEC_CYCLES" in d:
+            valu = 4 * d["SQ_ACTIVE_INST_VALU"]
+            row += [valu / (active * N_SIMD), d["SQ_VALU_MFMA_COEXEC_CYCLES"] / valu if valu else 0.0]
+            extra = True
+        acc.setdefault(name, []).append(row)
+    head = f"{'kernel':72s} {'n':>3s} {'avg ms':>8s} {'MFMA busy':>10s} {'clock GHz':>10s}"
+    out = [head + (f" {'VALU active':>12s} {'co-issued':>10s}" if extra else "")]
     for name, v in sorted(acc.items(), key=lambda kv: -sum(x[2] for x in kv[1])):
-        busy, clk, ms = (sum(x[i] for x in v) / len(v) for i in range(3))
-        out.append(f"{_short(name):72s} {len(v):3d} {ms:8.3f} {100 * busy:9.1f}% {clk:10.3f}")
+        cols = [sum(x[i] for x in v) / len(v) for i in range(len(v[0]))]
+        line = f"{_short(name):72s} {len(v):3d} {cols[2]:8.3f} {100 * cols[0]:9.1f}% {cols[1]:10.3f}"
+        if len(cols) > 3:
+            line += f" {100 * cols[3]:11.1f}% {100 * cols[4]:9.1f}%"
+        out.append(line)
     return "\n".join(out)
 
 

@@ -41,6 +41,23 @@ def test_mfma_busy_and_clock(tmp_path):
     assert fields[-4:] == ["2", "2.000", "60.0%", "1.800"]
 
 
+def test_mfma_coissue_columns(tmp_path):
+    """With SQ_ACTIVE_INST_VALU (quad-cycles) and SQ_VALU_MFMA_COEXEC_CYCLES:
+    vector-active share of SIMD cycles and the co-issued share of it."""
+    name = "void attn::(anonymous namespace)::bwd_dq_kernel<128, false, true>(attn::BwdArgs)"
+    ns = 1_000_000
+    per_xcd = 1.9e6
+    cyc = per_xcd * bench.N_SIMD                     # SIMD cycles of the dispatch
+    rows = [(1, name, "GRBM_GUI_ACTIVE", per_xcd * bench.N_XCD, 0, ns),
+            (1, name, "SQ_VALU_MFMA_BUSY_CYCLES", 0.6 * cyc, 0, ns),
+            (1, name, "SQ_ACTIVE_INST_VALU", 0.4 * cyc / 4, 0, ns),   # 40% of cycles, in quad-cycles
+            (1, name, "SQ_VALU_MFMA_COEXEC_CYCLES", 0.3 * cyc, 0, ns)]  # 75% of those co-issued
+    out = bench.summarize_mfma(_write(tmp_path / "c.csv", rows)).splitlines()
+    assert "VALU active" in out[0] and "co-issued" in out[0]
+    fields = out[1].split()
+    assert fields[-6:] == ["1", "1.000", "60.0%", "1.900", "40.0%", "75.0%"]
+
+
 def test_traffic_calibration(tmp_path):
     copy = "void at::native::vectorized_elementwise_kernel<4, copy>"
     kern = "void attn::fwd_bf16_kernel<128, false, true>(attn::FwdArgs)"
