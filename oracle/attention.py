@@ -61,12 +61,11 @@ SLIDING = "sliding"        # token-granular window (+ optional sink blocks)
 # Block lists  [index page, Abstract: window / sink / strided-block patterns;
 #               summary page, Approach: static, block-wise access]
 # ----------------------------------------------------------------------------
-def block_lists(kind, n_qblocks, *, sink_blocks=1, local_blocks=1, stride=0,
-                head=0, n_kblocks=None, window_tokens=0, block=64):
-    """Ascending KV-block list of every query block, by brute-force scan.
-
-    For query block ``i`` every key block ``j`` in ``0..n_kblocks-1`` is tested
-    for membership on its own:
+def block_list_row(kind, i, n_kblocks, *, sink_blocks=1, local_blocks=1, stride=0, head=0,
+                   window_tokens=0, block=64):
+    """Ascending KV-block list of query block ``i``, by brute-force scan:
+    every key block ``j`` in ``0..n_kblocks-1`` is tested for membership on
+    its own:
       * full:        j <= i
       * attnsink:    j < sink_blocks (and j <= i), or i-local_blocks < j <= i
       * blocksparse: the attnsink rule, or j < i with (j + head) % stride == 0
@@ -74,31 +73,36 @@ def block_lists(kind, n_qblocks, *, sink_blocks=1, local_blocks=1, stride=0,
                      within window_tokens of the first query of block i (the
                      blocks holding any key the token rule of
                      ``sliding_token_mask`` allows for some query of block i)
-    Returns a list of Python int lists.
     """
+    row = []
+    for j in range(n_kblocks):
+        if kind == FULL:
+            keep = j <= i
+        elif kind == SLIDING:
+            keep = j <= i and (j < sink_blocks or
+                               block * i - (block * j + block - 1) < window_tokens)
+        elif kind in (ATTNSINK, BLOCKSPARSE):
+            is_sink = j < sink_blocks and j <= i
+            is_local = (i - local_blocks) < j <= i
+            keep = is_sink or is_local
+            if kind == BLOCKSPARSE and not keep and stride > 0:
+                keep = j < i and (j + head) % stride == 0
+        else:
+            raise ValueError(f"unknown pattern kind {kind!r}")
+        if keep:
+            row.append(j)
+    return row
+
+
+def block_lists(kind, n_qblocks, *, sink_blocks=1, local_blocks=1, stride=0,
+                head=0, n_kblocks=None, window_tokens=0, block=64):
+    """Ascending KV-block list of every query block (``block_list_row`` for
+    each of ``0..n_qblocks-1``).  Returns a list of Python int lists."""
     if n_kblocks is None:
         n_kblocks = n_qblocks
-    out = []
-    for i in range(n_qblocks):
-        row = []
-        for j in range(n_kblocks):
-            if kind == FULL:
-                keep = j <= i
-            elif kind == SLIDING:
-                keep = j <= i and (j < sink_blocks or
-                                   block * i - (block * j + block - 1) < window_tokens)
-            elif kind in (ATTNSINK, BLOCKSPARSE):
-                is_sink = j < sink_blocks and j <= i
-                is_local = (i - local_blocks) < j <= i
-                keep = is_sink or is_local
-                if kind == BLOCKSPARSE and not keep and stride > 0:
-                    keep = j < i and (j + head) % stride == 0
-            else:
-                raise ValueError(f"unknown pattern kind {kind!r}")
-            if keep:
-                row.append(j)
-        out.append(row)
-    return out
+    return [block_list_row(kind, i, n_kblocks, sink_blocks=sink_blocks, local_blocks=local_blocks,
+                           stride=stride, head=head, window_tokens=window_tokens, block=block)
+            for i in range(n_qblocks)]
 
 
 def transpose_lists(lists, n_kblocks):
@@ -233,6 +237,17 @@ def pattern_lists_for_head(pattern, n_qblocks, head):
                        stride=pattern.get("stride", 0), head=head,
                        window_tokens=pattern.get("window_tokens", 0),
                        block=pattern.get("block", 64))
+
+
+def pattern_rows_for_head(pattern, qblocks, n_kblocks, head):
+    """{i: list of query block i} for the listed query blocks only (the same
+    rows ``pattern_lists_for_head`` gives, without building every row)."""
+    p = head_pattern(pattern, head)
+    return {i: block_list_row(p["kind"], i, n_kblocks, sink_blocks=p.get("sink_blocks", 0),
+                              local_blocks=p.get("local_blocks", 0), stride=p.get("stride", 0),
+                              head=head, window_tokens=p.get("window_tokens", 0),
+                              block=p.get("block", 64))
+            for i in qblocks}
 
 
 def pattern_token_mask(pattern, head, L, rows=None, lists=None):

@@ -26,6 +26,7 @@ import torch.nn.functional as F
 from oracle import (ATTNSINK, BLOCKSPARSE, FULL, SLIDING, attention_backward,
                     attention_forward, block_lists, blocksparse_decode_positions,
                     decode_one, decode_positions, dense_token_mask, kv_cache_bytes,
+                    pattern_lists_for_head, pattern_rows_for_head,
                     pattern_token_mask, sliding_token_mask, sparse_backward,
                     sparse_forward, transpose_lists)
 
@@ -118,6 +119,18 @@ def test_workload_nnz_closed_forms():
     for h in (0, 3, 7, 12):
         got = block_lists(BLOCKSPARSE, 512, sink_blocks=1, local_blocks=16, stride=8, head=h)
         assert sum(len(r) for r in got) == per_head[h]
+
+
+@pytest.mark.parametrize("kind,extra", [(ATTNSINK, dict(sink_blocks=2, local_blocks=3)),
+                                        (BLOCKSPARSE, dict(sink_blocks=1, local_blocks=2, stride=3)),
+                                        (FULL, dict()), (SLIDING, dict(sink_blocks=1, window_tokens=150))])
+def test_row_subset_equals_whole_lists(kind, extra):
+    """Building only some query blocks' rows gives the same rows."""
+    pat = dict(kind=kind, block=64, causal=True, **extra)
+    for h in (0, 1, 2):
+        whole = pattern_lists_for_head(pat, 23, h)
+        some = pattern_rows_for_head(pat, [0, 5, 17, 22], 23, h)
+        assert all(some[i] == whole[i] for i in some)
 
 
 def test_transpose_lists_roundtrip():
