@@ -12,7 +12,7 @@ import torch
 
 import long_context_sparse_static_amd as lcs
 from oracle import (attention_backward, attention_forward, pattern_lists_for_head,
-                    pattern_token_mask, transpose_lists)
+                    pattern_rows_for_head, pattern_token_mask, transpose_lists)
 from synth_inputs import as_f64
 
 # bf16 path: max-abs 2e-2 and mean-abs 2e-3; fp32 path: max-abs 1e-5.
@@ -63,8 +63,10 @@ def sample_rows_forward(q, k, v, pattern, head, b, rows, scale=None):
     L, d = q.shape[2], q.shape[3]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     nb = L // pattern.block
-    lists = pattern_lists_for_head(oracle_pattern(pattern), nb, head)
     rows = np.asarray(sorted(rows))
+    # only the sampled query blocks' rows ({block: list})
+    lists = pattern_rows_for_head(oracle_pattern(pattern), sorted({int(r) // pattern.block for r in rows}),
+                                  nb, head)
     kblocks = sorted({j for r in rows for j in lists[r // pattern.block]})
     keys = np.concatenate([np.arange(j * pattern.block, (j + 1) * pattern.block) for j in kblocks])
     mask = pattern_token_mask(oracle_pattern(pattern), head, L, rows=rows, lists=lists)[:, keys]

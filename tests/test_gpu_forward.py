@@ -203,6 +203,29 @@ def test_bf16_full_causal_128k_sampled():
         print("full_128k", h, mx, mean)
 
 
+def test_bf16_maximum_length_sampled():
+    """The longest sequence the bf16 forward takes at d = 128: 4,161,536
+    tokens (65,024 key blocks, whose union bitmap plus the output staging
+    fill a workgroup's LDS; one block more is rejected).  AttnSink, two
+    heads; sampled rows on their exact sub-problems, among them the first and
+    last blocks and blocks on either side of bitmap word boundaries."""
+    need_gpu()
+    pat, L, H, d = lcs.attnsink_pattern(1, 64), 4161536, 2, 128
+    q, k, v = _inputs((1, H, L, d), 77, torch.bfloat16, big=True)
+    o, lse = _run(q, k, v, pat)
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    rng = np.random.default_rng(5)
+    edge_blocks = [0, 1, 63, 64, 1023, 1024, 32767, 32768, 65022, 65023]
+    for h in range(H):
+        rows = np.unique(np.concatenate([[b * 64 + r for b in edge_blocks for r in (0, 31, 63)],
+                                         rng.integers(0, L, 24)]))
+        wo, wlse = sample_rows_forward(q, k, v, pat, h, 0, rows)
+        idx = torch.as_tensor(rows, device=q.device)
+        mx, mean = assert_bf16_close(as_f64(o[0, h, idx]), wo, f"max-length O head {h}")
+        assert_bf16_close(as_f64(lse[0, h, idx]), wlse, f"max-length LSE head {h}")
+        print("max length", h, mx, mean)
+
+
 # ----------------------------------------------------------------------------
 # Per-head pattern mix (retrieval heads with full attention beside sink +
 # window streaming heads) through one index and one launch.
