@@ -61,11 +61,9 @@ SLIDING = "sliding"        # token-granular window (+ optional sink blocks)
 # Block lists  [index page, Abstract: window / sink / strided-block patterns;
 #               summary page, Approach: static, block-wise access]
 # ----------------------------------------------------------------------------
-def block_list_row(kind, i, n_kblocks, *, sink_blocks=1, local_blocks=1, stride=0, head=0,
-                   window_tokens=0, block=64):
-    """Ascending KV-block list of query block ``i``, by brute-force scan:
-    every key block ``j`` in ``0..n_kblocks-1`` is tested for membership on
-    its own:
+def block_allowed(kind, i, j, *, sink_blocks=1, local_blocks=1, stride=0, head=0,
+                  window_tokens=0, block=64):
+    """Whether query block ``i`` reads key block ``j``:
       * full:        j <= i
       * attnsink:    j < sink_blocks (and j <= i), or i-local_blocks < j <= i
       * blocksparse: the attnsink rule, or j < i with (j + head) % stride == 0
@@ -74,24 +72,29 @@ def block_list_row(kind, i, n_kblocks, *, sink_blocks=1, local_blocks=1, stride=
                      blocks holding any key the token rule of
                      ``sliding_token_mask`` allows for some query of block i)
     """
-    row = []
-    for j in range(n_kblocks):
-        if kind == FULL:
-            keep = j <= i
-        elif kind == SLIDING:
-            keep = j <= i and (j < sink_blocks or
-                               block * i - (block * j + block - 1) < window_tokens)
-        elif kind in (ATTNSINK, BLOCKSPARSE):
-            is_sink = j < sink_blocks and j <= i
-            is_local = (i - local_blocks) < j <= i
-            keep = is_sink or is_local
-            if kind == BLOCKSPARSE and not keep and stride > 0:
-                keep = j < i and (j + head) % stride == 0
-        else:
-            raise ValueError(f"unknown pattern kind {kind!r}")
-        if keep:
-            row.append(j)
-    return row
+    if kind == FULL:
+        return j <= i
+    if kind == SLIDING:
+        return j <= i and (j < sink_blocks or block * i - (block * j + block - 1) < window_tokens)
+    if kind in (ATTNSINK, BLOCKSPARSE):
+        keep = (j < sink_blocks and j <= i) or (i - local_blocks) < j <= i
+        if kind == BLOCKSPARSE and not keep and stride > 0:
+            keep = j < i and (j + head) % stride == 0
+        return keep
+    raise ValueError(f"unknown pattern kind {kind!r}")
+
+
+def block_list_row(kind, i, n_kblocks, **rule):
+    """Ascending KV-block list of query block ``i``, by brute-force scan:
+    every key block ``j`` in ``0..n_kblocks-1`` is tested on its own with
+    ``block_allowed``."""
+    return [j for j in range(n_kblocks) if block_allowed(kind, i, j, **rule)]
+
+
+def block_column(kind, j, n_qblocks, **rule):
+    """Ascending list of the query blocks that read key block ``j`` (column
+    ``j`` of the lists), by the same scan over ``0..n_qblocks-1``."""
+    return [i for i in range(n_qblocks) if block_allowed(kind, i, j, **rule)]
 
 
 def block_lists(kind, n_qblocks, *, sink_blocks=1, local_blocks=1, stride=0,
@@ -114,36 +117,50 @@ def transpose_lists(lists, n_kblocks):
     return cols
 
 
-def sliding_token_mask(n_q_tokens, n_k_tokens, sink_tokens, window_tokens, rows=None):
-    """Boolean [n_rows, n_k_tokens] of the token-granular sliding window: query
+def sliding_token_mask(n_q_tokens, n_k_tokens, sink_tokens, window_tokens, rows=None, keys=None):
+    """Boolean [n_rows, n_keys] of the token-granular sliding window: query
     position q reads key position k when k <= q and either k is one of the
     first ``sink_tokens`` tokens or q - k < ``window_tokens`` (the window
     holds the query itself and the window_tokens - 1 tokens before it).
-    With sink_tokens = 0 this is plain sliding-window attention."""
+    With sink_tokens = 0 this is plain sliding-window attention.  ``rows`` /
+    ``keys``: the query / key positions to evaluate (default: all)."""
     if rows is None:
         rows = np.arange(n_q_tokens)
+    if keys is None:
+        keys = np.arange(n_k_tokens)
     rows = np.asarray(rows)[:, None]
-    k = np.arange(n_k_tokens)[None, :]
+    k = np.asarray(keys)[None, :]
     return (k <= rows) & ((k < sink_tokens) | (rows - k < window_tokens))
 
 
-def dense_token_mask(lists, block, n_q_tokens, n_k_tokens, causal, rows=None):
-    """Boolean [n_rows, n_k_tokens]: key token allowed for a query token.
+def dense_token_mask(lists, block, n_q_tokens, n_k_tokens, causal, rows=None, keys=None):
+    """Boolean [n_rows, n_keys]: key token allowed for a query token.
 
-    ``rows`` lists the query-token positions (default 0..n_q_tokens-1).  A key
-    is allowed when its block is in the query block's list and, if
-    ``causal``, its position does not exceed the query's position.
+    ``rows`` lists the query-token positions (default 0..n_q_tokens-1),
+    ``keys`` the key-token positions (default 0..n_k_tokens-1).  A key is
+    allowed when its block is in the query block's list and, if ``causal``,
+    its position does not exceed the query's position.  ``lists`` may be a
+    dict holding only the query blocks of ``rows``.
     """
     if rows is None:
         rows = np.arange(n_q_tokens)
-    m = np.zeros((len(rows), n_k_tokens), dtype=bool)
+    if keys is None:
+        m = np.zeros((len(rows), n_k_tokens), dtype=bool)
+        for n, qi in enumerate(rows):
+            for j in lists[qi // block]:
+                lo = j * block
+                hi = min(lo + block, n_k_tokens)
+                m[n, lo:hi] = True
+            if causal:
+                m[n, qi + 1:] = False
+        return m
+    keys = np.asarray(keys)
+    kb = keys // block
+    m = np.zeros((len(rows), len(keys)), dtype=bool)
     for n, qi in enumerate(rows):
-        for j in lists[qi // block]:
-            lo = j * block
-            hi = min(lo + block, n_k_tokens)
-            m[n, lo:hi] = True
+        m[n] = np.isin(kb, lists[qi // block]) & (keys < n_k_tokens)
         if causal:
-            m[n, qi + 1:] = False
+            m[n] &= keys <= qi
     return m
 
 
@@ -239,29 +256,40 @@ def pattern_lists_for_head(pattern, n_qblocks, head):
                        block=pattern.get("block", 64))
 
 
+def _rule(p, head):
+    return dict(sink_blocks=p.get("sink_blocks", 0), local_blocks=p.get("local_blocks", 0),
+                stride=p.get("stride", 0), head=head, window_tokens=p.get("window_tokens", 0),
+                block=p.get("block", 64))
+
+
 def pattern_rows_for_head(pattern, qblocks, n_kblocks, head):
     """{i: list of query block i} for the listed query blocks only (the same
     rows ``pattern_lists_for_head`` gives, without building every row)."""
     p = head_pattern(pattern, head)
-    return {i: block_list_row(p["kind"], i, n_kblocks, sink_blocks=p.get("sink_blocks", 0),
-                              local_blocks=p.get("local_blocks", 0), stride=p.get("stride", 0),
-                              head=head, window_tokens=p.get("window_tokens", 0),
-                              block=p.get("block", 64))
-            for i in qblocks}
+    return {i: block_list_row(p["kind"], i, n_kblocks, **_rule(p, head)) for i in qblocks}
 
 
-def pattern_token_mask(pattern, head, L, rows=None, lists=None):
-    """Dense [n_rows, L] mask of head ``head``: the token rule for a sliding
-    pattern, else the block lists expanded to tokens (causal inside blocks).
-    ``lists``: this head's block lists if the caller already holds them
-    (pattern_lists_for_head's result), to skip building them again."""
+def pattern_column_for_head(pattern, j, n_qblocks, head):
+    """Ascending query blocks of head ``head`` that read key block ``j`` (the
+    column ``transpose_lists`` gives, without building every row)."""
+    p = head_pattern(pattern, head)
+    return block_column(p["kind"], j, n_qblocks, **_rule(p, head))
+
+
+def pattern_token_mask(pattern, head, L, rows=None, lists=None, keys=None):
+    """Dense [n_rows, n_keys] mask of head ``head``: the token rule for a
+    sliding pattern, else the block lists expanded to tokens (causal inside
+    blocks).  ``lists``: this head's block lists if the caller already holds
+    them (pattern_lists_for_head's result, or a dict of the rows' blocks), to
+    skip building them again.  ``rows`` / ``keys``: the positions to evaluate
+    (default: all)."""
     p = head_pattern(pattern, head)
     if p["kind"] == SLIDING:
         return sliding_token_mask(L, L, p["block"] * p.get("sink_blocks", 0),
-                                  p["window_tokens"], rows=rows)
+                                  p["window_tokens"], rows=rows, keys=keys)
     if lists is None:
         lists = pattern_lists_for_head(pattern, L // p["block"], head)
-    return dense_token_mask(lists, p["block"], L, L, p.get("causal", True), rows=rows)
+    return dense_token_mask(lists, p["block"], L, L, p.get("causal", True), rows=rows, keys=keys)
 
 
 def sparse_forward(q, k, v, pattern, scale=None, heads=None, rows=None):

@@ -26,7 +26,7 @@ import torch.nn.functional as F
 from oracle import (ATTNSINK, BLOCKSPARSE, FULL, SLIDING, attention_backward,
                     attention_forward, block_lists, blocksparse_decode_positions,
                     decode_one, decode_positions, dense_token_mask, kv_cache_bytes,
-                    pattern_lists_for_head, pattern_rows_for_head,
+                    pattern_column_for_head, pattern_lists_for_head, pattern_rows_for_head,
                     pattern_token_mask, sliding_token_mask, sparse_backward,
                     sparse_forward, transpose_lists)
 
@@ -131,6 +131,41 @@ def test_row_subset_equals_whole_lists(kind, extra):
         whole = pattern_lists_for_head(pat, 23, h)
         some = pattern_rows_for_head(pat, [0, 5, 17, 22], 23, h)
         assert all(some[i] == whole[i] for i in some)
+
+
+@pytest.mark.parametrize("kind,extra", [(ATTNSINK, dict(sink_blocks=2, local_blocks=3)),
+                                        (BLOCKSPARSE, dict(sink_blocks=1, local_blocks=2, stride=3)),
+                                        (FULL, dict()), (SLIDING, dict(sink_blocks=1, window_tokens=150))])
+def test_single_columns_equal_transposed_rows(kind, extra):
+    """A key block's column built on its own (the same membership rule
+    scanned over query blocks) is that column of the transposed rows."""
+    pat = dict(kind=kind, block=64, causal=True, **extra)
+    for h in (0, 1, 2):
+        cols = transpose_lists(pattern_lists_for_head(pat, 23, h), 23)
+        assert all(pattern_column_for_head(pat, j, 23, h) == cols[j] for j in range(23))
+
+
+@pytest.mark.parametrize("kind,extra", [(BLOCKSPARSE, dict(sink_blocks=1, local_blocks=2, stride=3)),
+                                        (SLIDING, dict(sink_blocks=1, window_tokens=150)),
+                                        (FULL, dict())])
+def test_masks_at_key_subsets(kind, extra):
+    """Masks evaluated at chosen key positions equal those columns of the
+    whole mask (rows as well), with the rows' lists given whole or as a dict
+    of just their query blocks."""
+    pat = dict(kind=kind, block=64, causal=True, **extra)
+    L, h = 64 * 9, 1
+    rng = np.random.default_rng(3)
+    rows = np.sort(rng.choice(L, 40, replace=False))
+    keys = np.concatenate([np.arange(64, 192), rng.choice(L, 50, replace=False)])
+    whole = pattern_token_mask(pat, h, L, rows=rows)
+    assert np.array_equal(pattern_token_mask(pat, h, L, rows=rows, keys=keys), whole[:, keys])
+    some = pattern_rows_for_head(pat, sorted({int(r) // 64 for r in rows}), L // 64, h)
+    assert np.array_equal(pattern_token_mask(pat, h, L, rows=rows, lists=some, keys=keys), whole[:, keys])
+    lists = pattern_lists_for_head(pat, L // 64, h)
+    assert np.array_equal(dense_token_mask(lists, 64, L, L, True, rows=rows, keys=keys),
+                          dense_token_mask(lists, 64, L, L, True, rows=rows)[:, keys])
+    assert np.array_equal(sliding_token_mask(L, L, 64, 100, rows=rows, keys=keys),
+                          sliding_token_mask(L, L, 64, 100, rows=rows)[:, keys])
 
 
 def test_transpose_lists_roundtrip():
