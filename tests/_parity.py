@@ -11,8 +11,8 @@ import numpy as np
 import torch
 
 import long_context_sparse_static_amd as lcs
-from oracle import (attention_backward, attention_forward, pattern_lists_for_head,
-                    pattern_rows_for_head, pattern_token_mask, transpose_lists)
+from oracle import (attention_backward, attention_forward, pattern_column_for_head,
+                    pattern_lists_for_head, pattern_rows_for_head, pattern_token_mask)
 from synth_inputs import as_f64
 
 # bf16 path: max-abs 2e-2 and mean-abs 2e-3; fp32 path: max-abs 1e-5.
@@ -69,7 +69,7 @@ def sample_rows_forward(q, k, v, pattern, head, b, rows, scale=None):
                                   nb, head)
     kblocks = sorted({j for r in rows for j in lists[r // pattern.block]})
     keys = np.concatenate([np.arange(j * pattern.block, (j + 1) * pattern.block) for j in kblocks])
-    mask = pattern_token_mask(oracle_pattern(pattern), head, L, rows=rows, lists=lists)[:, keys]
+    mask = pattern_token_mask(oracle_pattern(pattern), head, L, rows=rows, lists=lists, keys=keys)
     qh = as_f64(q[b, head, torch.as_tensor(rows, device=q.device)])
     kh = as_f64(k[b, head, torch.as_tensor(keys, device=k.device)])
     vh = as_f64(v[b, head, torch.as_tensor(keys, device=v.device)])
@@ -81,22 +81,29 @@ def sample_backward(q, k, v, do, pattern, head, b, qblocks, kblocks, scale=None)
     ``kblocks`` for one (b, head).  A query block's gradients depend only on
     the keys it lists, so each query block is an exact sub-problem; a key
     block's dK/dV is the sum of the sub-problems of the query blocks that
-    list it."""
+    list it (its column).  Only the rows and columns involved are built and
+    only their tokens are copied, so this scales to the longest sequences."""
     L, d = q.shape[2], q.shape[3]
     B_ = pattern.block
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     nb = L // B_
     opat = oracle_pattern(pattern)
-    lists = pattern_lists_for_head(opat, nb, head)
-    cols = transpose_lists(lists, nb)
-    tok = lambda blocks: np.concatenate([np.arange(j * B_, (j + 1) * B_) for j in blocks])
-    qh, kh, vh, doh = (as_f64(t[b, head]) for t in (q, k, v, do))
+    cols = {j: pattern_column_for_head(opat, j, nb, head) for j in kblocks}
+    need = sorted(set(qblocks) | {i for j in kblocks for i in cols[j]})
+    lists = pattern_rows_for_head(opat, need, nb, head)
+    # token copies: the rows of the needed query blocks, the keys of their lists
+    blocks = sorted(set(need) | {j for i in need for j in lists[i]})
+    at = {j: n * B_ for n, j in enumerate(blocks)}
+    tok = lambda bl: np.concatenate([np.arange(j * B_, (j + 1) * B_) for j in bl])
+    idx = torch.as_tensor(tok(blocks), device=q.device)
+    qh, kh, vh, doh = (as_f64(t[b, head].index_select(0, idx)) for t in (q, k, v, do))
+    loc = lambda bl: np.concatenate([np.arange(at[j], at[j] + B_) for j in bl])
     cache = {}
 
     def sub(i):
         if i not in cache:
-            rows, keys = tok([i]), tok(lists[i])
-            mask = pattern_token_mask(opat, head, L, rows=rows, lists=lists)[:, keys]
+            rows, keys = loc([i]), loc(lists[i])
+            mask = pattern_token_mask(opat, head, L, rows=tok([i]), lists=lists, keys=tok(lists[i]))
             cache[i] = attention_backward(qh[rows], kh[keys], vh[keys], doh[rows], mask, scale)[:3]
         return cache[i]
 
@@ -108,9 +115,9 @@ def sample_backward(q, k, v, do, pattern, head, b, qblocks, kblocks, scale=None)
         dv = np.zeros((B_, d))
         for i in cols[j]:
             _, dki, dvi = sub(i)
-            at = lists[i].index(j) * B_
-            dk += dki[at:at + B_]
-            dv += dvi[at:at + B_]
+            o = lists[i].index(j) * B_
+            dk += dki[o:o + B_]
+            dv += dvi[o:o + B_]
             if len(cache) > 256:
                 cache.clear()
         out[("dk", j)] = dk

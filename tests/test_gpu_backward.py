@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import long_context_sparse_static_amd as lcs
-from _parity import assert_bf16_close, need_gpu, oracle_backward_heads, oracle_pattern
+from _parity import assert_bf16_close, need_gpu, oracle_backward_heads, oracle_pattern, sample_backward
 from oracle import sparse_backward
 from synth_inputs import as_f64, randn, seed_for
 
@@ -80,6 +80,32 @@ def test_backward_64k_four_heads_every_block():
         for name, g, w in zip(("dq", "dk", "dv"), (dq, dk, dv), want[h]):
             mx, mean = assert_bf16_close(as_f64(g[0, h]), w, f"{name} head {h}")
             print(name, h, mx, mean)
+
+
+def test_backward_maximum_length_sampled():
+    """Forward + backward at the forward's longest sequence for d = 128
+    (4,161,536 tokens, 65,024 blocks), AttnSink 1 + 64, two heads: every
+    gradient element finite; dQ of query blocks at the start, the end and on
+    either side of bitmap word boundaries, and dK/dV of key blocks whose
+    columns reach the same places, against the oracle's exact sub-problems.
+    (The sink block's dK/dV sums over all 65,024 query blocks; it is checked
+    on whole heads at 64K.)"""
+    need_gpu()
+    pat = lcs.attnsink_pattern(1, 64)
+    L, H = 4161536, 2
+    q, k, v, do = _inputs((1, H, L, 128), 78, big=True)
+    dq, dk, dv = _fwd_bwd(q, k, v, do, pat)
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    qbs = [0, 1, 63, 64, 1023, 1024, 32767, 32768, 65022, 65023]
+    kbs = [1, 63, 64, 32768, 65023]
+    for h in range(H):
+        want = sample_backward(q, k, v, do, pat, h, 0, qbs, kbs)
+        got = {("dq", i): dq[0, h, i * 64:(i + 1) * 64] for i in qbs}
+        got.update({(n, j): g[0, h, j * 64:(j + 1) * 64] for j in kbs for n, g in (("dk", dk), ("dv", dv))})
+        for key, g in got.items():
+            assert_bf16_close(as_f64(g), want[key], f"{key} head {h}")
+        print("max length head", h, "checked", len(got), "blocks")
 
 
 def test_bf16_backward_mixed_heads_full_oracle():
