@@ -28,6 +28,9 @@ Readings taken where the pages are silent (each is listed in the design notes):
     definitions (block 64, sink 1 block, window 4/16/64 blocks, stride 8);
   * the prefill window is block-granular and contains the diagonal block;
     causality masks keys later than the query inside any block;
+  * a sequence of L tokens has ceil(L / block) blocks; when L is not a
+    multiple of the block the last block is partial (its missing tokens do
+    not exist: no query reads them and no row is computed for them);
   * BlockSparse head h takes blocks j < i with (j + h) mod stride == 0;
   * the softmax scale is 1/sqrt(d); LSE is the natural log of the sum of
     exp(scaled scores) over allowed keys; an empty row gives O = 0, LSE = -inf;
@@ -288,7 +291,7 @@ def pattern_token_mask(pattern, head, L, rows=None, lists=None, keys=None):
         return sliding_token_mask(L, L, p["block"] * p.get("sink_blocks", 0),
                                   p["window_tokens"], rows=rows, keys=keys)
     if lists is None:
-        lists = pattern_lists_for_head(pattern, L // p["block"], head)
+        lists = pattern_lists_for_head(pattern, -(-L // p["block"]), head)   # last block may be partial
     return dense_token_mask(lists, p["block"], L, L, p.get("causal", True), rows=rows, keys=keys)
 
 

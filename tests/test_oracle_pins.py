@@ -189,7 +189,7 @@ def rand(*shape):
     return rng.standard_normal(shape)
 
 
-@pytest.mark.parametrize("L,block,d", [(96, 16, 8), (64, 64, 16), (130, 13, 5)])
+@pytest.mark.parametrize("L,block,d", [(96, 16, 8), (64, 64, 16), (130, 13, 5), (100, 16, 8), (37, 64, 4)])
 def test_full_pattern_is_causal_attention(L, block, d):
     q, k, v = rand(L, d), rand(L, d), rand(L, d)
     nb = -(-L // block)
@@ -308,12 +308,14 @@ def test_sliding_prefill_row_equals_decode():
         assert ld == pytest.approx(lse[0, 0, t], abs=1e-12)
 
 
+@pytest.mark.parametrize("short", [0, 3], ids=["whole_blocks", "partial_last_block"])
 @pytest.mark.parametrize("kind,s,w,stride,h", [(ATTNSINK, 1, 4, 0, 0), (ATTNSINK, 2, 3, 0, 0),
                                                (BLOCKSPARSE, 1, 3, 4, 1), (FULL, 0, 0, 0, 0)])
-def test_zero_query_closed_form(kind, s, w, stride, h):
-    """Q = 0: every allowed score is 0, so LSE = ln(count) and O = mean(V)."""
+def test_zero_query_closed_form(kind, s, w, stride, h, short):
+    """Q = 0: every allowed score is 0, so LSE = ln(count) and O = mean(V)
+    (also with the last block 3 tokens short)."""
     block, nb, d = 8, 13, 4
-    L = block * nb
+    L = block * nb - short
     q, k, v = np.zeros((L, d)), rand(L, d), rand(L, d)
     lists = block_lists(kind, nb, sink_blocks=s, local_blocks=w, stride=stride, head=h)
     o, lse = attention_forward(q, k, v, dense_token_mask(lists, block, L, L, True), 0.7)
@@ -330,6 +332,32 @@ def test_zero_query_closed_form(kind, s, w, stride, h):
         if kind == ATTNSINK:
             keys = set(range(0, block * min(s, bi))) | set(range(max(0, bi - w + 1) * block, p + 1))
             np.testing.assert_allclose(o[p], v[sorted(keys)].mean(axis=0), atol=1e-12)
+
+
+@pytest.mark.parametrize("kind,extra", [(ATTNSINK, dict(sink_blocks=1, local_blocks=2)),
+                                        (BLOCKSPARSE, dict(sink_blocks=1, local_blocks=2, stride=3)),
+                                        (FULL, dict()), (SLIDING, dict(sink_blocks=1, window_tokens=100))])
+def test_partial_last_block_is_the_truncated_problem(kind, extra):
+    """L = 64 nb - 27 tokens: the mask is the top-left L x L corner of the
+    mask for 64 nb tokens, and with causality the outputs and gradients of
+    the L rows equal those of the longer sequence restricted to them (its
+    extra tokens come later than every one of the L queries)."""
+    pat = dict(kind=kind, block=64, causal=True, **extra)
+    nb, h, d = 5, 2, 8
+    Lp = 64 * nb
+    L = Lp - 27
+    for hh in (0, h):
+        np.testing.assert_array_equal(pattern_token_mask(pat, hh, L), pattern_token_mask(pat, hh, Lp)[:L, :L])
+    q, k, v, do = (rand(1, 3, Lp, d) for _ in range(4))
+    o_p, lse_p = sparse_forward(q, k, v, pat)
+    o, lse = sparse_forward(q[:, :, :L], k[:, :, :L], v[:, :, :L], pat)
+    np.testing.assert_allclose(o, o_p[:, :, :L], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_p[:, :, :L], rtol=0, atol=1e-12)
+    do[:, :, L:] = 0.0   # the extra queries add nothing to dK, dV of the first L keys
+    g_p = sparse_backward(q, k, v, do, pat)
+    g = sparse_backward(q[:, :, :L], k[:, :, :L], v[:, :, :L], do[:, :, :L], pat)
+    for a_, b_ in zip(g[:3], g_p[:3]):
+        np.testing.assert_allclose(a_, b_[:, :, :L], rtol=0, atol=1e-12)
 
 
 def test_constant_values_give_constant_output():
