@@ -17,7 +17,9 @@
  *  - Tensors are contiguous, row-major [B, H, L, d] (batch, head, token,
  *    head dim).  LSE is float32 [B, H, L]: the natural log of the sum of
  *    exp(scale * q.k) over the keys a query may see.
- *  - A "block" is 64 consecutive tokens.  L must be a multiple of 64.
+ *  - A "block" is 64 consecutive tokens; a sequence of L tokens has
+ *    ceil(L / 64) blocks, the last one partial when L % 64 != 0.  Keys past
+ *    L do not exist; rows past L are never written.
  *  - Device pointers are HIP device (or managed) pointers; `stream` is a
  *    hipStream_t passed as void* (NULL = the default stream).
  *  - Ownership: the caller allocates and frees every buffer (tensors, index,
@@ -46,7 +48,7 @@ extern "C" {
 
 typedef enum {
   ATTN_OK = 0,
-  ATTN_ERR_INVALID_ARG = -1, /* null pointer, bad size, L % 64 != 0, ...      */
+  ATTN_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad stride, ...        */
   ATTN_ERR_UNSUPPORTED = -2, /* valid request the library does not implement */
   ATTN_ERR_BAD_INDEX = -3,   /* malformed block index (host validation)      */
   ATTN_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required   */
@@ -145,7 +147,7 @@ const char *attn_status_str(attn_status_t status);
  * ------------------------------------------------------------------------- */
 
 /* Total entries of the index of `pattern` for n_heads index heads and L
- * tokens (L % block == 0), written to *nnz_out.  The index is the static
+ * tokens (ceil(L / block) query and key blocks), written to *nnz_out.  The index is the static
  * block list of the sparse layers' fixed patterns -- sink, window and
  * strided blocks (mlsanity index page "A Little Goes a Long Way...",
  * "Abstract (arXiv)"), accessed block-wise and fixed ahead of time
@@ -215,10 +217,11 @@ size_t attn_workspace_bytes(int32_t op, attn_dtype_t dtype, int32_t B,
  * For every (b, h) and query token i: O[i] = softmax(scale * q_i K_S^T) V_S
  * over the allowed key set S of i, LSE[i] = log sum exp(scale * q_i K_S^T).
  *   dtype: ATTN_BF16 (q/k/v/o bf16, fp32 accumulation) or ATTN_F32 (all
- *          fp32).  d in {64, 128}.  pattern->block == 64; B, H >= 1 and
- *          L >= 64 with L % 64 == 0 (an empty batch or sequence is
- *          ATTN_ERR_INVALID_ARG).
- *   dev_index: device CSR for L/64 query and key blocks (CSC unused).
+ *          fp32).  d in {64, 128}.  pattern->block == 64; B, H, L >= 1
+ *          (an empty batch or sequence is ATTN_ERR_INVALID_ARG).  A partial
+ *          last block (L % 64 != 0) needs a causal pattern (ATTN_ERR_UNSUPPORTED
+ *          otherwise): causality is what keeps every query off the keys past L.
+ *   dev_index: device CSR for ceil(L/64) query and key blocks (CSC unused).
  *   pattern: its causal flag applies to every head; for kind ATTN_SLIDING
  *   its token window (sink_blocks, window_tokens) also masks keys inside
  *   the listed blocks of every head.  Sliding with causal == 0 is

@@ -255,7 +255,7 @@ class HostIndex:
 def attn_index_build(pattern: Pattern, n_heads: int, L: int, with_csc: bool = True) -> HostIndex:
     """Builds the CSR (and CSC) of ``pattern`` on the host (C++ builder)."""
     nnz = attn_index_nnz(pattern, n_heads, L)
-    nb = L // pattern.block
+    nb = -(-L // pattern.block)   # the last block may be partial
     row_ptr = np.zeros(n_heads * (nb + 1), dtype=np.int32)
     col_idx = np.zeros(max(nnz, 1), dtype=np.int32)[:nnz]
     col_ptr = np.zeros(n_heads * (nb + 1), dtype=np.int32) if with_csc else None
@@ -329,7 +329,7 @@ def attn_index_build_mixed(patterns, L: int, with_csc: bool = True) -> HostIndex
     """CSR (and CSC) of a per-head mix of patterns, built on the host."""
     H = len(patterns)
     nnz = attn_index_nnz_mixed(patterns, L)
-    nb = L // patterns[0].block
+    nb = -(-L // patterns[0].block)
     row_ptr = np.zeros(H * (nb + 1), dtype=np.int32)
     col_idx = np.zeros(max(nnz, 1), dtype=np.int32)[:nnz]
     col_ptr = np.zeros(H * (nb + 1), dtype=np.int32) if with_csc else None

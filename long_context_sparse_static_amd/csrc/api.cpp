@@ -14,7 +14,8 @@ using attn::IndexView;
 bool index_shape_ok(const attn_index_t *ix, int32_t H, int64_t L, bool need_csc) {
   if (!ix || !ix->row_ptr || !ix->col_idx) return false;
   if (ix->n_heads != 1 && ix->n_heads != H) return false;
-  if (ix->n_qblocks != L / attn::kBlock || ix->n_kblocks != L / attn::kBlock) return false;
+  const int64_t nb = (L + attn::kBlock - 1) / attn::kBlock;   // the last block may be partial
+  if (ix->n_qblocks != nb || ix->n_kblocks != nb) return false;
   if (ix->nnz < 0 || ix->nnz > INT32_MAX) return false;
   if (need_csc && (!ix->col_ptr || !ix->row_idx)) return false;
   return true;
@@ -35,13 +36,14 @@ IndexView view_of(const attn_index_t *ix) {
 
 bool prefill_dims_ok(int32_t B, int32_t H, int64_t L, int32_t d, float scale,
                      const attn_pattern_t *p) {
-  if (B < 1 || H < 1 || L < attn::kBlock || L % attn::kBlock != 0) return false;
+  if (B < 1 || H < 1 || L < 1) return false;
   if (!p || p->block != attn::kBlock) return false;
   if (p->kind == ATTN_SLIDING && (p->window_tokens < 1 || p->sink_blocks < 0 || !p->causal))
     return false;
   if (!(scale > 0.f) || !isfinite(scale)) return false;
-  // int32 token / tile arithmetic inside the kernels
-  if ((int64_t)B * H * L > INT32_MAX) return false;
+  // int32 token / tile arithmetic inside the kernels (over whole blocks)
+  const int64_t Lb = (L + attn::kBlock - 1) / attn::kBlock * attn::kBlock;
+  if ((int64_t)B * H * Lb > INT32_MAX) return false;
   (void)d;
   return true;
 }
@@ -121,6 +123,7 @@ attn_status_t fwd_impl(attn_dtype_t dtype, int32_t B, int32_t H, int64_t L, int3
     return ATTN_ERR_INVALID_ARG;
   if (!index_shape_ok(dev_index, H, L, false)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (L % attn::kBlock != 0 && !pattern->causal) return ATTN_ERR_UNSUPPORTED;  // keys past L unmasked
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (dtype == ATTN_BF16 && attn::fwd_bf16_lds_bytes(d, dev_index->n_kblocks) > attn::kMaxLdsPerWorkgroup)
     return ATTN_ERR_UNSUPPORTED;  // union bitmap of more than ~65K key blocks (~4M tokens)
@@ -163,6 +166,7 @@ attn_status_t bwd_impl(attn_dtype_t dtype, int32_t B, int32_t H, int64_t L, int3
     return ATTN_ERR_INVALID_ARG;
   if (!index_shape_ok(dev_index, H, L, true)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (L % attn::kBlock != 0 && !pattern->causal) return ATTN_ERR_UNSUPPORTED;  // keys past L unmasked
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (attn::bwd_bf16_lds_bytes(d, dev_index->n_qblocks) > attn::kMaxLdsPerWorkgroup)
     return ATTN_ERR_UNSUPPORTED;

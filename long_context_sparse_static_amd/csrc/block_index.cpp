@@ -25,9 +25,13 @@
 
 namespace {
 
+// Blocks of a sequence of L tokens: the last one may hold fewer than
+// `block` tokens.
+int64_t n_blocks(int64_t L, int32_t block) { return (L + block - 1) / block; }
+
 bool pattern_ok(const attn_pattern_t *p, int64_t L) {
-  if (!p || p->block <= 0 || L <= 0 || L % p->block != 0) return false;
-  if (L / p->block > INT32_MAX - 1) return false;
+  if (!p || p->block <= 0 || L <= 0) return false;
+  if (n_blocks(L, p->block) > INT32_MAX - 1) return false;
   if (p->kind == ATTN_FULL) return true;
   if (p->kind == ATTN_SLIDING) return p->sink_blocks >= 0 && p->window_tokens >= 1 && p->causal;
   if (p->kind != ATTN_ATTNSINK && p->kind != ATTN_BLOCKSPARSE) return false;
@@ -151,7 +155,7 @@ extern "C" {
 attn_status_t attn_index_nnz(const attn_pattern_t *p, int32_t n_heads, int64_t L,
                              int64_t *nnz_out) {
   if (!nnz_out || n_heads < 1 || !pattern_ok(p, L)) return ATTN_ERR_INVALID_ARG;
-  return count_nnz([p](int32_t) { return p; }, n_heads, L / p->block,
+  return count_nnz([p](int32_t) { return p; }, n_heads, n_blocks(L, p->block),
                    p->kind != ATTN_BLOCKSPARSE, nnz_out);
 }
 
@@ -163,7 +167,7 @@ attn_status_t attn_index_build(const attn_pattern_t *p, int32_t n_heads, int64_t
   if (st != ATTN_OK) return st;
   if (!row_ptr || !col_idx) return ATTN_ERR_INVALID_ARG;
   if ((col_ptr == nullptr) != (row_idx == nullptr)) return ATTN_ERR_INVALID_ARG;
-  build_lists([p](int32_t) { return p; }, n_heads, L / p->block, row_ptr, col_idx, col_ptr,
+  build_lists([p](int32_t) { return p; }, n_heads, n_blocks(L, p->block), row_ptr, col_idx, col_ptr,
               row_idx);
   return ATTN_OK;
 }
@@ -172,7 +176,7 @@ attn_status_t attn_index_nnz_mixed(const attn_pattern_t *patterns, int32_t n_hea
                                    int64_t *nnz_out) {
   if (!nnz_out || !mixed_ok(patterns, n_heads, L)) return ATTN_ERR_INVALID_ARG;
   return count_nnz([patterns](int32_t h) { return &patterns[h]; }, n_heads,
-                   L / patterns[0].block, false, nnz_out);
+                   n_blocks(L, patterns[0].block), false, nnz_out);
 }
 
 attn_status_t attn_index_build_mixed(const attn_pattern_t *patterns, int32_t n_heads, int64_t L,
@@ -183,7 +187,7 @@ attn_status_t attn_index_build_mixed(const attn_pattern_t *patterns, int32_t n_h
   if (st != ATTN_OK) return st;
   if (!row_ptr || !col_idx) return ATTN_ERR_INVALID_ARG;
   if ((col_ptr == nullptr) != (row_idx == nullptr)) return ATTN_ERR_INVALID_ARG;
-  build_lists([patterns](int32_t h) { return &patterns[h]; }, n_heads, L / patterns[0].block,
+  build_lists([patterns](int32_t h) { return &patterns[h]; }, n_heads, n_blocks(L, patterns[0].block),
               row_ptr, col_idx, col_ptr, row_idx);
   return ATTN_OK;
 }

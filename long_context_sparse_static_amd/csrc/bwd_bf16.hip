@@ -147,7 +147,9 @@ struct BwdPos {
 //   S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - D), dQ^T += K^T dS^T
 // K is read as rows and transposed (kBothRead), V as rows.
 // ----------------------------------------------------------------------------
-template <int D, bool WIN, bool DENSE>
+// RAG: L is not a multiple of 64 (the last block is partial); the range
+// checks compile away otherwise.
+template <int D, bool WIN, bool DENSE, bool RAG>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   using KT = SwzTile<D, kBothRead>;
   using VT = SwzTile<D, kRowRead>;
@@ -183,15 +185,17 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const bf16 *qp = (const bf16 *)a.q + (DENSE ? dense_base : a.qs.at(bb, head)) + (size_t)q_tok * lq;
   const bf16 *dop = (const bf16 *)a.dout + (DENSE ? dense_base : a.dos.at(bb, head)) + (size_t)q_tok * ldo;
 
+  // rows past L of a partial last block: zero operands, P = 0 (LSE2 = +inf)
+  const bool q_in = q_valid && (!RAG || q_tok < a.L);
   bf16x8 bq[KS], bdo[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    bq[ks] = q_valid ? *(const bf16x8 *)(qp + ks * 16 + hh * 8) : bf16x8{};
-    bdo[ks] = q_valid ? *(const bf16x8 *)(dop + ks * 16 + hh * 8) : bf16x8{};
+    bq[ks] = q_in ? *(const bf16x8 *)(qp + ks * 16 + hh * 8) : bf16x8{};
+    bdo[ks] = q_in ? *(const bf16x8 *)(dop + ks * 16 + hh * 8) : bf16x8{};
   }
   const float c = a.scale * kLog2e;
   float lse2 = INFINITY, dlt = 0.f;
-  if (q_valid) {
+  if (q_in) {
     lse2 = a.lse2[(size_t)bh * a.L + q_tok];
     dlt = -a.delta[(size_t)bh * a.L + q_tok];
   }
@@ -269,8 +273,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   BwdPos cur = advance(), nxt{false, 0, 0u};
   if (cur.valid) {
     nxt = advance();
-    kl.load(kg + (size_t)cur.j * kBlock * lk, k0);
-    vl.load(vg + (size_t)cur.j * kBlock * lv, v0);
+    kl.load(kg + (size_t)cur.j * kBlock * lk, RAG ? a.L - cur.j * kBlock : kBlock, lk, k0);
+    vl.load(vg + (size_t)cur.j * kBlock * lv, RAG ? a.L - cur.j * kBlock : kBlock, lv, v0);
   }
   // Block of walk step t lives in slot t & 1; the next block's tiles load into
   // the other slot while this one is computed.
@@ -280,8 +284,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (nxt.valid) {
-      kl.load(kg + (size_t)nxt.j * kBlock * lk, P ? k0 : k1);
-      vl.load(vg + (size_t)nxt.j * kBlock * lv, P ? v0 : v1);
+      kl.load(kg + (size_t)nxt.j * kBlock * lk, RAG ? a.L - nxt.j * kBlock : kBlock, lk, P ? k0 : k1);
+      vl.load(vg + (size_t)nxt.j * kBlock * lv, RAG ? a.L - nxt.j * kBlock : kBlock, lv, P ? v0 : v1);
     }
     if (listed(cur)) block_work(P ? k1 : k0, P ? v1 : v0, cur.j);
     cur = nxt;
@@ -297,9 +301,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   // they stage the output rows, waves 0-1 in k0, 2-3 in k1
   __syncthreads();
   if (!q_valid) return;
-  store_rows_staged<D>(acc, a.scale, (wave < 2 ? k0 : k1) + (wave & 1) * 32 * 2 * D,
+  store_rows_staged<D, RAG>(acc, a.scale, (wave < 2 ? k0 : k1) + (wave & 1) * 32 * 2 * D,
                        (bf16 *)a.dq + (DENSE ? dense_base : a.dqs.at(bb, head)) + (size_t)q_wave * ldq, ldq,
-                       lane);
+                       lane, a.L - q_wave);
 }
 
 // ----------------------------------------------------------------------------
@@ -325,7 +329,7 @@ constexpr int kDkvThreads = kDkvWaves * 64;
 constexpr int kDkvPairs = kDkvWaves / 2;
 constexpr int kDkvTB = kDkvPairs / 2;   // key blocks per workgroup (two pairs per block)
 
-template <int D, bool WIN, bool DENSE>
+template <int D, bool WIN, bool DENSE, bool RAG>
 __global__ __launch_bounds__(kDkvThreads, 8 / kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   using QT = SwzTile<D, kBothRead>;
   constexpr int KS = D / 16, MT = D / 32;
@@ -402,8 +406,8 @@ __global__ __launch_bounds__(kDkvThreads, 8 / kDkvWaves) void bwd_dkdv_kernel(Bw
     const bf16 *vp = (const bf16 *)a.v + (DENSE ? dense_base : a.vs.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.vs.l);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      bk[ks] = k_valid ? *(const bf16x8 *)(kp + ks * 16 + hh * 8) : bf16x8{};
-      bv[ks] = k_valid ? *(const bf16x8 *)(vp + ks * 16 + hh * 8) : bf16x8{};
+      bk[ks] = k_valid && (!RAG || k_tok < a.L) ? *(const bf16x8 *)(kp + ks * 16 + hh * 8) : bf16x8{};
+      bv[ks] = k_valid && (!RAG || k_tok < a.L) ? *(const bf16x8 *)(vp + ks * 16 + hh * 8) : bf16x8{};
     }
   }
   const float c = a.scale * kLog2e;
@@ -418,15 +422,18 @@ __global__ __launch_bounds__(kDkvThreads, 8 / kDkvWaves) void bwd_dkdv_kernel(Bw
   ldo.init(wave, lane, ldo_l);
   // the two 64-float per-token vectors of a query block: wave 0 loads LSE2,
   // wave 1 the -D values (4 bytes per lane)
+  // (a partial last block's rows past L load as zeros: zero Q and dO rows,
+  // LSE2 = 0 and -D = 0, so they add nothing to dK or dV)
   auto load_vec = [&](int i, float *lv, float *ev) __attribute__((always_inline)) {
+    const int bytes = RAG ? 4 * min(kBlock, a.L - i * kBlock) : -1;
     if (wave == 0)
-      load_lds<4>(buffer_rsrc(lseg + (size_t)i * kBlock), 4 * lane, lv);
+      load_lds<4>(buffer_rsrc_n(lseg + (size_t)i * kBlock, bytes), 4 * lane, lv);
     else if (wave == 1)
-      load_lds<4>(buffer_rsrc(ndltg + (size_t)i * kBlock), 4 * lane, ev);
+      load_lds<4>(buffer_rsrc_n(ndltg + (size_t)i * kBlock, bytes), 4 * lane, ev);
   };
   auto load_block = [&](int i, char *qt, char *ot, float *lv, float *ev) __attribute__((always_inline)) {
-    ldq.load(qg + (size_t)i * kBlock * lq, qt);
-    ldo.load(dog + (size_t)i * kBlock * ldo_l, ot);
+    ldq.load(qg + (size_t)i * kBlock * lq, RAG ? a.L - i * kBlock : kBlock, lq, qt);
+    ldo.load(dog + (size_t)i * kBlock * ldo_l, RAG ? a.L - i * kBlock : kBlock, ldo_l, ot);
     load_vec(i, lv, ev);
   };
 
@@ -605,11 +612,11 @@ __global__ __launch_bounds__(kDkvThreads, 8 / kDkvWaves) void bwd_dkdv_kernel(Bw
   const int ld_out = side0 ? (DENSE ? D : a.dvs.l) : (DENSE ? D : a.dks.l);
   bf16 *out = side0 ? (bf16 *)a.dv + (DENSE ? dense_base : a.dvs.at(bb, head)) + (size_t)k_wave * ld_out
                     : (bf16 *)a.dk + (DENSE ? dense_base : a.dks.at(bb, head)) + (size_t)k_wave * ld_out;
-  store_rows_staged<D>(acc, side0 ? 1.0f : a.scale, (wave < 2 ? q0 : q1) + (wave & 1) * 32 * 2 * D, out,
-                       ld_out, lane);
+  store_rows_staged<D, RAG>(acc, side0 ? 1.0f : a.scale, (wave < 2 ? q0 : q1) + (wave & 1) * 32 * 2 * D, out,
+                       ld_out, lane, a.L - k_wave);
 }
 
-template <int D, bool WIN, bool DENSE>
+template <int D, bool WIN, bool DENSE, bool RAG>
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const size_t rows = (size_t)a.B * a.H * a.L;
   const int rpb = 256 / (D / 8);
@@ -619,15 +626,15 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const int BH = a.B * a.H;
   const size_t dyn_k = RowsBitmap<kDkvTB>::lds_bytes(a.ix.n_qblocks);
   const size_t dyn_q = RowsBitmap<kBwdTB>::lds_bytes(a.ix.n_kblocks);
-  hipError_t e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel<D, WIN, DENSE>,
+  hipError_t e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel<D, WIN, DENSE, RAG>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_k);
   if (e == hipSuccess)
-    e = hipFuncSetAttribute((const void *)bwd_dq_kernel<D, WIN, DENSE>,
+    e = hipFuncSetAttribute((const void *)bwd_dq_kernel<D, WIN, DENSE, RAG>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_q);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3(grid_delta), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, WIN, DENSE>), dim3(BH * k_tiles), dim3(kDkvThreads), dyn_k, s, a);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, WIN, DENSE>), dim3(BH * q_tiles), dim3(kBwdThreads), dyn_q, s, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, WIN, DENSE, RAG>), dim3(BH * k_tiles), dim3(kDkvThreads), dyn_k, s, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, WIN, DENSE, RAG>), dim3(BH * q_tiles), dim3(kBwdThreads), dyn_q, s, a);
   return hipGetLastError();
 }
 
@@ -640,17 +647,23 @@ size_t bwd_bf16_lds_bytes(int d, int n_blocks) {
   return tiles + RowsBitmap<kDkvTB>::lds_bytes(n_blocks);
 }
 
+template <bool RAG>
+static hipError_t launch_bwd_rag(const BwdArgs &a, bool dense, hipStream_t s) {
+  if (a.window > 0) {
+    if (dense) return a.d == 128 ? launch_bwd<128, true, true, RAG>(a, s) : launch_bwd<64, true, true, RAG>(a, s);
+    return a.d == 128 ? launch_bwd<128, true, false, RAG>(a, s) : launch_bwd<64, true, false, RAG>(a, s);
+  }
+  if (dense) return a.d == 128 ? launch_bwd<128, false, true, RAG>(a, s) : launch_bwd<64, false, true, RAG>(a, s);
+  return a.d == 128 ? launch_bwd<128, false, false, RAG>(a, s) : launch_bwd<64, false, false, RAG>(a, s);
+}
+
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s) {
   const bool dense = dense_layout(a.qs, a.H, a.L, a.d) && dense_layout(a.ks, a.H, a.L, a.d) &&
                      dense_layout(a.vs, a.H, a.L, a.d) && dense_layout(a.os, a.H, a.L, a.d) &&
                      dense_layout(a.dos, a.H, a.L, a.d) && dense_layout(a.dqs, a.H, a.L, a.d) &&
                      dense_layout(a.dks, a.H, a.L, a.d) && dense_layout(a.dvs, a.H, a.L, a.d);
-  if (a.window > 0) {
-    if (dense) return a.d == 128 ? launch_bwd<128, true, true>(a, s) : launch_bwd<64, true, true>(a, s);
-    return a.d == 128 ? launch_bwd<128, true, false>(a, s) : launch_bwd<64, true, false>(a, s);
-  }
-  if (dense) return a.d == 128 ? launch_bwd<128, false, true>(a, s) : launch_bwd<64, false, true>(a, s);
-  return a.d == 128 ? launch_bwd<128, false, false>(a, s) : launch_bwd<64, false, false>(a, s);
+  if (a.L % kBlock != 0) return launch_bwd_rag<true>(a, dense, s);
+  return launch_bwd_rag<false>(a, dense, s);
 }
 
 }  // namespace attn

@@ -73,6 +73,11 @@ __device__ __forceinline__ float xor32_max(float x) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, 0x00020000);
 }
+// The same descriptor limited to `bytes`: loads at offsets >= bytes return
+// zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc_n(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
 template <int BYTES>
 __device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t rs, int byte_off, void *lds) {
   static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte lanes");

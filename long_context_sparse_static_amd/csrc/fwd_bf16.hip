@@ -91,7 +91,9 @@ struct WalkPos {
   uint32_t mask;  // bit r: listed by query block r of the workgroup
 };
 
-template <int D, bool WIN, bool DENSE>
+// RAG: L is not a multiple of 64 (the last block is partial); the range
+// checks compile away otherwise.
+template <int D, bool WIN, bool DENSE, bool RAG>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   using Lay = FwdLayout<D>;
   constexpr int KS = D / 16;   // k-steps of S^T = K Q^T
@@ -158,7 +160,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   bf16x8 bq[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    bq[ks] = q_valid ? *(const bf16x8 *)(qg + (size_t)q_tok * lq + ks * 16 + hh * 8) : bf16x8{};
+    bq[ks] = q_valid && (!RAG || q_tok < a.L) ? *(const bf16x8 *)(qg + (size_t)q_tok * lq + ks * 16 + hh * 8)
+                                               : bf16x8{};
 
   // Per-lane global element offsets of this wave's share of a tile load
   // (group B waves load; a wave's share is 16 token rows).
@@ -171,8 +174,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     goff_k[i] = 2 * (r * lk + ((pc ^ Lay::kswz(r)) << 3));   // bytes
     goff_v[i] = 2 * (r * lv + ((pc ^ Lay::vswz(r)) << 3));
   }
-  auto load_tile = [&](const bf16 *g, char *lds, const int (&goff)[Lay::LPW]) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g);
+  // tile of key block j of g (rows ld elements apart); the rows of a partial
+  // last block past L load as zeros
+  auto load_tile = [&](const bf16 *g, int j, int ld, char *lds, const int (&goff)[Lay::LPW])
+                       __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rs =
+        tile_rsrc(g + (size_t)j * kBlock * ld, RAG ? a.L - j * kBlock : kBlock, 2 * ld, RB);
 #pragma unroll
     for (int i = 0; i < Lay::LPW; ++i)
       load_lds<16>(rs, goff[i], lds + (lw * (kBlock / kLoadWaves) + i * Lay::RPI) * RB);
@@ -374,7 +381,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   WalkPos prev{false, 0, 0u}, cur = advance(), nxt{false, 0, 0u};
   if (cur.valid) {
     nxt = advance();
-    if (grp == 1) load_tile(kg + (size_t)cur.j * kBlock * lk, k0, goff_k);
+    if (grp == 1) load_tile(kg, cur.j, lk, k0, goff_k);
   }
   // Phases 2t and 2t+1 for t = 0 .. n (n = walk length): group A runs the
   // matrix-core step of walk block t in phase 2t and its vector step in
@@ -402,8 +409,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   // the matrix-core waves never queue behind the address unit).
   auto issue_loads = [&](auto PAR) __attribute__((always_inline)) {
     constexpr int P = decltype(PAR)::value;
-    if (nxt.valid) load_tile(kg + (size_t)nxt.j * kBlock * lk, P ? k0 : k1, goff_k);
-    if (cur.valid) load_tile(vg + (size_t)cur.j * kBlock * lv, P ? v1 : v0, goff_v);
+    if (nxt.valid) load_tile(kg, nxt.j, lk, P ? k0 : k1, goff_k);
+    if (cur.valid) load_tile(vg, cur.j, lv, P ? v1 : v0, goff_v);
   };
   auto matrix_phase = [&](auto PAR) __attribute__((always_inline)) {
     constexpr int P = decltype(PAR)::value;
@@ -454,24 +461,24 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   const float l_tot = lacc[0];   // sum of P' of the row (bf16-rounded, as in P V)
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   // O leaves through the wave's own LDS area as contiguous row runs
-  store_rows_staged<D>(oacc, inv, (char *)dyn_lds + fwd_ostage_offset(a.ix.n_kblocks) + wave * 32 * RB,
+  store_rows_staged<D, RAG>(oacc, inv, (char *)dyn_lds + fwd_ostage_offset(a.ix.n_kblocks) + wave * 32 * RB,
                        (bf16 *)a.o + (DENSE ? dense_base : a.os.at(bb, head)) + (size_t)q_wave * lo_, lo_,
-                       lane);
-  if (hh == 0)
+                       lane, a.L - q_wave);
+  if (hh == 0 && (!RAG || q_tok < a.L))
     // 2^63 l' = l exactly (a power-of-two scale): log2 of it, not of l', so
     // the LSE keeps full precision
     a.lse[(size_t)bh * a.L + q_tok] = l_tot > 0.f ? (m_run + fast_log2(l_tot * 0x1p63f)) * kLn2 : -INFINITY;
 }
 
-template <int D, bool WIN, bool DENSE>
+template <int D, bool WIN, bool DENSE, bool RAG>
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
   const int n_tiles = (a.ix.n_qblocks + kFwdQB - 1) / kFwdQB;
   const int grid = a.B * a.H * n_tiles;
   const size_t dyn = fwd_ostage_offset(a.ix.n_kblocks) + (size_t)kFwdWaves * 32 * FwdLayout<D>::RB;
-  hipError_t e = hipFuncSetAttribute((const void *)fwd_bf16_kernel<D, WIN, DENSE>,
+  hipError_t e = hipFuncSetAttribute((const void *)fwd_bf16_kernel<D, WIN, DENSE, RAG>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, WIN, DENSE>), dim3(grid), dim3(kFwdThreads), dyn, s, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, WIN, DENSE, RAG>), dim3(grid), dim3(kFwdThreads), dyn, s, a);
   return hipGetLastError();
 }
 
@@ -479,8 +486,8 @@ template <int D, bool WIN>
 hipError_t launch_fwd_layout(const FwdArgs &a, hipStream_t s) {
   return dense_layout(a.qs, a.H, a.L, D) && dense_layout(a.ks, a.H, a.L, D) &&
                  dense_layout(a.vs, a.H, a.L, D) && dense_layout(a.os, a.H, a.L, D)
-             ? launch_fwd<D, WIN, true>(a, s)
-             : launch_fwd<D, WIN, false>(a, s);
+             ? (a.L % kBlock ? launch_fwd<D, WIN, true, true>(a, s) : launch_fwd<D, WIN, true, false>(a, s))
+             : (a.L % kBlock ? launch_fwd<D, WIN, false, true>(a, s) : launch_fwd<D, WIN, false, false>(a, s));
 }
 
 }  // namespace

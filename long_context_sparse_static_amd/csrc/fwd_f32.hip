@@ -35,9 +35,10 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
   const int qi = t >> 2, part = t & 3;
   const int q_tok = qb * kBlock + qi;
   float qv[DP], ov[DP];
+  const bool q_in = q_tok < a.L;   // rows past L of a partial last block: computed, not stored
 #pragma unroll
   for (int i = 0; i < DP; ++i) {
-    qv[i] = qg[(size_t)q_tok * a.qs.l + part * DP + i];
+    qv[i] = q_in ? qg[(size_t)q_tok * a.qs.l + part * DP + i] : 0.f;
     ov[i] = 0.f;
   }
   float m_run = -INFINITY, l_run = 0.f;
@@ -51,8 +52,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
     __syncthreads();
     for (int i = t; i < kBlock * D / 4; i += blockDim.x) {
       const size_t row = (size_t)j * kBlock + i / (D / 4), c4 = 4 * (i % (D / 4));
-      ((f32x4 *)klds)[i] = *(const f32x4 *)(kg + row * a.ks.l + c4);
-      ((f32x4 *)vlds)[i] = *(const f32x4 *)(vg + row * a.vs.l + c4);
+      const bool in = row < (size_t)a.L;   // keys past L: zeros (later than every query, so masked)
+      ((f32x4 *)klds)[i] = in ? *(const f32x4 *)(kg + row * a.ks.l + c4) : f32x4{};
+      ((f32x4 *)vlds)[i] = in ? *(const f32x4 *)(vg + row * a.vs.l + c4) : f32x4{};
     }
     __syncthreads();
     float s[kBlock];
@@ -85,6 +87,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
       for (int i = 0; i < DP; ++i) ov[i] = __builtin_fmaf(p, vlds[kk * D + part * DP + i], ov[i]);
     }
   }
+  if (!q_in) return;
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
 #pragma unroll
   for (int i = 0; i < DP; ++i) og[(size_t)q_tok * a.os.l + part * DP + i] = ov[i] * inv;

@@ -27,6 +27,14 @@ namespace attn {
 // reads).
 enum SwzKind { kRowRead = 0, kTrRead = 1, kBothRead = 2 };
 
+// Descriptor for the 64-row tile at g (rows ld_bytes apart, row_bytes used
+// per row) of a sequence with rows_left rows from the tile's first row: a
+// partial last block's rows past the end load as zeros and are never read.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *g, int rows_left, int ld_bytes,
+                                                            int row_bytes) {
+  return buffer_rsrc_n(g, rows_left >= kBlock ? -1 : (rows_left - 1) * ld_bytes + row_bytes);
+}
+
 template <int D, int KIND>
 struct SwzTile {
   static constexpr int RB = 2 * D;          // bytes per token row
@@ -56,8 +64,10 @@ struct SwzTile {
         goff[i] = 2 * (r * row_stride + (((lane % CPR) ^ swz(r)) << 3));
       }
     }
-    __device__ __forceinline__ void load(const bf16 *g, char *lds) const {
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g);
+    // the tile at g of a sequence with rows_left rows from g on, row stride
+    // ld elements (rows past the end load as zeros)
+    __device__ __forceinline__ void load(const bf16 *g, int rows_left, int ld, char *lds) const {
+      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(g, rows_left, 2 * ld, RB);
 #pragma unroll
       for (int i = 0; i < LPW; ++i) load_lds<16>(rs, goff[i], lds + (lds_row0 + i * RPI) * RB);
     }
@@ -101,10 +111,11 @@ struct SwzTile {
 // written in that layout with the 16-byte chunks of a row XOR-swizzled by
 // the row (the writes spread over the banks), read back as whole chunks of
 // consecutive rows and stored as contiguous 1 KB runs -- not as 8-byte
-// pieces of 32 different rows per store instruction.
-template <int D>
+// pieces of 32 different rows per store instruction.  With LIMIT, rows
+// n_rows .. 31 (past the end of a partial last block) are not stored.
+template <int D, bool LIMIT = false>
 __device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[D / 32], float sc, char *st,
-                                                  bf16 *out, int ld, int lane) {
+                                                  bf16 *out, int ld, int lane, int n_rows = 32) {
   constexpr int RB = 2 * D, CPR = RB / 16, RPS = 1024 / RB;
   const int n = lane & 31, hh = lane >> 5;
 #pragma unroll
@@ -121,7 +132,7 @@ __device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[D / 32], f
   for (int i = 0; i < 32 / RPS; ++i) {
     const int r = i * RPS + lane / CPR, ch = lane % CPR;
     const u32x4 v = *(const u32x4 *)(st + r * RB + ((ch ^ (r & (CPR - 1))) << 4));
-    *(u32x4 *)(out + (size_t)r * ld + ch * 8) = v;
+    if (!LIMIT || r < n_rows) *(u32x4 *)(out + (size_t)r * ld + ch * 8) = v;
   }
 }
 

@@ -59,7 +59,7 @@ def forward_chunk(task):
     task: (pattern dict, head, L, scale, qblocks, q rows [n_q*64, d] of those
     blocks, key_blocks (sorted), k, v rows [n_k*64, d] of those blocks)."""
     pattern, head, L, scale, qblocks, q, key_blocks, k, v = task
-    lists = _lists(pattern, head, L // BLOCK)
+    lists = _lists(pattern, head, -(-L // BLOCK))
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     o = np.zeros((len(qblocks) * BLOCK, q.shape[1]))
     lse = np.zeros(len(qblocks) * BLOCK)
@@ -79,7 +79,7 @@ def backward_chunk(task):
     task: (pattern dict, head, L, scale, qblocks, q, do rows of those blocks,
     key_blocks (sorted), k, v rows of those blocks)."""
     pattern, head, L, scale, qblocks, q, do, key_blocks, k, v = task
-    lists = _lists(pattern, head, L // BLOCK)
+    lists = _lists(pattern, head, -(-L // BLOCK))
     q, do, k, v = (np.asarray(x, dtype=np.float64) for x in (q, do, k, v))
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)

@@ -62,7 +62,7 @@ def sample_rows_forward(q, k, v, pattern, head, b, rows, scale=None):
     sub-problem of the keys those rows may see."""
     L, d = q.shape[2], q.shape[3]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    nb = L // pattern.block
+    nb = -(-L // pattern.block)
     rows = np.asarray(sorted(rows))
     # only the sampled query blocks' rows ({block: list})
     lists = pattern_rows_for_head(oracle_pattern(pattern), sorted({int(r) // pattern.block for r in rows}),
@@ -86,7 +86,7 @@ def sample_backward(q, k, v, do, pattern, head, b, qblocks, kblocks, scale=None)
     L, d = q.shape[2], q.shape[3]
     B_ = pattern.block
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    nb = L // B_
+    nb = -(-L // B_)
     opat = oracle_pattern(pattern)
     cols = {j: pattern_column_for_head(opat, j, nb, head) for j in kblocks}
     need = sorted(set(qblocks) | {i for j in kblocks for i in cols[j]})
@@ -171,7 +171,7 @@ def oracle_forward_heads(q, k, v, pattern, heads, b=0, scale=None, chunk=32):
     import _oracle_pool as pool
     L, d = q.shape[2], q.shape[3]
     scale = pool.default_scale(d) if scale is None else scale
-    nb = L // pattern.block
+    nb = -(-L // pattern.block)
     opat = oracle_pattern(pattern)
     out = {h: (np.full((L, d), np.nan), np.full(L, np.nan)) for h in heads}
 
@@ -202,7 +202,7 @@ def oracle_backward_heads(q, k, v, do, pattern, heads, b=0, scale=None, chunk=32
     import _oracle_pool as pool
     L, d = q.shape[2], q.shape[3]
     scale = pool.default_scale(d) if scale is None else scale
-    nb = L // pattern.block
+    nb = -(-L // pattern.block)
     opat = oracle_pattern(pattern)
     out = {h: (np.full((L, d), np.nan), np.zeros((L, d)), np.zeros((L, d))) for h in heads}
 

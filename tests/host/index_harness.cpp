@@ -121,7 +121,12 @@ int main() {
   bad = pat(ATTN_SLIDING, 1, 0, 0, 0);
   CHECK(attn_index_nnz(&bad, 1, 640, &nnz) != ATTN_OK);
   bad = pat(ATTN_ATTNSINK, 1, 2, 0);
-  CHECK(attn_index_nnz(&bad, 1, 650, &nnz) != ATTN_OK);  // L % 64
+  CHECK(attn_index_nnz(&bad, 1, 0, &nnz) != ATTN_OK);    // empty sequence
+  // a partial last block: ceil(650 / 64) = 11 blocks, the lists of 704 tokens
+  int64_t nnz_ragged = 0, nnz_whole = 0;
+  CHECK(attn_index_nnz(&bad, 1, 650, &nnz_ragged) == ATTN_OK);
+  CHECK(attn_index_nnz(&bad, 1, 704, &nnz_whole) == ATTN_OK);
+  CHECK(nnz_ragged == nnz_whole);
   CHECK(attn_index_nnz(&bad, 1, 640, nullptr) != ATTN_OK);
 
   // layer map

@@ -11,7 +11,7 @@ import pytest
 
 import long_context_sparse_static_amd as lcs
 from oracle import (ATTNSINK, BLOCKSPARSE, FULL, SLIDING, block_lists, blocksparse_decode_positions,
-                    transpose_lists)
+                    pattern_lists_for_head, transpose_lists)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn_sparse.h")
@@ -116,7 +116,7 @@ def test_mixed_index_rejects_inconsistent_heads():
     with pytest.raises(lcs.AttnError):
         lcs.attn_index_nnz_mixed([lcs.full_pattern(), lcs.Pattern(7)], L)  # unknown kind
     with pytest.raises(lcs.AttnError):
-        lcs.attn_index_nnz_mixed([lcs.full_pattern()], 1000)              # L % 64
+        lcs.attn_index_nnz_mixed([lcs.full_pattern()], 0)                 # empty sequence
     with pytest.raises(lcs.AttnError):                                    # one token window per launch
         lcs.attn_index_nnz_mixed([lcs.full_pattern(), lcs.sliding_pattern(1, 100)], L)
 
@@ -127,6 +127,27 @@ def test_sliding_pattern_rejections():
                 lcs.Pattern(lcs.ATTN_SLIDING, 1, 0, 0, False, window_tokens=64)):
         with pytest.raises(lcs.AttnError):
             lcs.attn_index_nnz(bad, 1, L)
+
+
+@pytest.mark.parametrize("L", [1, 63, 65, 1000, 64 * 9 + 37])
+def test_index_of_ragged_length(L):
+    """A sequence whose last block is partial has ceil(L / 64) blocks and the
+    same lists as the whole-block length: the oracle's scan over ceil(L/64)."""
+    nb = -(-L // 64)
+    for pat in (lcs.attnsink_pattern(1, 3), lcs.blocksparse_pattern(1, 2, 3), lcs.full_pattern(),
+                lcs.sliding_pattern(1, 100)):
+        H = 3 if pat.head_dependent else 1
+        ix = lcs.attn_index_build(pat, H, L, with_csc=True)
+        assert (ix.n_qblocks, ix.n_kblocks) == (nb, nb)
+        lcs.attn_index_validate(ix)
+        assert ix.nnz == lcs.attn_index_nnz(pat, H, 64 * nb)
+        for h in range(H):
+            opat = dict(kind={lcs.ATTN_FULL: FULL, lcs.ATTN_ATTNSINK: ATTNSINK, lcs.ATTN_BLOCKSPARSE: BLOCKSPARSE,
+                              lcs.ATTN_SLIDING: SLIDING}[pat.kind], block=64, sink_blocks=pat.sink_blocks,
+                        local_blocks=pat.local_blocks, stride=pat.stride, window_tokens=pat.window_tokens)
+            want = pattern_lists_for_head(opat, nb, h)
+            assert [ix.row(h, i) for i in range(nb)] == want
+            assert [ix.col(h, j) for j in range(nb)] == transpose_lists(want, nb)
 
 
 def test_index_nnz_closed_forms():
@@ -141,7 +162,7 @@ def test_index_nnz_closed_forms():
 
 def test_index_rejects_bad_arguments():
     with pytest.raises(lcs.AttnError):
-        lcs.attn_index_nnz(lcs.attnsink_pattern(1, 4), 1, 1000)          # L % 64
+        lcs.attn_index_nnz(lcs.attnsink_pattern(1, 4), 1, 0)             # empty sequence
     with pytest.raises(lcs.AttnError):
         lcs.attn_index_nnz(lcs.attnsink_pattern(1, 0), 1, 1024)          # local < 1
     with pytest.raises(lcs.AttnError):
@@ -207,7 +228,10 @@ def _fwd(dtype=lcs.ATTN_BF16, B=1, H=2, L=256, d=128, scale=0.1, pattern=None, i
 
 
 def test_forward_validation_errors():
-    assert _fwd(L=1000) == lcs.ATTN_ERR_INVALID_ARG                   # L % 64
+    assert _fwd(L=1000) == lcs.ATTN_ERR_INVALID_ARG                   # index of 15 blocks, not ceil(1000/64)
+    ragged_ix = lcs.attn_index_t(1, 16, 16, 10, FAKE, FAKE, None, None)
+    non_causal = lcs.Pattern(lcs.ATTN_ATTNSINK, 1, 2, causal=False).c_struct()
+    assert _fwd(L=1000, ix=ragged_ix, pattern=non_causal) == lcs.ATTN_ERR_UNSUPPORTED   # keys past L
     assert _fwd(B=0) == lcs.ATTN_ERR_INVALID_ARG
     assert _fwd(H=0) == lcs.ATTN_ERR_INVALID_ARG
     assert _fwd(L=0) == lcs.ATTN_ERR_INVALID_ARG                      # empty sequence
