@@ -42,6 +42,9 @@ def test_fp32_attnsink_1k_exact_workload():
 @pytest.mark.parametrize("pat,d,H,nb", [
     (lcs.blocksparse_pattern(1, 3, 4), 128, 4, 13),
     (lcs.full_pattern(), 64, 2, 9),
+    # 2 x 4 x 40 = 320 query blocks: the launch with one key group per row
+    (lcs.blocksparse_pattern(1, 3, 4), 128, 4, 40),
+    (lcs.sliding_pattern(1, 100), 64, 4, 40),
 ])
 def test_fp32_other_patterns(pat, d, H, nb):
     need_gpu()
