@@ -146,6 +146,54 @@ def test_out_of_range_index_entries_are_skipped():
     assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
 
 
+def _junk_index(good, nb, with_csc):
+    """The lists of ``good`` (one index head) with out-of-range ids (-5, and
+    1000) around every row and column, and final pointers past nnz."""
+    class Raw:
+        def __init__(self, device):
+            rows = [[-5] + good.row(0, i) + [1000] for i in range(nb)]
+            rp = np.cumsum([0] + [len(r) for r in rows]).astype(np.int32)
+            rp[-1] += 50
+            ci = np.array([x for r in rows for x in r], dtype=np.int32)
+            self.t = [torch.from_numpy(rp).to(device), torch.from_numpy(ci).to(device)]
+            self.ix = lcs.attn_index_t(1, nb, nb, len(ci), self.t[0].data_ptr(), self.t[1].data_ptr(), None, None)
+            if with_csc:
+                cols = [[-5] + good.col(0, j) + [1000] for j in range(nb)]
+                cp = np.cumsum([0] + [len(c) for c in cols]).astype(np.int32)
+                cp[-1] += 50
+                ri = np.array([x for c in cols for x in c], dtype=np.int32)
+                assert len(ri) == len(ci)
+                self.t += [torch.from_numpy(cp).to(device), torch.from_numpy(ri).to(device)]
+                self.ix.col_ptr, self.ix.row_idx = self.t[2].data_ptr(), self.t[3].data_ptr()
+
+        def c_struct(self):
+            return self.ix
+    return Raw
+
+
+def test_out_of_range_entries_skipped_fp32_and_backward():
+    """The fp32 forward and the backward (CSR and CSC walks) skip the same
+    junk entries and give the results of the clean index, bit for bit."""
+    need_gpu()
+    pat = lcs.attnsink_pattern(1, 2)
+    L, nb = 64 * 5, 5
+    good = lcs.attn_index_build(pat, 1, L, with_csc=True)
+    gix = lcs.DeviceIndex(good, torch.device("cuda"))
+    junk = _junk_index(good, nb, True)(torch.device("cuda"))
+    q, k, v = _inputs((1, 2, L, 64), 91, torch.float32)
+    o_ref, l_ref = lcs.attn_sparse_fwd(q, k, v, gix, pat)
+    o, lse = lcs.attn_sparse_fwd(q, k, v, junk, pat)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+    q, k, v, do = (x.to(torch.bfloat16) for x in (q, k, v, torch.randn_like(q)))
+    o, lse = lcs.attn_sparse_fwd(q, k, v, gix, pat)
+    ref = lcs.attn_sparse_bwd(q, k, v, o, lse, do, gix, pat)
+    got = lcs.attn_sparse_bwd(q, k, v, o, lse, do, junk, pat)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(got, ref):
+        assert torch.equal(a_, b_)
+
+
 def test_deterministic_repeat():
     need_gpu()
     pat = lcs.blocksparse_pattern(1, 4, 8)
