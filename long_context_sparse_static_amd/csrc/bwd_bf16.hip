@@ -307,30 +307,37 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// dK, dV: one workgroup per 64 key tokens (one key block, its CSC list),
-// two workgroups per CU.  4 waves as 2 pairs; pair p (waves p and p + 2)
-// owns 32 keys (lane = key) and splits each listed query block by its
-// 32-query halves: wave p takes half 0 and accumulates dV, wave p + 2 takes
-// half 1 and accumulates dK.  The two workgroups on a CU share each SIMD
-// (one wave each) and run unsynchronised, so one's vector work overlaps the
-// other's matrix work; within a workgroup the pair's waves work in step.  Per block, each wave on its half:
+// dK, dV: NW waves as NW / 2 pairs; pair p (waves p and p + NW / 2) owns 32
+// keys (lane = key) of key block p / 2 of the workgroup's tile and splits
+// each listed query block by its 32-query halves: wave p takes half 0 and
+// accumulates dV, its partner takes half 1 and accumulates dK.  The
+// workgroup walks the union of its key blocks' CSC lists.
+//   NW = 4: one key block per workgroup, two workgroups per CU, which run
+//   unsynchronised, so one's vector work overlaps the other's matrix work.
+//   NW = 8 (BlockSparse): two members of a head's strided class per
+//   workgroup (KeyTiles), one workgroup per CU.  Every Q and dO tile loaded
+//   serves both blocks: those columns run over nearly all later query
+//   blocks, and with one key block per workgroup the 128K BlockSparse dK/dV
+//   pass hit L2 on only 24% of its tile reads.
+// Per block, each wave on its half:
 //   S = Q K^T, dP = dO V^T - D (the accumulator starts at -D),
 //   P = exp2(S c - LSE2) (masked), dS = P dP, both packed to bf16;
 // then the pair trades through LDS what the other's product needs (wave p
-// sends its dS, wave p + 4 its P) and, after the exchange barrier,
-//   wave p:      dV^T += dO^T P       wave p + 4:  dK^T += Q^T dS
+// sends its dS, its partner its P) and, after the exchange barrier,
+//   wave p:      dV^T += dO^T P       partner:     dK^T += Q^T dS
 // over the whole block.  Each wave holds one accumulator set, so both fit
 // on their SIMD at once (a single wave holding all of it needs about 400
 // registers and runs alone), and the two halves of the vector work run on
 // the two waves.  Q and dO are read as rows and transposed (kBothRead).
 // ----------------------------------------------------------------------------
-constexpr int kDkvWaves = 4;
-constexpr int kDkvThreads = kDkvWaves * 64;
-constexpr int kDkvPairs = kDkvWaves / 2;
-constexpr int kDkvTB = kDkvPairs / 2;   // key blocks per workgroup (two pairs per block)
+constexpr int kDkvMaxPairs = 4;   // of the NW = 8 form (LDS sizing)
 
-template <int D, bool WIN, bool DENSE, bool RAG>
-__global__ __launch_bounds__(kDkvThreads, 8 / kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
+template <int D, bool WIN, bool DENSE, bool RAG, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int kDkvWaves = NW;
+  constexpr int kDkvThreads = NW * 64;
+  constexpr int kDkvPairs = NW / 2;
+  constexpr int kDkvTB = kDkvPairs / 2;   // key blocks per workgroup (two pairs per block)
   using QT = SwzTile<D, kBothRead>;
   constexpr int KS = D / 16, MT = D / 32;
   __shared__ __attribute__((aligned(1024))) char q0[QT::TILE];
@@ -604,16 +611,31 @@ __global__ __launch_bounds__(kDkvThreads, 8 / kDkvWaves) void bwd_dkdv_kernel(Bw
     }
   }
 
-  // every wave is done with the Q slots (no loads in flight after the walk):
-  // they stage the output rows, waves 0-1 in q0, 2-3 in q1
-  static_assert(kDkvWaves == 4, "output staging holds two waves per Q slot");
+  // every wave is done with the tile slots (no loads in flight after the
+  // walk): they stage the output rows, two waves per slot
+  static_assert(kDkvWaves == 4 || kDkvWaves == 8, "output staging: waves 0-1 in q0, 2-3 q1, 4-5 o0, 6-7 o1");
   __syncthreads();
   if (!k_valid) return;
   const int ld_out = side0 ? (DENSE ? D : a.dvs.l) : (DENSE ? D : a.dks.l);
   bf16 *out = side0 ? (bf16 *)a.dv + (DENSE ? dense_base : a.dvs.at(bb, head)) + (size_t)k_wave * ld_out
                     : (bf16 *)a.dk + (DENSE ? dense_base : a.dks.at(bb, head)) + (size_t)k_wave * ld_out;
-  store_rows_staged<D, RAG>(acc, side0 ? 1.0f : a.scale, (wave < 2 ? q0 : q1) + (wave & 1) * 32 * 2 * D, out,
-                       ld_out, lane, a.L - k_wave);
+  char *stage = wave < 2 ? q0 : wave < 4 ? q1 : wave < 6 ? o0 : o1;
+  store_rows_staged<D, RAG>(acc, side0 ? 1.0f : a.scale, stage + (wave & 1) * 32 * 2 * D, out, ld_out, lane,
+                            a.L - k_wave);
+}
+
+// dK/dV launch with NW waves per workgroup (see bwd_dkdv_kernel)
+template <int D, bool WIN, bool DENSE, bool RAG, int NW>
+hipError_t launch_dkdv(const BwdArgs &a, hipStream_t s) {
+  constexpr int TB = NW / 4;
+  const int k_tiles = KeyTiles<TB>::per_head(a.ix.n_kblocks, a.kgroup);
+  const size_t dyn_k = RowsBitmap<TB>::lds_bytes(a.ix.n_qblocks);
+  hipError_t e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel<D, WIN, DENSE, RAG, NW>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_k);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, WIN, DENSE, RAG, NW>), dim3(a.B * a.H * k_tiles), dim3(NW * 64), dyn_k,
+                     s, a);
+  return hipSuccess;
 }
 
 template <int D, bool WIN, bool DENSE, bool RAG>
@@ -622,18 +644,20 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const int rpb = 256 / (D / 8);
   const int grid_delta = (int)((rows + rpb - 1) / rpb);
   const int q_tiles = (a.ix.n_qblocks + kBwdTB - 1) / kBwdTB;
-  const int k_tiles = KeyTiles<kDkvTB>::per_head(a.ix.n_kblocks, a.kgroup);
   const int BH = a.B * a.H;
-  const size_t dyn_k = RowsBitmap<kDkvTB>::lds_bytes(a.ix.n_qblocks);
   const size_t dyn_q = RowsBitmap<kBwdTB>::lds_bytes(a.ix.n_kblocks);
-  hipError_t e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel<D, WIN, DENSE, RAG>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_k);
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute((const void *)bwd_dq_kernel<D, WIN, DENSE, RAG>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_q);
+  hipError_t e = hipFuncSetAttribute((const void *)bwd_dq_kernel<D, WIN, DENSE, RAG>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_q);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3(grid_delta), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, WIN, DENSE, RAG>), dim3(BH * k_tiles), dim3(kDkvThreads), dyn_k, s, a);
+  // BlockSparse (a per-head index grouped by strided class): two key blocks
+  // per dK/dV workgroup; otherwise one
+  if constexpr (!WIN) {
+    e = a.kgroup > 1 ? launch_dkdv<D, WIN, DENSE, RAG, 8>(a, s) : launch_dkdv<D, WIN, DENSE, RAG, 4>(a, s);
+  } else {
+    e = launch_dkdv<D, WIN, DENSE, RAG, 4>(a, s);
+  }
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dq_kernel<D, WIN, DENSE, RAG>), dim3(BH * q_tiles), dim3(kBwdThreads), dyn_q, s, a);
   return hipGetLastError();
 }
@@ -643,8 +667,8 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
 size_t bwd_bf16_lds_bytes(int d, int n_blocks) {
   // dK/dV kernel: two Q and two dO slots, four 64-float vectors, the
   // packed-operand exchange (4 KB per pair), bitmaps
-  const size_t tiles = 4 * (size_t)kBlock * 2 * d + 4 * kBlock * sizeof(float) + kDkvPairs * 4 * 64 * 16;
-  return tiles + RowsBitmap<kDkvTB>::lds_bytes(n_blocks);
+  const size_t tiles = 4 * (size_t)kBlock * 2 * d + 4 * kBlock * sizeof(float) + kDkvMaxPairs * 4 * 64 * 16;
+  return tiles + RowsBitmap<2>::lds_bytes(n_blocks);
 }
 
 template <bool RAG>
