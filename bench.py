@@ -274,17 +274,23 @@ class Prefill:
         torch.cuda.synchronize()
         self.pairs = self.ix.host.nnz * (heads if not pattern.head_dependent else 1)
 
+    def fwd(self):
+        lcs.attn_sparse_fwd(self.q, self.k, self.v, self.ix, self.pattern, o=self.o, lse=self.lse)
+
+    def bwd(self):
+        lcs.attn_sparse_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, self.ix,
+                            self.pattern, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
+
     def step(self, timer):
         with timer.span("fwd"):
-            lcs.attn_sparse_fwd(self.q, self.k, self.v, self.ix, self.pattern, o=self.o, lse=self.lse)
+            self.fwd()
         if self.backward:
             with timer.span("bwd"):
-                lcs.attn_sparse_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, self.ix,
-                                    self.pattern, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
+                self.bwd()
 
     def summary(self, times):
-        """Per-launch medians / minima and rates of one timed run (every span
-        is one call)."""
+        """Per-launch medians / minima and rates from lists of per-call times
+        (ms) under "fwd" and "bwd"."""
         fl = self.pairs * pair_flops(self.d)
         f = times["fwd"]
         out = dict(block_pairs=self.pairs, fwd_tflop=fl / 1e12, fwd_ms=float(np.median(f)),
@@ -327,7 +333,12 @@ class Prefill:
 
 # The five configurations of the workload definitions plus the 128K
 # BlockSparse layer that the prefill target names, timed in the default run
-# after the hybrid step (each one launch per call, hipEvents on the stream).
+# after the hybrid step.  Each figure is the time per call of a batch of
+# back-to-back calls between one pair of hipEvents on the stream (median over
+# batches): an event pair around every call adds up to about 60 us to a
+# 0.4 ms launch (8K AttnSink: 0.449 ms per-call spans against 0.387 ms per
+# call back to back and 0.386 ms of kernel time under rocprofv3), and nothing
+# at 128K.
 CONFIGS = (
     ("C1_attnsink1k_fp32", lambda: Prefill("attnsink1k_fp32", lcs.attnsink_pattern(1, 4), 1024, 1,
                                            heads=1, d=64, dtype=torch.float32)),
@@ -339,26 +350,46 @@ CONFIGS = (
 )
 
 
-def config_sweep(warmup=3, iters=10, names=None):
-    """Times every configuration in CONFIGS (warmup untimed calls, then
-    iters timed calls); returns {name: summary}."""
+def batch_ms(call, iters, batches):
+    """Per-call time (ms) of iters back-to-back calls between one event pair,
+    once per batch."""
+    out = []
+    for _ in range(batches):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(iters):
+            call()
+        e.record()
+        torch.cuda.synchronize()
+        out.append(s.elapsed_time(e) / iters)
+    return out
+
+
+def config_sweep(warmup=3, iters=10, batches=5, names=None):
+    """Times every configuration in CONFIGS (warmup untimed steps, then
+    batches of iters back-to-back forward calls, and of backward calls where
+    the configuration trains); returns {name: summary}."""
     out = {}
     for name, make in CONFIGS:
         if names and name not in names:
             continue
         log(f"[bench] config {name}")
         wl = make()
-        timer = Timer()
         for _ in range(warmup):
-            wl.step(timer)
-        timer.collect()
-        for _ in range(iters):
-            wl.step(timer)
-        rep = wl.summary(timer.collect())
+            wl.fwd()
+            if wl.backward:
+                wl.bwd()
+        torch.cuda.synchronize()
+        times = {"fwd": batch_ms(wl.fwd, iters, batches)}
+        if wl.backward:
+            times["bwd"] = batch_ms(wl.bwd, iters, batches)
+        rep = wl.summary(times)
         rep["workload"] = wl.describe()
         rep["iters"] = iters
+        rep["batches"] = batches
         if wl.dtype == torch.float32:
-            # 73 MFLOP in 16 workgroups: bound by launch latency, not by a roofline
+            # 73 MFLOP in 64 small workgroups: bound by launch latency, not by a roofline
             rep["bound"] = "launch"
             rep.pop("fwd_frac_of_peak")
         out[name] = rep
