@@ -182,23 +182,33 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const bool q_valid = qb < nqb;
   const int q_wave = qb * kBlock + (wave & 1) * 32;  // first query of this wave
   const int q_tok = q_wave + n;
-  const bf16 *qp = (const bf16 *)a.q + (DENSE ? dense_base : a.qs.at(bb, head)) + (size_t)q_tok * lq;
-  const bf16 *dop = (const bf16 *)a.dout + (DENSE ? dense_base : a.dos.at(bb, head)) + (size_t)q_tok * ldo;
+  const bf16 *qw = (const bf16 *)a.q + (DENSE ? dense_base : a.qs.at(bb, head)) + (size_t)q_wave * lq;
+  const bf16 *dow = (const bf16 *)a.dout + (DENSE ? dense_base : a.dos.at(bb, head)) + (size_t)q_wave * ldo;
 
-  // rows past L of a partial last block: zero operands, P = 0 (LSE2 = +inf)
+  // The wave's operand rows, loaded inside the bitmap build behind the list
+  // reads.  Rows past L of a partial last block (and every row of a query
+  // block past the last) load as zero operands, and P = 0 there (LSE2 = +inf).
   const bool q_in = q_valid && (!RAG || q_tok < a.L);
+  const int rows_left = q_valid ? a.L - q_wave : 0;
   bf16x8 bq[KS], bdo[KS];
+  float lse2, dlt;
+  auto load_rows = [&]() __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rq = rows_rsrc<32>(qw, rows_left, 2 * lq, 2 * D);
+    const __amdgpu_buffer_rsrc_t ro = rows_rsrc<32>(dow, rows_left, 2 * ldo, 2 * D);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    bq[ks] = q_in ? *(const bf16x8 *)(qp + ks * 16 + hh * 8) : bf16x8{};
-    bdo[ks] = q_in ? *(const bf16x8 *)(dop + ks * 16 + hh * 8) : bf16x8{};
-  }
+    for (int ks = 0; ks < KS; ++ks) {
+      bq[ks] = load_row16(rq, 2 * (n * lq + ks * 16 + hh * 8));
+      bdo[ks] = load_row16(ro, 2 * (n * ldo + ks * 16 + hh * 8));
+    }
+    const size_t v0 = (size_t)bh * a.L + q_wave;
+    const float l = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rows_rsrc<32>(a.lse2 + v0, rows_left, 4, 4), 4 * n, 0, 0));
+    const float e = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rows_rsrc<32>(a.delta + v0, rows_left, 4, 4), 4 * n, 0, 0));
+    lse2 = q_in ? l : INFINITY;
+    dlt = q_in ? -e : 0.f;
+  };
   const float c = a.scale * kLog2e;
-  float lse2 = INFINITY, dlt = 0.f;
-  if (q_in) {
-    lse2 = a.lse2[(size_t)bh * a.L + q_tok];
-    dlt = -a.delta[(size_t)bh * a.L + q_tok];
-  }
 
   KT kr;
   kr.init_reads(lane);
@@ -212,7 +222,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   RowsBitmap<kBwdTB> pb;
   pb.init(dyn_lds, a.ix.n_kblocks);
   pb.build(a.ix.row_ptr + (size_t)hidx * (nqb + 1), tile * kBwdTB, nqb, a.ix.nnz, a.ix.col_idx,
-           a.ix.n_kblocks, kBwdThreads);
+           a.ix.n_kblocks, kBwdThreads, load_rows);
   RowsIter<kBwdTB> it;
   it.start(a.ix.n_kblocks, min(tile * kBwdTB + kBwdTB - 1, nqb - 1) & ~63);
   auto advance = [&]() __attribute__((always_inline)) -> BwdPos {
@@ -406,17 +416,22 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv_kernel(BwdArgs a) {
   const int k_wave = kb * kBlock + (pair & 1) * 32;  // first key of this pair
   const int k_tok = k_wave + n;
 
-  // K and V of the pair's keys: the B operands of S and dP
+  // K and V of the pair's keys: the B operands of S and dP, loaded inside
+  // the bitmap build behind the list reads (keys past L load as zeros)
   bf16x8 bk[KS], bv[KS];
-  {
-    const bf16 *kp = (const bf16 *)a.k + (DENSE ? dense_base : a.ks.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.ks.l);
-    const bf16 *vp = (const bf16 *)a.v + (DENSE ? dense_base : a.vs.at(bb, head)) + (size_t)k_tok * (DENSE ? D : a.vs.l);
+  auto load_kv = [&]() __attribute__((always_inline)) {
+    const int lk = DENSE ? D : a.ks.l, lv = DENSE ? D : a.vs.l;
+    const bf16 *kw = (const bf16 *)a.k + (DENSE ? dense_base : a.ks.at(bb, head)) + (size_t)k_wave * lk;
+    const bf16 *vw = (const bf16 *)a.v + (DENSE ? dense_base : a.vs.at(bb, head)) + (size_t)k_wave * lv;
+    const int rows_left = k_valid ? a.L - k_wave : 0;
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc<32>(kw, rows_left, 2 * lk, 2 * D);
+    const __amdgpu_buffer_rsrc_t rv = rows_rsrc<32>(vw, rows_left, 2 * lv, 2 * D);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      bk[ks] = k_valid && (!RAG || k_tok < a.L) ? *(const bf16x8 *)(kp + ks * 16 + hh * 8) : bf16x8{};
-      bv[ks] = k_valid && (!RAG || k_tok < a.L) ? *(const bf16x8 *)(vp + ks * 16 + hh * 8) : bf16x8{};
+      bk[ks] = load_row16(rk, 2 * (n * lk + ks * 16 + hh * 8));
+      bv[ks] = load_row16(rv, 2 * (n * lv + ks * 16 + hh * 8));
     }
-  }
+  };
   const float c = a.scale * kLog2e;
   f32x16 acc[MT];   // dV^T (side 0) or dK^T (side 1) of the pair's keys
 #pragma unroll
@@ -447,7 +462,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv_kernel(BwdArgs a) {
   RowsBitmap<kDkvTB> pb;
   pb.init(dyn_lds, nqb);
   pb.build_rows(a.ix.col_ptr + (size_t)hidx * (nkb + 1), krows, a.ix.nnz, a.ix.row_idx, nqb,
-                kDkvThreads);
+                kDkvThreads, load_kv);
   RowsIter<kDkvTB> it;
   it.start(nqb, (krows[0] + 63) & ~63);
   auto advance = [&]() __attribute__((always_inline)) -> BwdPos {

@@ -156,12 +156,16 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int q_wave = qb * kBlock + (wave & 1) * 32;  // first query of this wave
   const int q_tok = q_wave + n;
 
-  // Q^T operand of S^T = K Q^T: lane holds query n, d = 16 ks + 8 hh .. +7.
+  // Q^T operand of S^T = K Q^T: lane holds query n, d = 16 ks + 8 hh .. +7
+  // (loaded inside the bitmap build, behind the list reads; rows past L,
+  // and every row of a query block past the last, load as zeros)
   bf16x8 bq[KS];
+  auto load_q = [&]() __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rs =
+        rows_rsrc<32>(qg + (size_t)q_wave * lq, q_valid ? a.L - q_wave : 0, 2 * lq, 2 * D);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    bq[ks] = q_valid && (!RAG || q_tok < a.L) ? *(const bf16x8 *)(qg + (size_t)q_tok * lq + ks * 16 + hh * 8)
-                                               : bf16x8{};
+    for (int ks = 0; ks < KS; ++ks) bq[ks] = load_row16(rs, 2 * (n * lq + ks * 16 + hh * 8));
+  };
 
   // Per-lane global element offsets of this wave's share of a tile load
   // (group B waves load; a wave's share is 16 token rows).
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   RowsBitmap<kFwdQB> pb;
   pb.init(dyn_lds, a.ix.n_kblocks);
   pb.build(a.ix.row_ptr + (size_t)hidx * (nqb + 1), tile * kFwdQB, nqb, a.ix.nnz, a.ix.col_idx,
-           a.ix.n_kblocks, kFwdThreads);
+           a.ix.n_kblocks, kFwdThreads, load_q);
   RowsIter<kFwdQB> it;
   it.start(a.ix.n_kblocks, min(tile * kFwdQB + kFwdQB - 1, nqb - 1) & ~63);
   auto advance = [&]() __attribute__((always_inline)) -> WalkPos {

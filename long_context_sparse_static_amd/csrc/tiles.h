@@ -35,6 +35,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *g, int r
   return buffer_rsrc_n(g, rows_left >= kBlock ? -1 : (rows_left - 1) * ld_bytes + row_bytes);
 }
 
+// Descriptor for reading ROWS rows from g (ld_bytes apart, row_bytes used
+// per row) of which rows_left exist (none if rows_left <= 0): loads past
+// them return zeros, so a wave's operand rows load without a branch.
+template <int ROWS>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void *g, int rows_left, int ld_bytes,
+                                                            int row_bytes) {
+  return buffer_rsrc_n(g, rows_left >= ROWS ? -1 : rows_left <= 0 ? 0 : (rows_left - 1) * ld_bytes + row_bytes);
+}
+// 16 bytes of a row operand through a rows_rsrc descriptor
+__device__ __forceinline__ bf16x8 load_row16(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0));
+}
+
 template <int D, int KIND>
 struct SwzTile {
   static constexpr int RB = 2 * D;          // bytes per token row
@@ -168,8 +181,13 @@ struct RowsBitmap {
   // extents are read first and the R lists then read as one flat range, kU
   // entries per thread in flight, so the build waits for two dependent
   // global reads rather than two per row (and one per entry and thread).
+  // issue() runs once per thread after the first round of list reads is
+  // issued and before any of them is used: loads it issues are not waited
+  // for here (loads return in order, so a load issued before the list reads
+  // would hold up the build until it landed).
+  template <typename Issue>
   __device__ void build_rows(const int32_t *ptr, const int (&rows)[R], int nnz, const int32_t *ids,
-                             int n_ids, int nt) {
+                             int n_ids, int nt, Issue &&issue) {
     constexpr int kU = R >= 4 ? 8 : 1;   // the two-row (backward) tiles gained nothing from more
     int beg[R], len[R];
 #pragma unroll
@@ -199,8 +217,8 @@ struct RowsBitmap {
       }
       return pos;
     };
-    for (int x0 = threadIdx.x; x0 < total; x0 += kU * nt) {
-      int jv[kU], rv[kU];
+    int jv[kU], rv[kU];
+    auto read_round = [&](int x0) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int x = x0 + u * nt;
@@ -208,11 +226,20 @@ struct RowsBitmap {
         rv[u] = 0;
         if (x < total) jv[u] = ids[locate(x, rv[u])];
       }
+    };
+    auto or_round = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int j = jv[u];
         if (j >= 0 && j < n_ids) atomicOr(&bm[rv[u] * nw + (j >> 5)], 1u << (j & 31));
       }
+    };
+    read_round(threadIdx.x);   // every thread, entries or not, so issue() runs once each
+    issue();
+    or_round();
+    for (int x0 = threadIdx.x + kU * nt; x0 < total; x0 += kU * nt) {
+      read_round(x0);
+      or_round();
     }
     __syncthreads();
     for (int w = threadIdx.x; w < nw; w += nt) {
@@ -223,14 +250,19 @@ struct RowsBitmap {
     }
     __syncthreads();
   }
+  __device__ void build_rows(const int32_t *ptr, const int (&rows)[R], int nnz, const int32_t *ids,
+                             int n_ids, int nt) {
+    build_rows(ptr, rows, nnz, ids, n_ids, nt, []() {});
+  }
 
   // Lists first .. first + R - 1 (those below n_rows).
+  template <typename Issue>
   __device__ void build(const int32_t *ptr, int first, int n_rows, int nnz, const int32_t *ids,
-                        int n_ids, int nt) {
+                        int n_ids, int nt, Issue &&issue) {
     int rows[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) rows[r] = first + r < n_rows ? first + r : -1;
-    build_rows(ptr, rows, nnz, ids, n_ids, nt);
+    build_rows(ptr, rows, nnz, ids, n_ids, nt, issue);
   }
 };
 
