@@ -152,9 +152,9 @@ __device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[D / 32], f
 // Union of R consecutive CSR (or CSC) rows -- the 64-token blocks of one
 // workgroup tile -- held as R LDS bitmaps over block ids plus a summary
 // bitmap of the non-empty words.  Built once per workgroup (atomicOr per list
-// entry, so row order, duplicates and out-of-range ids cannot matter: bad ids
-// are dropped), then walked in ascending order by every wave with scalar bit
-// tricks.
+// entry into both, so row order, duplicates and out-of-range ids cannot
+// matter: bad ids are dropped), then walked in ascending order by every wave
+// with scalar bit tricks.
 //   LDS layout (32-bit words): bm[r*nw .. r*nw+nw) row r, then sm[0..nsw)
 //   (bit w set when word w of any row is non-zero).
 template <int R>
@@ -227,11 +227,15 @@ struct RowsBitmap {
         if (x < total) jv[u] = ids[locate(x, rv[u])];
       }
     };
+    // each entry sets its bit and its word's summary bit
     auto or_round = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int j = jv[u];
-        if (j >= 0 && j < n_ids) atomicOr(&bm[rv[u] * nw + (j >> 5)], 1u << (j & 31));
+        if (j >= 0 && j < n_ids) {
+          atomicOr(&bm[rv[u] * nw + (j >> 5)], 1u << (j & 31));
+          atomicOr(&sm[j >> 10], 1u << ((j >> 5) & 31));
+        }
       }
     };
     read_round(threadIdx.x);   // every thread, entries or not, so issue() runs once each
@@ -240,13 +244,6 @@ struct RowsBitmap {
     for (int x0 = threadIdx.x + kU * nt; x0 < total; x0 += kU * nt) {
       read_round(x0);
       or_round();
-    }
-    __syncthreads();
-    for (int w = threadIdx.x; w < nw; w += nt) {
-      uint32_t any = 0u;
-#pragma unroll
-      for (int r = 0; r < R; ++r) any |= bm[r * nw + w];
-      if (any) atomicOr(&sm[w >> 5], 1u << (w & 31));
     }
     __syncthreads();
   }
