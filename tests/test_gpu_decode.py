@@ -197,6 +197,7 @@ def test_decode_full_size_all_heads():
     # token position p lives in slot p (sink) or sink + (p - sink) % window
     slots = [p if p < sink else sink + (p - sink) % window for p in keep]
     j_new = keep.tolist().index(t)
+    worst = [0.0, 0.0]
     for b in (0, 9):
         for h in range(H):
             kk = as_f64(rk0[b, h])[slots]
@@ -204,8 +205,10 @@ def test_decode_full_size_all_heads():
             kk[j_new] = as_f64(k_new[b, h, 0])
             vv[j_new] = as_f64(v_new[b, h, 0])
             wo, wl = decode_one(as_f64(q[b, h, 0]), kk, vv, np.arange(len(keep)), 1 / math.sqrt(d))
-            assert_bf16_close(as_f64(o[b, h, 0]), wo, f"sparse b{b} h{h}")
+            mx, mean = assert_bf16_close(as_f64(o[b, h, 0]), wo, f"sparse b{b} h{h}")
+            worst = [max(worst[0], mx), max(worst[1], mean)]
             assert abs(float(lse[b, h]) - wl) < 2e-3
+    print("sparse decode 2 seqs x 32 heads: O max", worst[0], "largest per-head mean", worst[1])
     assert torch.equal(ring_k[:, :, slot_new], k_new[:, :, 0])
     del ring_k, ring_v, rk0, rv0
 
@@ -216,12 +219,15 @@ def test_decode_full_size_all_heads():
     before = {b: (kc[b].clone(), vc[b].clone()) for b in seqs}    # the oracle's inputs (device copies)
     o, lse = lcs.attn_full_decode(q, k_new, v_new, kc, vc, pos, max_pos=t)
     torch.cuda.synchronize()
+    worst = [0.0, 0.0]
     for b in seqs:
         for h in range(H):
             kk, vv = (as_f64(x[h]) for x in before[b])
             kk[t] = as_f64(k_new[b, h, 0])
             vv[t] = as_f64(v_new[b, h, 0])
             wo, wl = decode_one(as_f64(q[b, h, 0]), kk, vv, np.arange(cap), 1 / math.sqrt(d))
-            assert_bf16_close(as_f64(o[b, h, 0]), wo, f"full b{b} h{h}")
+            mx, mean = assert_bf16_close(as_f64(o[b, h, 0]), wo, f"full b{b} h{h}")
+            worst = [max(worst[0], mx), max(worst[1], mean)]
             assert abs(float(lse[b, h]) - wl) < 2e-3
         assert torch.equal(kc[b, :, t], k_new[b, :, 0])
+    print("full decode 2 seqs x 32 heads: O max", worst[0], "largest per-head mean", worst[1])
