@@ -417,7 +417,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv_kernel(BwdArgs a) {
   const int k_tok = k_wave + n;
 
   // K and V of the pair's keys: the B operands of S and dP, loaded inside
-  // the bitmap build behind the list reads (keys past L load as zeros)
+  // the bitmap build behind the list reads (keys past L load as zeros when
+  // rows do not overlap in memory; their dK and dV are never stored)
   bf16x8 bk[KS], bv[KS];
   auto load_kv = [&]() __attribute__((always_inline)) {
     const int lk = DENSE ? D : a.ks.l, lv = DENSE ? D : a.vs.l;
@@ -444,8 +445,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv_kernel(BwdArgs a) {
   ldo.init(wave, lane, ldo_l);
   // the two 64-float per-token vectors of a query block: wave 0 loads LSE2,
   // wave 1 the -D values (4 bytes per lane)
-  // (a partial last block's rows past L load as zeros: zero Q and dO rows,
-  // LSE2 = 0 and -D = 0, so they add nothing to dK or dV)
+  // (a partial last block's vectors past L load as zeros, and its queries
+  // past L are masked in the vector step, so they add nothing to dK or dV)
   auto load_vec = [&](int i, float *lv, float *ev) __attribute__((always_inline)) {
     const int bytes = RAG ? 4 * min(kBlock, a.L - i * kBlock) : -1;
     if (wave == 0)
@@ -526,6 +527,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv_kernel(BwdArgs a) {
         constexpr int r = decltype(R)::value;
         s[r] = mask_neg_inf(s[r], (8 * (r >> 2) + (r & 3)) - lim);
       });
+    }
+    if constexpr (RAG) {
+      // queries past L of a partial last block: their Q and dO rows load as
+      // zeros only when rows do not overlap in memory (row stride >= d), so
+      // they are masked here as well
+      if ((i + 1) * kBlock > a.L) {
+        const int qlim = a.L - i * kBlock - 32 * h - 4 * hh;   // offsets below it are queries < L
+        static_for<16>([&](auto R) __attribute__((always_inline)) {
+          constexpr int r = decltype(R)::value;
+          s[r] = mask_neg_inf(s[r], qlim - 1 - (8 * (r >> 2) + (r & 3)));
+        });
+      }
     }
     if constexpr (WIN) {
       // queries at or past key + window: offset >= lim + window

@@ -83,3 +83,34 @@ def test_fused_qkv_forward_backward(d):
     assert_bf16_close(as_f64(o), wo, "O")
     for name, t, w in (("dq", dq, wq), ("dk", dk, wk), ("dv", dv, wv)):
         print(d, name, assert_bf16_close(as_f64(t), w, name))
+
+
+@pytest.mark.parametrize("stride", [0, 8, 72])
+def test_inputs_with_token_stride_below_d(stride):
+    """Q, K, V and dO whose token rows overlap (row stride below d; 0 repeats
+    one row), at a length with a partial last block: every tile and operand
+    load stays in range, and forward and backward equal those of contiguous
+    copies bit for bit."""
+    need_gpu()
+    pat = lcs.attnsink_pattern(1, 3)
+    B, H, L, d = 1, 2, 64 * 5 + 17, 128
+
+    def overlapping(name):
+        n = (L - 1) * stride + d
+        buf = randn((B, H, n), seed_for(930 + stride, 0, name), torch.bfloat16).cuda()
+        return buf.as_strided((B, H, L, d), (H * n, n, stride, 1))
+
+    q, k, v, do = (overlapping(n) for n in ("q", "k", "v", "do"))
+    ix = lcs.build_device_index(pat, H, L, q.device, with_csc=True)
+    o, lse = lcs.attn_sparse_fwd_strided(q, k, v, ix, pat)
+    dq, dk, dv = lcs.attn_sparse_bwd_strided(q, k, v, o, lse, do, ix, pat)
+    qc, kc, vc, doc = (t.contiguous() for t in (q, k, v, do))
+    o2, lse2 = lcs.attn_sparse_fwd(qc, kc, vc, ix, pat)
+    dq2, dk2, dv2 = lcs.attn_sparse_bwd(qc, kc, vc, o2, lse2, doc, ix, pat)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a, b)
+    wo, wl = sparse_forward(as_f64(q), as_f64(k), as_f64(v), oracle_pattern(pat))
+    assert_bf16_close(as_f64(o), wo, "O")
+    assert_bf16_close(as_f64(lse), wl, "LSE")
