@@ -78,15 +78,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base) 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc_n(const void *base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
 }
-template <int BYTES>
+// IMM, the instruction's immediate offset, moves the global and the LDS
+// address alike: lane i's bytes come from base + byte_off + IMM and land at
+// lds + IMM + i * BYTES.  Loads that differ only in IMM share one LDS base,
+// so they need no M0 value (and no SGPR) each.
+template <int BYTES, int IMM = 0>
 __device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t rs, int byte_off, void *lds) {
   static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte lanes");
+  static_assert(IMM >= 0 && IMM < 4096, "12-bit immediate offset");
   auto *l = (__attribute__((address_space(3))) void *)lds;
-  // the builtin wants its size as a literal
+  // the builtin wants its size and offset as literals
   if constexpr (BYTES == 16)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, byte_off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, byte_off, 0, IMM, 0);
   else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 4, byte_off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 4, byte_off, 0, IMM, 0);
 }
 
 // x if keep >= 0, else -inf: one bitfield insert keyed on keep's sign bit,

@@ -167,26 +167,34 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     for (int ks = 0; ks < KS; ++ks) bq[ks] = load_row16(rs, 2 * (n * lq + ks * 16 + hh * 8));
   };
 
-  // Per-lane global element offsets of this wave's share of a tile load
-  // (group B waves load; a wave's share is 16 token rows).
+  // Per-lane byte offsets of this wave's share of a tile load (group B
+  // waves load; a wave's share is 16 token rows).  Instruction i fills the
+  // LDS rows i KB past the wave's first: that step is its immediate offset,
+  // which moves the global address too, so it is taken out of the lane
+  // offsets, and every instruction of a slot shares one LDS base.  The
+  // descriptor base sits kShift bytes before the tile, so the offsets stay
+  // non-negative for any row stride.
+  constexpr int kShift = (Lay::LPW - 1) * Lay::RPI * RB;
   const int lw = wave & (kLoadWaves - 1);
   int goff_k[Lay::LPW], goff_v[Lay::LPW];
 #pragma unroll
   for (int i = 0; i < Lay::LPW; ++i) {
     const int r = lw * (kBlock / kLoadWaves) + i * Lay::RPI + lane / Lay::CPR;
     const int pc = lane % Lay::CPR;
-    goff_k[i] = 2 * (r * lk + ((pc ^ Lay::kswz(r)) << 3));   // bytes
-    goff_v[i] = 2 * (r * lv + ((pc ^ Lay::vswz(r)) << 3));
+    goff_k[i] = 2 * (r * lk + ((pc ^ Lay::kswz(r)) << 3)) + kShift - i * Lay::RPI * RB;
+    goff_v[i] = 2 * (r * lv + ((pc ^ Lay::vswz(r)) << 3)) + kShift - i * Lay::RPI * RB;
   }
   // tile of key block j of g (rows ld elements apart); the rows of a partial
   // last block past L load as zeros
   auto load_tile = [&](const bf16 *g, int j, int ld, char *lds, const int (&goff)[Lay::LPW])
                        __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rs =
-        tile_rsrc(g + (size_t)j * kBlock * ld, RAG ? a.L - j * kBlock : kBlock, 2 * ld, RB);
-#pragma unroll
-    for (int i = 0; i < Lay::LPW; ++i)
-      load_lds<16>(rs, goff[i], lds + (lw * (kBlock / kLoadWaves) + i * Lay::RPI) * RB);
+        tile_rsrc(g + (size_t)j * kBlock * ld, RAG ? a.L - j * kBlock : kBlock, 2 * ld, RB, kShift);
+    char *base = lds + lw * (kBlock / kLoadWaves) * RB;
+    static_for<Lay::LPW>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      load_lds<16, i * Lay::RPI * RB>(rs, goff[i], base);
+    });
   };
 
   // Per-lane LDS read offsets.  K row operand for k-step ks: row n (+32 t),

@@ -30,9 +30,13 @@ enum SwzKind { kRowRead = 0, kTrRead = 1, kBothRead = 2 };
 // Descriptor for the 64-row tile at g (rows ld_bytes apart, row_bytes used
 // per row) of a sequence with rows_left rows from the tile's first row: a
 // partial last block's rows past the end load as zeros and are never read.
+// The descriptor's base may sit `shift` bytes before g (the per-lane offsets
+// then carry the shift): offsets stay non-negative when an instruction's
+// immediate offset exceeds its rows' distance from g.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *g, int rows_left, int ld_bytes,
-                                                            int row_bytes) {
-  return buffer_rsrc_n(g, rows_left >= kBlock ? -1 : (rows_left - 1) * ld_bytes + row_bytes);
+                                                            int row_bytes, int shift = 0) {
+  return buffer_rsrc_n((const char *)g - shift,
+                       rows_left >= kBlock ? -1 : (rows_left - 1) * ld_bytes + row_bytes + shift);
 }
 
 // Descriptor for reading ROWS rows from g (ld_bytes apart, row_bytes used
@@ -66,7 +70,13 @@ struct SwzTile {
   struct Loader {
     static constexpr int LPW = kBlock / NL / RPI;  // instructions per wave
     static_assert(LPW >= 1 && kBlock % (NL * RPI) == 0, "load shape");
-    int goff[LPW];   // per-lane global byte offsets from the tile's first row
+    // Instruction i's LDS rows start i KB after the wave's first row: that
+    // step is its immediate offset, which moves the global address too, so
+    // it is taken back out of the lane offsets.  The descriptor base sits
+    // SHIFT bytes before the tile, so those stay non-negative for any row
+    // stride (also one below d).
+    static constexpr int SHIFT = (LPW - 1) * RPI * RB;
+    int goff[LPW];   // per-lane byte offsets from the descriptor base, less i KB
     int lds_row0;    // first LDS row of this wave's share
     // row_stride: elements between consecutive token rows in global memory
     __device__ __forceinline__ void init(int lw, int lane, int row_stride) {
@@ -74,15 +84,18 @@ struct SwzTile {
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int r = lds_row0 + i * RPI + lane / CPR;
-        goff[i] = 2 * (r * row_stride + (((lane % CPR) ^ swz(r)) << 3));
+        goff[i] = 2 * (r * row_stride + (((lane % CPR) ^ swz(r)) << 3)) + SHIFT - i * RPI * RB;
       }
     }
     // the tile at g of a sequence with rows_left rows from g on, row stride
     // ld elements (rows past the end load as zeros)
     __device__ __forceinline__ void load(const bf16 *g, int rows_left, int ld, char *lds) const {
-      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(g, rows_left, 2 * ld, RB);
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) load_lds<16>(rs, goff[i], lds + (lds_row0 + i * RPI) * RB);
+      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(g, rows_left, 2 * ld, RB, SHIFT);
+      char *base = lds + lds_row0 * RB;
+      static_for<LPW>([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        load_lds<16, i * RPI * RB>(rs, goff[i], base);
+      });
     }
   };
 
