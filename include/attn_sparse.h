@@ -131,8 +131,9 @@ typedef struct {
  * Q of a fused [B,L,3,H,d] projection is {3*L*H*d, d, 3*H*d} at offset 0
  * (K at H*d, V at 2*H*d).  Strides must be >= 0 and whole 16-byte vectors
  * (multiples of 8 bf16 / 4 fp32 elements), token <= INT32_MAX / 128, and the
- * base pointer 16-byte aligned.  Outputs must not overlap each other or the
- * inputs. */
+ * base pointer 16-byte aligned.  Input rows may overlap (a token stride
+ * below d, or 0 to repeat one row).  Outputs must not overlap each other or
+ * the inputs. */
 typedef struct {
   int64_t batch;
   int64_t head;
