@@ -542,6 +542,8 @@ def make_workload(name):
         return Prefill(name, lcs.blocksparse_pattern(1, 16, 8), 131072, 3)
     if name == "attnsink128k":
         return Prefill(name, lcs.attnsink_pattern(1, 64), 131072, 5)
+    if name == "full128k":
+        return Prefill(name, lcs.full_pattern(), 131072, 5)
     if name == "train64k":
         return Prefill(name, lcs.attnsink_pattern(1, 64), 65536, 4, backward=True)
     if name == "blocksparse32k_train":
