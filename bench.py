@@ -613,7 +613,15 @@ def cpu_baseline(spec, budget_s=15.0):
     threads = _blas_threads()
     rng = np.random.default_rng(0)
     common = dict(kind="oracle", cores=threads, affinity_cpus=len(os.sched_getaffinity(0)),
-                  cpu_model=cpu_model())
+                  cpu_model=cpu_model(), blas_threads=threads)
+
+    def extrapolated(rate_tflops):
+        # the benched work at the sampled rate, linear in its FLOPs (not run)
+        if "work_tflop" not in spec or rate_tflops <= 0:
+            return {}
+        return dict(extrapolated_s=spec["work_tflop"] / rate_tflops,
+                    extrapolated=f"{spec['work']} ({spec['work_tflop']:.1f} TFLOP) at the sampled rate, "
+                                 "linear in FLOPs; not run")
     kind = spec["kind"]
     if kind in ("prefill", "train"):
         pat, L, d, dtype = spec["pattern"], spec["L"], spec.get("d", D), spec.get("dtype", torch.bfloat16)
@@ -652,6 +660,7 @@ def cpu_baseline(spec, budget_s=15.0):
             return dict(value=flops / t_used / 1e12, unit="TFLOP/s", **common,
                         sample=f"{n_done} query rows (random, past the first window) of one head of "
                                f"{spec['what']}, float64 dense-masked NumPy; {t_used:.1f} s",
+                        sample_s=t_used, **extrapolated(flops / t_used / 1e12),
                         parity_vs_gpu=dict(rows=n_done, o_max_abs=err_o, o_mean_abs=err_sum / max(n_el, 1),
                                            lse_max_abs=err_l, tolerance="max 2e-2, mean 2e-3"))
         t0 = time.perf_counter()
@@ -672,7 +681,8 @@ def cpu_baseline(spec, budget_s=15.0):
         return dict(value=flops / t_used / 1e12, unit="TFLOP/s", **common,
                     sample=f"{n_done} query blocks (random, past the first window) of one head of "
                            f"{spec['what']}: forward + backward of each block's exact sub-problem, "
-                           f"float64 NumPy; {t_used:.1f} s")
+                           f"float64 NumPy; {t_used:.1f} s",
+                    sample_s=t_used, **extrapolated(flops / t_used / 1e12))
     if kind == "decode":
         t, d = spec["t"], D
         g = torch.Generator().manual_seed(spec["seed"])
@@ -699,10 +709,14 @@ def baseline_spec(name, wl):
     import oracle
     if name == "hybrid128k":
         return dict(kind="prefill", pattern=lcs.attnsink_pattern(SINK_BLOCKS, WINDOW_BLOCKS), L=131072,
-                    seed=seed_for(5, 0, "q"), what="one 128K AttnSink layer (the metric's sparse prefill)")
+                    seed=seed_for(5, 0, "q"), what="one 128K AttnSink layer (the metric's sparse prefill)",
+                    work_tflop=(N_LAYERS - (FULL_LAST - FULL_FIRST + 1)) * wl.nnz_sparse * pair_flops() / 1e12,
+                    work="the step's 21 sparse prefill layers")
     if isinstance(wl, Prefill):
+        fl = wl.pairs * pair_flops(wl.d) / 1e12
         return dict(kind="train" if wl.backward else "prefill", pattern=wl.pattern, L=wl.L, d=wl.d,
-                    dtype=wl.dtype, seed=seed_for(9, 0, "q"), what=wl.describe())
+                    dtype=wl.dtype, seed=seed_for(9, 0, "q"), what=wl.describe(),
+                    work_tflop=3.5 * fl if wl.backward else fl, work="one step of the workload")
     if name == "bsdecode128k":
         opat = _oracle_pattern(wl.pat)
         return dict(kind="decode", t=wl.t, seed=seed_for(6, 0, "cache"), what="a BlockSparse layer",
