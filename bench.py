@@ -320,7 +320,7 @@ class Prefill:
             t_b = sum(times["bwd"]) / steps
             extra.update(bwd_tflops=2.5 * fl / (t_b * 1e-3) / 1e12, bwd_ms=t_b)
             value = 3.5 * fl / ((t_f + t_b) * 1e-3) / 1e12
-            kernel, per_launch, avg = "attn_sparse_bwd (delta + dkdv + dq)", 2.5 * fl, t_b
+            kernel, per_launch, avg = "attn_sparse_bwd (dq, then dkdv)", 2.5 * fl, t_b
             traffic = None
         ach = per_launch / (avg * 1e-3) / 1e12
         return dict(value=value, extra=extra,

@@ -6,14 +6,16 @@
 // "Approach").
 //
 // With P = exp(scale * Q K^T - LSE) on the allowed (query, key) pairs:
-//   D  = rowsum(dO * O)                       bwd_delta_kernel
+//   D  = rowsum(dO * O)                       bwd_dq_kernel     (first; each query
+//   dQ = scale * dS K                                              tile's own rows,
+//        with dS = P * (dO V^T - D)                                walks the CSR)
 //   dV = P^T dO,  dK = scale * dS^T Q          bwd_dkdv_kernel   (key-tile major,
-//        with dS = P * (dO V^T - D)                                 walks the CSC)
-//   dQ = scale * dS K                          bwd_dq_kernel     (query-tile major,
-//                                                                   walks the CSR)
+//                                                                   walks the CSC)
 // P and dS are recomputed per block pair from the forward's LSE, never stored.
-// Splitting dQ into its own pass keeps every output written by exactly one
-// workgroup: no atomics, bitwise-deterministic results.
+// The dQ pass computes D and the base-2 LSE of its own rows and leaves them in
+// the workspace for the dK/dV pass.  Splitting dQ into its own pass keeps
+// every output written by exactly one workgroup: no atomics,
+// bitwise-deterministic results.
 //
 // gfx950 mapping (both MFMA kernels): the streamed tiles (K and V for dQ; Q
 // and dO for dK/dV) go straight from global memory into XOR-swizzled LDS
@@ -36,36 +38,6 @@ namespace {
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = kBwdWaves * 64;
 constexpr int kBwdTB = kBwdWaves / 2;  // 64-token blocks per tile (32 rows per wave)
-
-// -D = -rowsum(dO * O) and the base-2 LSE (lse * log2 e; +inf for an empty
-// row, so that P = exp2(s - lse2) = 0 there) per token.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
-  constexpr int LPR = D / 8;      // lanes per row
-  constexpr int RPB = 256 / LPR;  // rows per workgroup
-  const size_t total = (size_t)a.B * a.H * a.L;
-  const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int c = threadIdx.x % LPR;
-  float acc = 0.f;
-  if (row < total) {
-    const int bh = (int)(row / a.L), l = (int)(row % a.L);
-    const int bb = bh / a.H, head = bh % a.H;
-    const bf16 *op = (const bf16 *)a.o + a.os.at(bb, head) + (size_t)l * a.os.l;
-    const bf16 *gp = (const bf16 *)a.dout + a.dos.at(bb, head) + (size_t)l * a.dos.l;
-    const u32x4 o = *(const u32x4 *)(op + c * 8);
-    const u32x4 g = *(const u32x4 *)(gp + c * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc += bf16_lo(o[i]) * bf16_lo(g[i]) + bf16_hi(o[i]) * bf16_hi(g[i]);
-  }
-#pragma unroll
-  for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
-  if (row < total && c == 0) {
-    a.delta[row] = -acc;   // -D: the dK/dV kernel starts its dP accumulator from it
-    const float l = a.lse[row];
-    a.lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
-  }
-}
 
 // A compile-time order of k-steps: KOrder<...>::value[i].
 template <int... J>
@@ -170,7 +142,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int bb = bh / a.H, head = bh % a.H;
   const size_t dense_base = (size_t)bh * a.L * D;
   const int lq = DENSE ? D : a.qs.l, lk = DENSE ? D : a.ks.l, lv = DENSE ? D : a.vs.l;
-  const int ldo = DENSE ? D : a.dos.l, ldq = DENSE ? D : a.dqs.l;
+  const int ldo = DENSE ? D : a.dos.l, ldq = DENSE ? D : a.dqs.l, lo_ = DENSE ? D : a.os.l;
   const bf16 *kg = (const bf16 *)a.k + (DENSE ? dense_base : a.ks.at(bb, head));
   const bf16 *vg = (const bf16 *)a.v + (DENSE ? dense_base : a.vs.at(bb, head));
 
@@ -184,29 +156,29 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int q_tok = q_wave + n;
   const bf16 *qw = (const bf16 *)a.q + (DENSE ? dense_base : a.qs.at(bb, head)) + (size_t)q_wave * lq;
   const bf16 *dow = (const bf16 *)a.dout + (DENSE ? dense_base : a.dos.at(bb, head)) + (size_t)q_wave * ldo;
+  const bf16 *ow = (const bf16 *)a.o + (DENSE ? dense_base : a.os.at(bb, head)) + (size_t)q_wave * lo_;
 
-  // The wave's operand rows, loaded inside the bitmap build behind the list
-  // reads.  Rows past L of a partial last block (and every row of a query
-  // block past the last) load as zero operands, and P = 0 there (LSE2 = +inf).
+  // The wave's operand rows, and the O rows and LSE of its queries (for D),
+  // loaded inside the bitmap build behind the list reads.  Rows past L of a
+  // partial last block (and every row of a query block past the last) load as
+  // zeros, and P = 0 there (LSE2 = +inf).
   const bool q_in = q_valid && (!RAG || q_tok < a.L);
   const int rows_left = q_valid ? a.L - q_wave : 0;
-  bf16x8 bq[KS], bdo[KS];
-  float lse2, dlt;
+  const size_t vrow = (size_t)bh * a.L + q_wave;   // the wave's first entry of [B,H,L] vectors
+  bf16x8 bq[KS], bdo[KS], bo[KS];
+  float lse;
   auto load_rows = [&]() __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rq = rows_rsrc<32>(qw, rows_left, 2 * lq, 2 * D);
-    const __amdgpu_buffer_rsrc_t ro = rows_rsrc<32>(dow, rows_left, 2 * ldo, 2 * D);
+    const __amdgpu_buffer_rsrc_t rg = rows_rsrc<32>(dow, rows_left, 2 * ldo, 2 * D);
+    const __amdgpu_buffer_rsrc_t ro = rows_rsrc<32>(ow, rows_left, 2 * lo_, 2 * D);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bq[ks] = load_row16(rq, 2 * (n * lq + ks * 16 + hh * 8));
-      bdo[ks] = load_row16(ro, 2 * (n * ldo + ks * 16 + hh * 8));
+      bdo[ks] = load_row16(rg, 2 * (n * ldo + ks * 16 + hh * 8));
+      bo[ks] = load_row16(ro, 2 * (n * lo_ + ks * 16 + hh * 8));
     }
-    const size_t v0 = (size_t)bh * a.L + q_wave;
-    const float l = __uint_as_float(
-        __builtin_amdgcn_raw_buffer_load_b32(rows_rsrc<32>(a.lse2 + v0, rows_left, 4, 4), 4 * n, 0, 0));
-    const float e = __uint_as_float(
-        __builtin_amdgcn_raw_buffer_load_b32(rows_rsrc<32>(a.delta + v0, rows_left, 4, 4), 4 * n, 0, 0));
-    lse2 = q_in ? l : INFINITY;
-    dlt = q_in ? -e : 0.f;
+    lse = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rows_rsrc<32>(a.lse + vrow, rows_left, 4, 4), 4 * n, 0, 0));
   };
   const float c = a.scale * kLog2e;
 
@@ -223,6 +195,29 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   pb.init(dyn_lds, a.ix.n_kblocks);
   pb.build(a.ix.row_ptr + (size_t)hidx * (nqb + 1), tile * kBwdTB, nqb, a.ix.nnz, a.ix.col_idx,
            a.ix.n_kblocks, kBwdThreads, load_rows);
+
+  // D = rowsum(dO * O) of the lane's query: its 64 dims (d = 16 ks + 8 hh ..
+  // +7), then the other 64 from lane n + 32 (the same sum on both lanes); and
+  // the base-2 LSE (+inf for an empty row, so that P = 0 there).  Both go to
+  // the workspace for the dK/dV pass (one writer per query).
+  float lse2, dlt;
+  {
+    float dsum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 o = __builtin_bit_cast(u32x4, bo[ks]), g = __builtin_bit_cast(u32x4, bdo[ks]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dsum += bf16_lo(o[i]) * bf16_lo(g[i]) + bf16_hi(o[i]) * bf16_hi(g[i]);
+    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dsum), __float_as_uint(dsum), false, false);
+    dsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    lse2 = q_in && lse != -INFINITY ? lse * kLog2e : INFINITY;
+    dlt = q_in ? dsum : 0.f;
+    if (q_in && hh == 0) {
+      a.delta[vrow + n] = -dsum;   // -D: the dK/dV kernel starts its dP accumulator from it
+      a.lse2[vrow + n] = lse2;
+    }
+  }
   RowsIter<kBwdTB> it;
   it.start(a.ix.n_kblocks, min(tile * kBwdTB + kBwdTB - 1, nqb - 1) & ~63);
   auto advance = [&]() __attribute__((always_inline)) -> BwdPos {
@@ -668,16 +663,14 @@ hipError_t launch_dkdv(const BwdArgs &a, hipStream_t s) {
 
 template <int D, bool WIN, bool DENSE, bool RAG>
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
-  const size_t rows = (size_t)a.B * a.H * a.L;
-  const int rpb = 256 / (D / 8);
-  const int grid_delta = (int)((rows + rpb - 1) / rpb);
   const int q_tiles = (a.ix.n_qblocks + kBwdTB - 1) / kBwdTB;
   const int BH = a.B * a.H;
   const size_t dyn_q = RowsBitmap<kBwdTB>::lds_bytes(a.ix.n_kblocks);
   hipError_t e = hipFuncSetAttribute((const void *)bwd_dq_kernel<D, WIN, DENSE, RAG>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_q);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3(grid_delta), dim3(256), 0, s, a);
+  // dQ first: it leaves D and the base-2 LSE in the workspace
+  hipLaunchKernelGGL((bwd_dq_kernel<D, WIN, DENSE, RAG>), dim3(BH * q_tiles), dim3(kBwdThreads), dyn_q, s, a);
   // BlockSparse (a per-head index grouped by strided class): two key blocks
   // per dK/dV workgroup; otherwise one
   if constexpr (!WIN) {
@@ -686,7 +679,6 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
     e = launch_dkdv<D, WIN, DENSE, RAG, 4>(a, s);
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, WIN, DENSE, RAG>), dim3(BH * q_tiles), dim3(kBwdThreads), dyn_q, s, a);
   return hipGetLastError();
 }
 
