@@ -68,13 +68,9 @@ __device__ __forceinline__ float xor32_max(float x) {
 // Unlike global_load_lds, the compiler counts this form on vmcnt alone, so
 // LDS reads issued while it is in flight keep exact lgkmcnt waits (with a
 // global_load_lds pending it waits for every outstanding LDS read instead).
-// Descriptor: stride 0 (raw bytes), no range limit, data format 32 (the
-// untyped-buffer setting of the gfx9 descriptor word 3).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, 0x00020000);
-}
-// The same descriptor limited to `bytes`: loads at offsets >= bytes return
-// zeros without touching memory.
+// Descriptor: stride 0 (raw bytes), data format 32 (the untyped-buffer
+// setting of the gfx9 descriptor word 3), limited to `bytes` (-1: no limit):
+// loads at offsets >= bytes return zeros without touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc_n(const void *base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
 }

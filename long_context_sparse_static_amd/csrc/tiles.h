@@ -260,10 +260,6 @@ struct RowsBitmap {
     }
     __syncthreads();
   }
-  __device__ void build_rows(const int32_t *ptr, const int (&rows)[R], int nnz, const int32_t *ids,
-                             int n_ids, int nt) {
-    build_rows(ptr, rows, nnz, ids, n_ids, nt, []() {});
-  }
 
   // Lists first .. first + R - 1 (those below n_rows).
   template <typename Issue>
