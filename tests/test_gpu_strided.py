@@ -114,3 +114,28 @@ def test_inputs_with_token_stride_below_d(stride):
     wo, wl = sparse_forward(as_f64(q), as_f64(k), as_f64(v), oracle_pattern(pat))
     assert_bf16_close(as_f64(o), wo, "O")
     assert_bf16_close(as_f64(lse), wl, "LSE")
+
+
+@pytest.mark.parametrize("stride", [0, 32])
+def test_fp32_inputs_with_token_stride_below_d(stride):
+    """The fp32 forward on Q, K, V whose token rows overlap (row stride below
+    d), at a length with a partial last block: equal to contiguous copies bit
+    for bit, and to the oracle."""
+    need_gpu()
+    pat = lcs.attnsink_pattern(1, 2)
+    B, H, L, d = 1, 2, 64 * 4 + 9, 64
+
+    def overlapping(name):
+        n = (L - 1) * stride + d
+        buf = randn((B, H, n), seed_for(940 + stride, 0, name), torch.float32).cuda()
+        return buf.as_strided((B, H, L, d), (H * n, n, stride, 1))
+
+    q, k, v = (overlapping(n) for n in ("q", "k", "v"))
+    ix = lcs.build_device_index(pat, H, L, q.device, with_csc=False)
+    o, lse = lcs.attn_sparse_fwd_strided(q, k, v, ix, pat)
+    o2, lse2 = lcs.attn_sparse_fwd(q.contiguous(), k.contiguous(), v.contiguous(), ix, pat)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    wo, wl = sparse_forward(as_f64(q), as_f64(k), as_f64(v), oracle_pattern(pat))
+    assert_f32_close(as_f64(o), wo, "O")
+    assert_f32_close(as_f64(lse), wl, "LSE")
