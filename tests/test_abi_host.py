@@ -150,6 +150,24 @@ def test_index_of_ragged_length(L):
             assert [ix.col(h, j) for j in range(nb)] == transpose_lists(want, nb)
 
 
+@pytest.mark.parametrize("L", [64 * 11 + 23, 64 * 40])
+def test_patterns_listing_every_causal_block_build_the_full_index(L):
+    """A window that covers the sequence, BlockSparse with stride 1 (every
+    earlier block strided) and a token window longer than the sequence all
+    list every causal block: their CSR and CSC arrays equal the full
+    pattern's, head by head."""
+    nb = -(-L // 64)
+    full = lcs.attn_index_build(lcs.full_pattern(), 1, L, with_csc=True)
+    for pat in (lcs.attnsink_pattern(1, nb), lcs.attnsink_pattern(0, nb + 5), lcs.blocksparse_pattern(1, 1, 1),
+                lcs.blocksparse_pattern(2, 3, 1), lcs.sliding_pattern(1, L + 64)):
+        H = 3 if pat.head_dependent else 1
+        ix = lcs.attn_index_build(pat, H, L, with_csc=True)
+        assert ix.nnz == H * full.nnz
+        for h in range(H):
+            assert [ix.row(h, i) for i in range(nb)] == [full.row(0, i) for i in range(nb)]
+            assert [ix.col(h, j) for j in range(nb)] == [full.col(0, j) for j in range(nb)]
+
+
 def test_index_nnz_closed_forms():
     assert lcs.attn_index_nnz(lcs.attnsink_pattern(1, 4), 1, 1024) == 70
     assert lcs.attn_index_nnz(lcs.attnsink_pattern(1, 64), 1, 8192) == 6240

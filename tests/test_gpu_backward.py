@@ -207,3 +207,30 @@ def test_backward_custom_index_empty_rows_and_columns():
             assert_bf16_close(as_f64(g), w, f"{name} head {h}")
     assert torch.all(dq[:, :, 64:128] == 0)
     assert torch.all(dk[:, :, 192:256] == 0) and torch.all(dv[:, :, 192:256] == 0)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_patterns_listing_every_causal_block_match_full(d):
+    """A window covering the sequence and BlockSparse with stride 1 list
+    every causal block, as the full pattern does: the same block pairs in
+    the same walk order, so forward and backward equal the full pattern's
+    bit for bit (at a length with a partial last block)."""
+    need_gpu()
+    B, H, L = 1, 3, 64 * 11 + 23
+    nb = -(-L // 64)
+    q, k, v, do = _inputs((B, H, L, d), 470 + d)
+    results = []
+    for pat in (lcs.full_pattern(), lcs.attnsink_pattern(1, nb), lcs.blocksparse_pattern(1, 1, 1)):
+        ix = lcs.build_device_index(pat, H, L, q.device, with_csc=True)
+        o, lse = lcs.attn_sparse_fwd(q, k, v, ix, pat)
+        dq, dk, dv = lcs.attn_sparse_bwd(q, k, v, o, lse, do, ix, pat)
+        results.append((o, lse, dq, dk, dv))
+    torch.cuda.synchronize()
+    for other in results[1:]:
+        for a, b in zip(results[0], other):
+            assert torch.equal(a, b)
+    wq, wk, wv, wo, _ = sparse_backward(as_f64(q), as_f64(k), as_f64(v), as_f64(do),
+                                        oracle_pattern(lcs.full_pattern()))
+    for n, g, w in (("o", results[0][0], wo), ("dq", results[0][2], wq), ("dk", results[0][3], wk),
+                    ("dv", results[0][4], wv)):
+        assert_bf16_close(as_f64(g), w, n)
