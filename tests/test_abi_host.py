@@ -462,3 +462,40 @@ def test_blocksparse_cache_sizing_rejections():
     assert L.attn_blocksparse_cache_slots(ctypes.byref(good), -1, ctypes.byref(out64)) == lcs.ATTN_ERR_INVALID_ARG
     assert L.attn_blocksparse_cache_slots(ctypes.byref(good), 2 ** 31 - 1, ctypes.byref(out64)) == lcs.ATTN_ERR_UNSUPPORTED
     assert out32.value == -7 and out64.value == -7          # nothing written on an error
+
+
+def _random_pattern(rng):
+    kind = int(rng.integers(0, 4))
+    if kind == 0:
+        return lcs.full_pattern()
+    if kind == 1:
+        return lcs.attnsink_pattern(int(rng.integers(0, 5)), int(rng.integers(1, 21)))
+    if kind == 2:
+        return lcs.blocksparse_pattern(int(rng.integers(0, 5)), int(rng.integers(1, 21)), int(rng.integers(1, 10)))
+    return lcs.sliding_pattern(int(rng.integers(0, 4)), int(rng.integers(1, 3000)))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_index_of_random_patterns_matches_oracle(seed):
+    """Seeded random pattern parameters (sink, local, stride, token window),
+    head counts and lengths, whole and ragged: the builder's CSR and CSC equal
+    the oracle's brute-force lists, and nnz its count."""
+    rng = np.random.default_rng(7100 + seed)
+    kinds = {lcs.ATTN_FULL: FULL, lcs.ATTN_ATTNSINK: ATTNSINK, lcs.ATTN_BLOCKSPARSE: BLOCKSPARSE,
+             lcs.ATTN_SLIDING: SLIDING}
+    for _ in range(15):
+        pat = _random_pattern(rng)
+        L = int(rng.integers(1, 64 * 60))
+        nb = -(-L // 64)
+        H = int(rng.integers(1, 6)) if pat.head_dependent else 1
+        ix = lcs.attn_index_build(pat, H, L, with_csc=True)
+        lcs.attn_index_validate(ix)
+        opat = dict(kind=kinds[pat.kind], block=64, sink_blocks=pat.sink_blocks, local_blocks=pat.local_blocks,
+                    stride=pat.stride, window_tokens=pat.window_tokens)
+        total = 0
+        for h in range(H):
+            want = pattern_lists_for_head(opat, nb, h)
+            total += sum(len(r) for r in want)
+            assert [ix.row(h, i) for i in range(nb)] == want, (pat, L, h)
+            assert [ix.col(h, j) for j in range(nb)] == transpose_lists(want, nb), (pat, L, h)
+        assert ix.nnz == total == lcs.attn_index_nnz(pat, H, L)
