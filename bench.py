@@ -802,6 +802,35 @@ def summarize_mfma(path):
     return "\n".join(out)
 
 
+def summarize_counters(paths):
+    """Per attention kernel, from one or more rocprofv3 --pmc runs of the same
+    command: every counter averaged over dispatches and, where a run also
+    counted SQ_WAVES, divided by the waves of a dispatch (per-wave figures;
+    the SQ_*_CYCLES and SQ_ACTIVE_* / SQ_WAIT_* counters are in quad-cycles)."""
+    import csv
+    sums = {}
+    for path in paths:
+        per = {}
+        for r in csv.DictReader(open(path)):
+            if "attn::" not in r["Kernel_Name"]:
+                continue
+            per.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        for (name, _), d in per.items():
+            k = sums.setdefault(name, {})
+            for c, x in d.items():
+                k.setdefault(c, []).append(x)
+    out = []
+    for name, k in sorted(sums.items()):
+        avg = {c: sum(v) / len(v) for c, v in k.items()}
+        waves = avg.get("SQ_WAVES")
+        out.append(_short(name))
+        out.append(f"  {'counter':28s} {'per dispatch':>14s} {'per wave':>12s}")
+        for c in sorted(avg):
+            per_wave = f"{avg[c] / waves:12.1f}" if waves and c.startswith("SQ_") and c != "SQ_WAVES" else f"{'':12s}"
+            out.append(f"  {c:28s} {avg[c]:14.5g} {per_wave}")
+    return "\n".join(out)
+
+
 def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel, scaled so that
     the copy1g kernel reads 1 GiB and writes 1 GiB."""
@@ -843,6 +872,8 @@ def main():
                     help="print matrix-core busy fraction and clock per attention kernel from a "
                          "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
                          "counter_collection.csv, and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="COUNTER_CSV",
+                    help="print per-kernel counter averages (and per-wave figures) of rocprofv3 --pmc runs")
     ap.add_argument("--summarize-traffic", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="print per-kernel HBM bytes from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
@@ -850,6 +881,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_stats:
         print(summarize_stats(args.summarize_stats))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
         return
     if args.summarize_mfma:
         print(summarize_mfma(args.summarize_mfma))

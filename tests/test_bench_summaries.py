@@ -72,3 +72,22 @@ def test_traffic_calibration(tmp_path):
     line = [x for x in text.splitlines() if "fwd_bf16_kernel" in x][0]
     # mean fetch 2e6 KiB x 2 + mean write 5e5 KiB x 1, in GB
     assert abs(float(line.split()[-1]) - (2e6 * 2 + 5e5) * 1024 / 1e9) < 1e-3
+
+
+def test_counter_averages_and_per_wave(tmp_path):
+    """Two passes of one command: each counter averaged over dispatches;
+    SQ_ counters also per wave (divided by the dispatch's SQ_WAVES, counted
+    in the first pass), GRBM_ ones not."""
+    name = "void attn::(anonymous namespace)::fwd_bf16_kernel<128, false, true>(attn::FwdArgs)"
+    p1 = _write(tmp_path / "p1.csv", [(1, name, "SQ_WAVES", 1000, 0, 1), (1, name, "SQ_INSTS_VALU", 150000, 0, 1),
+                                      (2, name, "SQ_WAVES", 1000, 0, 1), (2, name, "SQ_INSTS_VALU", 170000, 0, 1),
+                                      (3, "void at::native::fill_kernel", "SQ_WAVES", 7, 0, 1)])
+    p2 = _write(tmp_path / "p2.csv", [(1, name, "SQ_INSTS_SALU", 50000, 0, 1), (1, name, "GRBM_GUI_ACTIVE", 8e6, 0, 1),
+                                      (2, name, "SQ_INSTS_SALU", 60000, 0, 1), (2, name, "GRBM_GUI_ACTIVE", 8e6, 0, 1)])
+    out = bench.summarize_counters([p1, p2]).splitlines()
+    assert len(out) == 6 and "fwd_bf16_kernel" in out[0]
+    rows = {ln.split()[0]: ln.split()[1:] for ln in out[2:]}
+    assert rows["SQ_INSTS_VALU"] == ["1.6e+05", "160.0"]
+    assert rows["SQ_INSTS_SALU"] == ["55000", "55.0"]
+    assert rows["GRBM_GUI_ACTIVE"] == ["8e+06"]
+    assert rows["SQ_WAVES"] == ["1000"]
