@@ -31,6 +31,13 @@
  *    kernel launch returns ATTN_ERR_HIP.  Faults inside kernels surface at the
  *    caller's next synchronisation of `stream`.  No C++ exception crosses the
  *    ABI.
+ *  - Streams and graphs: a device op only enqueues kernels on `stream`; it
+ *    makes no allocation, synchronisation, memset or copy of its own, and
+ *    its launch shapes depend on host arguments only (a decode's split count
+ *    on the capacity or max_pos, never on the device-side positions).  So
+ *    calls on different streams run concurrently, and a call can be captured
+ *    in a HIP graph and replayed with new contents of the same buffers
+ *    (positions included).
  *  - Kernels treat a malformed device index defensively: row pointers are
  *    clamped to [0, nnz] and out-of-range block ids are skipped, so a bad
  *    index gives wrong numbers, never an out-of-bounds access.  Use
